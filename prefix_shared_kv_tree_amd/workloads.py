@@ -1,0 +1,260 @@
+"""Seeded synthetic decode workloads for prefix-shared KV attention.
+
+This module only draws inputs. It holds none of the attention arithmetic and
+none of the tree logic, so both the fp64 oracle (through the tests) and the
+HIP path consume exactly the same arrays.
+
+A workload is a set of token *segments* (a shared root prompt, a shared
+branch, a private suffix...) and, for every sequence of the decode batch, the
+list of segments its context is made of, in order.  Each segment carries its
+own K and V values, drawn once, so a segment shared by several sequences is
+literally the same array for all of them.  Shapes follow the microkernel
+benchmark of the ChunkAttention page (Knowl 6: one decoded token per
+sequence, h heads, head_dim d, chunk size c, fp16 Q/K/V); values are N(0,1)
+drawn in float32 and rounded to fp16 (round-to-nearest-even).
+
+Draw order for a named config (all from one numpy PCG64 generator seeded
+with ``1000 + config index``):
+  1. structure parameters (only the long-prompt config: the private suffix
+     lengths, ``integers(256, 1025)`` per sequence),
+  2. token ids of every segment, in segment order, uniform in [0, 32000),
+  3. Q as a [b, h, d] block,
+  4. for each layer, for each segment in order: K [len, h, d] then V.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional
+
+import numpy as np
+
+VOCAB = 32000
+
+#: Names of the seeded configurations, in index order (seed = 1000 + index).
+CONFIG_NAMES = ("tiny", "c2", "c3", "c4", "c5")
+
+CONFIG_DESCRIPTIONS = {
+    "tiny": "4 decode queries, 2 heads, head_dim 64, chunk 16; one shared "
+            "64-token prefix plus a private 32-token suffix per sequence",
+    "c2": "32 heads, head_dim 128, chunk 64; batch 32 sharing a 1024-token "
+          "prefix, private 512-token suffix each",
+    "c3": "32 heads, head_dim 128, chunk 64; batch 64 sharing a 4096-token "
+          "prefix, private suffix lengths uniform in [256, 1024]",
+    "c4": "32 heads, head_dim 128, chunk 64; 2 roots x 2048 tokens (32 seqs "
+          "each), 4 branches x 512 tokens per root (8 seqs each), private "
+          "256-token suffixes; batch 64",
+    "c5": "32 heads, head_dim 128, chunk 64; batch 64, each over its own "
+          "private 2048-token context (nothing shared)",
+}
+
+
+@dataclasses.dataclass
+class Segment:
+    """A run of consecutive context tokens with its per-layer K and V."""
+    tokens: np.ndarray                 # int32 [L]
+    k: List[np.ndarray]                # per layer: float16 [L, h, d]
+    v: List[np.ndarray]                # per layer: float16 [L, h, d]
+
+    def __len__(self) -> int:
+        return int(self.tokens.shape[0])
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    h: int
+    d: int
+    c: int
+    segments: List[Segment]
+    seq_paths: List[List[int]]         # per sequence: segment indices, in order
+    q: np.ndarray                      # float16 [b, h, d]
+    layers: int = 1
+
+    @property
+    def b(self) -> int:
+        return len(self.seq_paths)
+
+    def seq_tokens(self, u: int) -> np.ndarray:
+        return np.concatenate([self.segments[s].tokens for s in self.seq_paths[u]])
+
+    def seq_len(self, u: int) -> int:
+        return int(sum(len(self.segments[s]) for s in self.seq_paths[u]))
+
+    def all_seq_tokens(self) -> List[np.ndarray]:
+        return [self.seq_tokens(u) for u in range(self.b)]
+
+
+def _normal_f16(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) drawn as float32, rounded to fp16. Drawn in slabs to bound memory."""
+    shape = tuple(int(s) for s in shape)
+    out = np.empty(shape, dtype=np.float16)
+    if out.size == 0:
+        return out
+    flat = out.reshape(shape[0], -1)
+    row = flat.shape[1]
+    step = max(1, (1 << 24) // max(row, 1))
+    for i in range(0, shape[0], step):
+        j = min(shape[0], i + step)
+        flat[i:j] = rng.standard_normal((j - i, row), dtype=np.float32).astype(np.float16)
+    return out
+
+
+def _finish(name, rng, h, d, c, seg_lens, seq_paths, layers, token_fn=None,
+            with_kv: bool = True) -> Workload:
+    tokens = []
+    for L in seg_lens:
+        if token_fn is None:
+            tokens.append(rng.integers(0, VOCAB, size=L, dtype=np.int64).astype(np.int32))
+        else:
+            tokens.append(token_fn(L))
+    b = len(seq_paths)
+    q = _normal_f16(rng, (b, h, d))
+    segs = [Segment(tokens=t, k=[], v=[]) for t in tokens]
+    for _ in range(layers if with_kv else 0):
+        for s in segs:
+            s.k.append(_normal_f16(rng, (len(s), h, d)))
+            s.v.append(_normal_f16(rng, (len(s), h, d)))
+    return Workload(name=name, h=h, d=d, c=c, segments=segs,
+                    seq_paths=[list(p) for p in seq_paths], q=q, layers=layers)
+
+
+def make_config(name: str, layers: int = 1, seed: Optional[int] = None,
+                with_kv: bool = True) -> Workload:
+    """Build one of the five named configurations (see CONFIG_DESCRIPTIONS).
+
+    ``with_kv=False`` skips the K/V draws (they come last, so tokens and Q
+    are unchanged) for tests that only need the token structure."""
+    idx = CONFIG_NAMES.index(name)
+    rng = np.random.Generator(np.random.PCG64(1000 + idx if seed is None else seed))
+    if name == "tiny":
+        b, h, d, c = 4, 2, 64, 16
+        seg_lens = [64] + [32] * b
+        paths = [[0, 1 + u] for u in range(b)]
+        return _finish(name, rng, h, d, c, seg_lens, paths, layers, with_kv=with_kv)
+    h, d, c = 32, 128, 64
+    if name == "c2":
+        b = 32
+        seg_lens = [1024] + [512] * b
+        paths = [[0, 1 + u] for u in range(b)]
+    elif name == "c3":
+        b = 64
+        priv = rng.integers(256, 1025, size=b)
+        seg_lens = [4096] + [int(x) for x in priv]
+        paths = [[0, 1 + u] for u in range(b)]
+    elif name == "c4":
+        b = 64
+        # segments: 2 roots, 8 branches (root r owns branches 2 + 4r .. 2 + 4r + 3), 64 privates
+        seg_lens = [2048, 2048] + [512] * 8 + [256] * b
+        paths = []
+        for u in range(b):
+            root = u // 32
+            branch = 2 + 4 * root + (u // 8) % 4
+            paths.append([root, branch, 10 + u])
+    elif name == "c5":
+        b = 64
+        seg_lens = [2048] * b
+        paths = [[u] for u in range(b)]
+    else:  # pragma: no cover
+        raise ValueError(name)
+    return _finish(name, rng, h, d, c, seg_lens, paths, layers, with_kv=with_kv)
+
+
+def random_tree(seed: int, h: int = 2, d: int = 16, c: int = 4, max_b: int = 6,
+                max_len: int = 80, vocab: int = VOCAB, layers: int = 1,
+                unaligned: bool = True) -> Workload:
+    """A small random prefix forest with ragged lengths.
+
+    Each new sequence either starts a fresh root (probability 0.2) or picks a
+    random earlier sequence and a random cut point, reuses that sequence's
+    first ``cut`` tokens (the same segments, hence the same K/V values) and
+    appends a fresh suffix.  With ``unaligned`` the cut is any token
+    position, so chunk boundaries and segment boundaries need not coincide.
+    A small ``vocab`` makes accidental full-chunk matches between unrelated
+    token runs likely; use it only for tree tests, since attention parity
+    additionally needs equal token prefixes to carry equal K/V values.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    b = int(rng.integers(1, max_b + 1))
+    seg_tokens: List[np.ndarray] = []
+    paths: List[List[int]] = []
+
+    def new_seg(toks):
+        seg_tokens.append(np.asarray(toks, dtype=np.int32))
+        return len(seg_tokens) - 1
+
+    def fresh(L):
+        return new_seg(rng.integers(0, vocab, size=L, dtype=np.int64))
+
+    for u in range(b):
+        if u == 0 or rng.random() < 0.2:
+            paths.append([fresh(int(rng.integers(1, max_len + 1)))])
+            continue
+        parent = list(paths[int(rng.integers(0, u))])
+        plen = sum(len(seg_tokens[s]) for s in parent)
+        cut = int(rng.integers(0, plen + 1))
+        if not unaligned:
+            cut -= cut % c
+        path: List[int] = []
+        acc = 0
+        split = None
+        for s in parent:
+            L = len(seg_tokens[s])
+            if acc + L <= cut:
+                path.append(s)
+                acc += L
+                continue
+            take = cut - acc
+            if take > 0:
+                split = (s, take)
+            break
+        if split is not None:
+            s, take = split
+            head = new_seg(seg_tokens[s][:take])
+            tail = new_seg(seg_tokens[s][take:])
+            for p in paths:
+                if s in p:
+                    i = p.index(s)
+                    p[i:i + 1] = [head, tail]
+            path.append(head)
+            acc += take
+        extra = int(rng.integers(0 if acc > 0 else 1, max(2, max_len - acc + 1)))
+        if extra > 0:
+            path.append(fresh(extra))
+        paths.append(path)
+    used = sorted({s for p in paths for s in p})
+    remap = {s: i for i, s in enumerate(used)}
+    tok_list = [seg_tokens[s] for s in used]
+    paths = [[remap[s] for s in p] for p in paths]
+    it = iter(tok_list)
+    return _finish(f"random{seed}", rng, h, d, c, [len(t) for t in tok_list], paths,
+                   layers, token_fn=lambda L: next(it))
+
+
+def unshare(w: Workload, token_offset: int = 1 << 20) -> Workload:
+    """Same K/V values, but every sequence gets private copies of its segments
+    under distinct token ids, so nothing can be shared by a prefix tree.  The
+    attention result per sequence is unchanged by construction."""
+    segs: List[Segment] = []
+    paths: List[List[int]] = []
+    for u, p in enumerate(w.seq_paths):
+        np_ = []
+        for s in p:
+            src = w.segments[s]
+            segs.append(Segment(tokens=src.tokens + np.int32(token_offset * (u + 1)),
+                                k=src.k, v=src.v))
+            np_.append(len(segs) - 1)
+        paths.append(np_)
+    return Workload(name=w.name + "-unshared", h=w.h, d=w.d, c=w.c, segments=segs,
+                    seq_paths=paths, q=w.q, layers=w.layers)
+
+
+def unique_tokens(w: Workload) -> int:
+    """Number of distinct token positions when every full-chunk prefix is
+    stored once: this is the count of *stored* KV rows, used for the
+    effective-bytes metric.  Computed from segment structure only for the
+    named configs, whose shared boundaries are chunk-aligned."""
+    return int(sum(len(s) for s in w.segments))
+
+
+def logical_tokens(w: Workload) -> int:
+    return int(sum(w.seq_len(u) for u in range(w.b)))

@@ -1,0 +1,238 @@
+"""Pins for the fp64 attention oracle (CPU only).
+
+None of these re-types the oracle's formula: they compare it with hand-worked
+closed forms, a library implementation of the textbook definition, a scalar
+brute force that locates every token by walking the segment list, special
+cases with known answers, and invariances the definition implies.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import sharing as S
+from prefix_shared_kv_tree_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("fixture", ["two_key_closed_form.json", "three_key_closed_form.json"])
+def test_closed_form_fixture(fixture):
+    fx = _load(fixture)
+    q = np.array(fx["q"])[None, :]
+    K = np.array(fx["K"])[:, None, :]
+    V = np.array(fx["V"])[:, None, :]
+    d = q.shape[1]
+    O = A.attention_one(q, K, V, 1.0 / math.sqrt(d))
+    np.testing.assert_allclose(O[0], fx["O"], rtol=0, atol=1e-12)
+
+
+def _brute_force(w, u, hh, scale):
+    """Scalar brute force: token t of sequence u is found by walking the
+    segment list; scores and weights use math.exp/math.fsum, no max shift."""
+    L = w.seq_len(u)
+    d = w.d
+
+    def row(arrs, t):
+        for s in w.seq_paths[u]:
+            n = len(w.segments[s])
+            if t < n:
+                return [float(x) for x in arrs(w.segments[s])[t, hh]]
+            t -= n
+        raise IndexError
+
+    q = [float(x) for x in w.q[u, hh]]
+    scores = []
+    for t in range(L):
+        k = row(lambda s: s.k[0], t)
+        scores.append(math.fsum(q[i] * k[i] for i in range(d)) * scale)
+    wts = [math.exp(s) for s in scores]
+    tot = math.fsum(wts)
+    out = []
+    for i in range(d):
+        out.append(math.fsum(wts[t] * row(lambda s: s.v[0], t)[i] for t in range(L)) / tot)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_random_trees(seed):
+    w = W.random_tree(seed, h=2, d=8, c=4, max_b=4, max_len=24)
+    O = A.attention_batch(w)
+    scale = 1.0 / math.sqrt(w.d)
+    for u in range(w.b):
+        for hh in range(w.h):
+            np.testing.assert_allclose(O[u, hh], _brute_force(w, u, hh, scale), rtol=1e-12, atol=1e-12)
+
+
+def test_brute_force_tiny_config_sampled():
+    w = W.make_config("tiny")
+    O = A.attention_batch(w)
+    scale = 1.0 / math.sqrt(w.d)
+    for u, hh in [(0, 0), (3, 1)]:
+        np.testing.assert_allclose(O[u, hh], _brute_force(w, u, hh, scale), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["tiny"])
+def test_against_torch_sdpa(name):
+    """Library routine implementing softmax(QK^T/sqrt(d))V, in float64."""
+    w = W.make_config(name)
+    O = A.attention_batch(w)
+    for u in range(w.b):
+        K, V = A.materialize(w, u)
+        q = torch.from_numpy(w.q[u].astype(np.float64))[:, None, :]      # [h, 1, d]
+        k = torch.from_numpy(np.ascontiguousarray(K.transpose(1, 0, 2)))  # [h, L, d]
+        v = torch.from_numpy(np.ascontiguousarray(V.transpose(1, 0, 2)))
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)[:, 0, :].numpy()
+        np.testing.assert_allclose(O[u], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_materialize_follows_path_order():
+    """Values encode (segment, offset); the materialized rows must list the
+    path's segments in order."""
+    w = W.make_config("c4")
+    w.h, w.d = 1, 2
+    for si, s in enumerate(w.segments):
+        n = len(s)
+        s.k = [np.stack([np.full(n, si), np.arange(n)], axis=1).astype(np.float64)[:, None, :]]
+        s.v = [s.k[0].copy()]
+    for u in [0, 9, 63]:
+        K, _ = A.materialize(w, u)
+        expect = []
+        for si in w.seq_paths[u]:
+            expect += [(si, o) for o in range(len(w.segments[si]))]
+        got = [(int(r[0, 0]), int(r[0, 1])) for r in K]
+        assert got == expect
+
+
+def test_single_key_is_value_row():
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((3, 16))
+    K = rng.standard_normal((1, 3, 16))
+    V = rng.standard_normal((1, 3, 16))
+    O = A.attention_one(q, K, V, 0.25)
+    assert np.array_equal(O, V[0])
+
+
+def test_zero_query_gives_mean():
+    rng = np.random.default_rng(1)
+    K = rng.standard_normal((37, 2, 8))
+    V = rng.standard_normal((37, 2, 8))
+    O = A.attention_one(np.zeros((2, 8)), K, V, 0.3)
+    np.testing.assert_allclose(O, V.mean(axis=0), rtol=0, atol=1e-12)
+
+
+def test_equal_keys_give_mean():
+    rng = np.random.default_rng(2)
+    K = np.repeat(rng.standard_normal((1, 2, 8)), 19, axis=0)
+    V = rng.standard_normal((19, 2, 8))
+    O = A.attention_one(rng.standard_normal((2, 8)), K, V, 0.3)
+    np.testing.assert_allclose(O, V.mean(axis=0), rtol=0, atol=1e-12)
+
+
+def test_saturation_selects_row():
+    """q = alpha k_j with a large score gap puts all weight on row j."""
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((50, 1, 16))
+    K /= np.linalg.norm(K, axis=2, keepdims=True)
+    V = rng.standard_normal((50, 1, 16))
+    j = 17
+    q = 400.0 * K[j]          # gap >= 400 * (1 - max cos) * scale, far beyond 40
+    O = A.attention_one(q, K, V, 1.0)
+    np.testing.assert_allclose(O[0], V[j, 0], rtol=0, atol=1e-12)
+
+
+def test_key_permutation_invariance():
+    rng = np.random.default_rng(4)
+    K = rng.standard_normal((41, 3, 8))
+    V = rng.standard_normal((41, 3, 8))
+    q = rng.standard_normal((3, 8))
+    p = rng.permutation(41)
+    np.testing.assert_allclose(A.attention_one(q, K, V, 0.4), A.attention_one(q, K[p], V[p], 0.4),
+                               rtol=1e-12, atol=1e-14)
+
+
+def test_scale_enters_scores():
+    """Doubling the scale is the same as doubling q (pins that the scale
+    multiplies the scores, not the output)."""
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((9, 1, 4))
+    V = rng.standard_normal((9, 1, 4))
+    q = rng.standard_normal((1, 4))
+    a = A.attention_one(q, K, V, 0.5)
+    b = A.attention_one(2 * q, K, V, 0.25)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    assert not np.allclose(a, A.attention_one(q, K, V, 0.25))
+
+
+# ---- partitioned form (Knowl 2 / 3) ---------------------------------------
+
+def test_attn_reduce_identity():
+    o = np.arange(4.0)
+    got = A.attn_reduce(o, 1.5, 2.0, np.zeros(4), -math.inf, 0.0)
+    assert np.array_equal(got[0], o) and got[1] == 1.5 and got[2] == 2.0
+    got = A.attn_reduce(np.zeros(4), -math.inf, 0.0, o, 1.5, 2.0)
+    assert np.array_equal(got[0], o) and got[1] == 1.5 and got[2] == 2.0
+
+
+def test_partial_attn_single_chunk_is_attention():
+    """One chunk covering the whole context: O / n is the definition."""
+    rng = np.random.default_rng(6)
+    Q = rng.standard_normal((5, 8))
+    Kc = rng.standard_normal((13, 8))
+    Vc = rng.standard_normal((13, 8))
+    O, m, n = A.partial_attn(Q * 0.3, Kc, Vc)
+    for r in range(5):
+        ref = A.attention_one(Q[r][None], Kc[:, None], Vc[:, None], 0.3)[0]
+        np.testing.assert_allclose(O[r] / n[r], ref, rtol=1e-12, atol=1e-14)
+    assert np.all(n >= 1.0)          # the max element contributes exp(0) = 1
+
+
+def test_attn_reduce_two_halves():
+    """Merging the partials of two halves equals the partial of the whole."""
+    rng = np.random.default_rng(7)
+    Q = rng.standard_normal((1, 8))
+    K = rng.standard_normal((20, 8))
+    V = rng.standard_normal((20, 8))
+    Oa, ma, na = A.partial_attn(Q, K[:7], V[:7])
+    Ob, mb, nb = A.partial_attn(Q, K[7:], V[7:])
+    Ow, mw, nw = A.partial_attn(Q, K, V)
+    o, m, n = A.attn_reduce(Oa[0], ma[0], na[0], np.zeros(8), -math.inf, 0.0)
+    o, m, n = A.attn_reduce(Ob[0], mb[0], nb[0], o, m, n)
+    assert m == mw[0]
+    np.testing.assert_allclose(n, nw[0], rtol=1e-13)
+    np.testing.assert_allclose(o, Ow[0], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("order", ["path", "reverse", "random"])
+@pytest.mark.parametrize("case", ["tiny", "rand0", "rand1", "rand2", "rand3"])
+def test_tpp_equals_monolithic(case, order):
+    if case == "tiny":
+        w = W.make_config("tiny")
+    else:
+        w = W.random_tree(int(case[4:]) + 10, h=2, d=8, c=4, max_b=6, max_len=60)
+    labs = S.chunk_labels(w.all_seq_tokens(), w.c)
+    ref = A.attention_batch(w)
+    got = A.tpp_attention(w, labs, w.c, order=order, rng=np.random.default_rng(3))
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_tpp_detects_wrong_sharing():
+    """The partitioned oracle reads a shared chunk's K/V once, so an
+    incorrect sharing map changes its result (the same mechanism that makes
+    a GPU tree with a wrong map fail parity)."""
+    w = W.make_config("tiny")
+    labs = S.chunk_labels(w.all_seq_tokens(), w.c)
+    bad = [l.copy() for l in labs]
+    bad[1][4] = bad[0][4]           # pretend seq 1's first private chunk is seq 0's
+    ref = A.attention_batch(w)
+    got = A.tpp_attention(w, bad, w.c)
+    assert np.abs(got[1] - ref[1]).max() > 1e-3

@@ -1,0 +1,184 @@
+"""Pins for the sharing-map oracle and the Knowl 4 closed forms (CPU only)."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import sharing as S
+from prefix_shared_kv_tree_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _pairwise_same(toks_u, toks_v, k, c):
+    """The sharing definition evaluated directly for one pair of chunks."""
+    n_u, n_v = len(toks_u), len(toks_v)
+    if (k + 1) * c > n_u or (k + 1) * c > n_v:
+        return False
+    return list(toks_u[:(k + 1) * c]) == list(toks_v[:(k + 1) * c])
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_labels_match_pairwise_definition(seed):
+    w = W.random_tree(seed, c=4, max_b=7, max_len=40, vocab=2)
+    toks = w.all_seq_tokens()
+    labs = S.chunk_labels(toks, 4)
+    for u, v in itertools.product(range(w.b), repeat=2):
+        for k in range(min(len(labs[u]), len(labs[v]))):
+            same = _pairwise_same(toks[u], toks[v], k, 4) or (u == v and True)
+            assert (labs[u][k] == labs[v][k]) == same, (u, v, k)
+    # label count per sequence = ceil(L/c)
+    for u in range(w.b):
+        assert len(labs[u]) == -(-len(toks[u]) // 4)
+
+
+def test_canonicalize_first_appearance():
+    got = S.canonicalize([[7, 3, 9], [7, 4], [3]])
+    assert [list(x) for x in got] == [[0, 1, 2], [0, 3], [1]]
+
+
+def _n_unique(w):
+    return len({int(x) for l in S.chunk_labels(w.all_seq_tokens(), w.c) for x in l})
+
+
+@pytest.mark.parametrize("name,expect", [("tiny", 12), ("c2", 272), ("c4", 384), ("c5", 2048)])
+def test_config_chunk_counts(name, expect):
+    assert _n_unique(W.make_config(name, with_kv=False)) == expect
+
+
+def test_c3_chunk_count_closed_form():
+    w = W.make_config("c3", with_kv=False)
+    priv = [len(w.segments[p[1]]) for p in w.seq_paths]
+    assert _n_unique(w) == 64 + sum(-(-s // 64) for s in priv)
+
+
+@pytest.mark.parametrize("name", ["tiny", "c2", "c4"])
+def test_shared_chunks_cover_expected_sequences(name):
+    w = W.make_config(name, with_kv=False)
+    labs = S.chunk_labels(w.all_seq_tokens(), w.c)
+    cov = S.coverage(labs)
+    sizes = sorted(len(v) for v in cov.values())
+    if name == "tiny":
+        assert sizes.count(4) == 4 and sizes.count(1) == 8
+    elif name == "c2":
+        assert sizes.count(32) == 16 and sizes.count(1) == 256
+    else:
+        # 2 roots x 32 chunks covering 32 seqs, 8 branches x 8 chunks covering 8, 64 x 4 private
+        assert sizes.count(32) == 64 and sizes.count(8) == 64 and sizes.count(1) == 256
+
+
+def test_capacity_multiplier_closed_form():
+    """Knowl 4: with n_s shared and n_q private tokens per sequence, the
+    ratio of logical to stored tokens is b(n_s+n_q)/(n_s+b n_q), which tends
+    to 1/(1-r) with r = n_s/(n_s+n_q) as the batch grows."""
+    w = W.make_config("c2", with_kv=False)
+    labs = S.chunk_labels(w.all_seq_tokens(), w.c)
+    stored = len({int(x) for l in labs for x in l}) * w.c      # all chunks full here
+    logical = sum(w.seq_len(u) for u in range(w.b))
+    b, n_s, n_q = 32, 1024, 512
+    assert logical / stored == pytest.approx(b * (n_s + n_q) / (n_s + b * n_q), rel=1e-15)
+    assert logical / stored == pytest.approx(2.8235294117647, rel=1e-12)
+    r = S.sharing_ratio(n_s, n_s + n_q, 0)
+    assert r == pytest.approx(2 / 3)
+    for bb in [10, 100, 1000, 10000]:
+        exact = bb * (n_s + n_q) / (n_s + bb * n_q)
+        assert abs(exact - S.capacity_multiplier(r)) <= 3.0 * 2 / bb + 1e-12
+    assert S.capacity_multiplier(0.0) == 1.0
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_fragmentation_bound(seed):
+    """Knowl 4: slots lost to a partial leaf are at most c-1, i.e. a
+    fraction <= (c-1)/n of a sequence's n tokens."""
+    c = 8
+    w = W.random_tree(seed, c=c, max_b=6, max_len=100)
+    for u in range(w.b):
+        n = w.seq_len(u)
+        allocated = -(-n // c) * c
+        assert allocated - n <= c - 1
+        assert (allocated - n) / n <= S.fragmentation_bound(c, n) + 1e-15
+
+
+# ---- reference model -------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(25))
+def test_model_insert_only_matches_definition(seed):
+    w = W.random_tree(seed, c=4, max_b=7, max_len=40, vocab=2)
+    m = S.SharingModel(4)
+    for t in w.all_seq_tokens():
+        m.insert(t)
+    got = S.canonicalize(m.paths())
+    want = S.chunk_labels(w.all_seq_tokens(), 4)
+    assert [list(x) for x in got] == [list(x) for x in want]
+
+
+def test_model_dynamic_fixture():
+    with open(os.path.join(GOLDEN, "dynamic_sharing_c4.json")) as f:
+        fx = json.load(f)
+    m = S.SharingModel(fx["c"])
+    for op in fx["ops"]:
+        if op[0] == "insert":
+            m.insert(op[1])
+        elif op[0] == "append":
+            m.append(op[1], op[2])
+        elif op[0] == "remove":
+            m.remove(op[1])
+        else:
+            exp = op[1]
+            assert m.live() == exp["live"]
+            labs = [list(x) for x in S.canonicalize(m.paths())]
+            assert labs == exp["labels"]
+            rc = m.refcounts()
+            assert [[rc[n] for n in p] for p in m.paths()] == exp["refcounts"]
+            assert m.used_chunks() == exp["used"]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_model_random_ops_invariants(seed):
+    """Random insert/append/remove: every live path spells the sequence's
+    tokens, refcounts count covering sequences, shared chunks never change,
+    and removing everything frees everything."""
+    rng = np.random.default_rng(seed)
+    c = 4
+    m = S.SharingModel(c)
+    toks = {}
+    frozen = {}
+    for _ in range(200):
+        r = rng.random()
+        if r < 0.35 or not m.live():
+            base = []
+            if m.live() and rng.random() < 0.7:
+                src = toks[int(rng.choice(m.live()))]
+                base = src[:int(rng.integers(0, len(src) + 1))]
+            t = base + [int(x) for x in rng.integers(0, 2, size=int(rng.integers(1 if not base else 0, 12)))]
+            if not t:
+                t = [0]
+            sid = m.insert(t)
+            toks[sid] = list(t)
+        elif r < 0.85:
+            sid = int(rng.choice(m.live()))
+            tok = int(rng.integers(0, 2))
+            m.append(sid, tok)
+            toks[sid].append(tok)
+        else:
+            sid = int(rng.choice(m.live()))
+            m.remove(sid)
+            del toks[sid]
+        rc = m.refcounts()
+        for s in m.live():
+            path = m.seqs[s]
+            assert sum((n.tokens for n in path), []) == toks[s]
+            assert all(len(n.tokens) == c for n in path[:-1])
+            for n in path:
+                assert rc[n.nid] == sum(1 for s2 in m.live() if n in m.seqs[s2])
+                if len(n.refs) > 1:
+                    if n.nid in frozen:
+                        assert frozen[n.nid] == n.tokens
+                    frozen[n.nid] = list(n.tokens)
+                    assert len(n.tokens) == c          # shared => full
+    for s in list(m.live()):
+        m.remove(s)
+    assert m.used_chunks() == 0 and not m.root.children
