@@ -1,0 +1,243 @@
+/*
+ * pkvt.h -- C ABI of libpkvt: decode-time self-attention over a prefix-tree
+ * KV cache, computed as a two-phase partition, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Source of the method: "ChunkAttention: Efficient Self-Attention with
+ * Prefix-Aware KV Cache and Two-Phase Partition" (Ye, Tao, Huang, Li; ACL
+ * 2024), as digested on its chapterpal page:
+ *   Knowl 1 -- prefix-aware KV cache: KV sliced into chunks of c tokens that
+ *              are nodes of a prefix tree; arrival / decode / departure; pool
+ *              allocator with a free list.
+ *   Knowl 2 -- the two-phase partition (TPP) decode algorithm.
+ *   Knowl 3 -- partial_attn and attn_reduce (online softmax) equations.
+ *   Knowl 5 -- context tuples (C, i, j) sent to the GPU, lazy context copy.
+ * The 1/sqrt(d) score scale is the attention definition's (CachedAttention
+ * digest, "Load-bearing equations"); callers pass it explicitly.
+ *
+ * Conventions
+ *   - Every function returns pkvt_status: 0 on success, a negative code on
+ *     failure.  Nothing throws across the ABI.  pkvt_last_error() returns a
+ *     thread-local message describing the last failure on the calling thread.
+ *   - A pkvt_tree is host state owned by the library (create/destroy).  It is
+ *     not thread-safe: use one host thread per tree at a time.
+ *   - All DEVICE memory (K/V pools, Q, O, metadata, workspace, slot arrays
+ *     for the scatter) is allocated and owned by the caller and passed as
+ *     raw device pointers.  The library never allocates device memory.
+ *   - "stream" arguments are hipStream_t values passed as void*; NULL is the
+ *     default stream.  Device work is asynchronous on that stream.
+ *   - Host pointer arguments are only read/written during the call.
+ *   - Mutating calls that fail leave the tree exactly as it was.
+ *
+ * Shapes: n_heads h (query heads == KV heads), all tensors fp16 (IEEE
+ * binary16).  The kernels support head_dim d in {64, 128} and chunk_size c
+ * in {16, 32, 64, 128}; the host tree and planner accept any c in [1, 4096]
+ * and d >= 1, and the device entry points (pkvt_pool_bytes, pkvt_kv_scatter,
+ * pkvt_plan_upload, pkvt_attn_decode) return UNSUPPORTED_SHAPE otherwise.
+ */
+#ifndef PKVT_H
+#define PKVT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkvt_status;
+
+#define PKVT_OK                     0
+#define PKVT_ERR_INVALID_ARG       -1  /* bad pointer, size, id list, or option            */
+#define PKVT_ERR_NO_CHUNKS         -2  /* chunk pool exhausted (nothing was changed)        */
+#define PKVT_ERR_UNKNOWN_SEQ       -3  /* sequence id is not live                           */
+#define PKVT_ERR_EMPTY_SEQ         -4  /* a sequence with zero tokens                       */
+#define PKVT_ERR_UNSUPPORTED_SHAPE -5  /* head_dim / chunk_size outside the supported set   */
+#define PKVT_ERR_BUFFER_TOO_SMALL  -6  /* caller buffer smaller than required               */
+#define PKVT_ERR_STALE_PLAN        -7  /* no plan, plan older than the tree, or not uploaded */
+#define PKVT_ERR_HIP               -8  /* a HIP runtime call or kernel launch failed        */
+#define PKVT_ERR_HOST_MEMORY       -9  /* host allocation failed                            */
+
+typedef struct pkvt_tree pkvt_tree;
+
+/* ------------------------------------------------------------------------
+ * Device chunk pool (Knowl 1: each tree node owns one chunk holding the K
+ * and V slices, h x c x d each, of its c tokens).
+ *
+ * A chunk id n in [0, pool_chunks) addresses one slice of h*c*d halves in
+ * the K pool and one in the V pool, at element offset n*h*c*d.  Within a
+ * chunk, head j's slice starts at j*c*d and is laid out for the gfx950
+ * matrix cores, not as a plain [c][d] matrix:
+ *   K slice: [d/8][c][8]  -- element (token t, dim x) at ((x/8)*c + t)*8 + x%8
+ *   V slice: [c/4][d][4]  -- element (token t, dim x) at ((t/4)*d + x)*4 + t%4
+ * Callers never compute these offsets: pkvt_kv_scatter writes tokens given
+ * in natural [token][head][dim] order.  pkvt_pool_bytes gives the size of
+ * ONE pool (K or V) for one layer.
+ * ---------------------------------------------------------------------- */
+pkvt_status pkvt_pool_bytes(int32_t n_heads, int32_t head_dim, int32_t chunk_size,
+                            int32_t pool_chunks, size_t* bytes);
+
+/* ------------------------------------------------------------------------
+ * Host prefix tree (Knowl 1).
+ * ---------------------------------------------------------------------- */
+
+/* Create an empty tree over a pool of pool_chunks chunks (all free).
+ * INVALID_ARG if n_heads < 1, head_dim < 1, chunk_size outside [1, 4096],
+ * pool_chunks < 1 or out is NULL. */
+pkvt_status pkvt_tree_create(int32_t n_heads, int32_t head_dim, int32_t chunk_size,
+                             int32_t pool_chunks, pkvt_tree** out);
+void        pkvt_tree_destroy(pkvt_tree* tree);
+
+/* Sequence arrival (Knowl 1): insert n_seqs prompts.
+ *   tokens  : int32 token ids of all prompts, concatenated.
+ *   offsets : int64 [n_seqs+1]; prompt s is tokens[offsets[s] .. offsets[s+1]).
+ * Matching is whole-chunk from token 0: the longest run of FULL chunks whose
+ * c tokens (and therefore whole prefix) equal an existing full chunk on the
+ * path is shared (refcount + 1); the remaining tokens are stored in newly
+ * allocated chunks, inserted as a branch; a partial last chunk is private.
+ * Prompts inserted earlier in the same call can be matched by later ones.
+ * Outputs:
+ *   seq_ids : int32 [n_seqs], the new sequences' ids (never reused).
+ *   slots   : int64 [offsets[n_seqs]]; for each token, chunk_id*c + position
+ *             in the chunk where the caller must store that token's K/V, or
+ *             -1 when the token lives in a chunk that already existed.
+ * Errors: EMPTY_SEQ (a prompt of length 0), NO_CHUNKS (pool exhausted),
+ * INVALID_ARG.  All-or-nothing: on error no sequence is inserted. */
+pkvt_status pkvt_tree_build(pkvt_tree* tree, int32_t n_seqs, const int32_t* tokens,
+                            const int64_t* offsets, int32_t* seq_ids, int64_t* slots);
+
+/* Decode append (Knowl 1): token i goes to sequence seq_ids[i]'s leaf chunk
+ * until that chunk is full, then to a new private leaf chunk.  Several
+ * entries may name the same sequence; they are applied in order.
+ * slots[i] receives chunk_id*c + position for token i (never -1).
+ * Errors: UNKNOWN_SEQ, NO_CHUNKS, INVALID_ARG.  All-or-nothing. */
+pkvt_status pkvt_tree_append(pkvt_tree* tree, int32_t n, const int32_t* seq_ids,
+                             const int32_t* tokens, int64_t* slots);
+
+/* Sequence departure (Knowl 1): drop the sequence from its path; chunks no
+ * live sequence uses any more return to the free list (pool memory is kept)
+ * and their nodes are pruned.  Errors: UNKNOWN_SEQ. */
+pkvt_status pkvt_tree_remove(pkvt_tree* tree, int32_t seq_id);
+
+/* Introspection (tests, accounting). */
+typedef struct {
+    int32_t capacity;       /* pool_chunks                                    */
+    int32_t used_chunks;    /* chunks owned by live nodes                     */
+    int32_t free_chunks;    /* capacity - used_chunks                         */
+    int32_t shared_chunks;  /* live chunks with refcount >= 2                 */
+    int32_t live_seqs;
+    int32_t reserved[3];
+} pkvt_stats;
+pkvt_status pkvt_tree_stats(const pkvt_tree* tree, pkvt_stats* out);
+/* Chunk ids of the sequence's root-to-leaf path.  *n receives the path
+ * length; at most cap ids are written (BUFFER_TOO_SMALL if cap < *n). */
+pkvt_status pkvt_tree_chunk_path(const pkvt_tree* tree, int32_t seq_id, int32_t* ids,
+                                 int32_t cap, int32_t* n);
+/* Number of tokens currently stored for the sequence. */
+pkvt_status pkvt_tree_seq_len(const pkvt_tree* tree, int32_t seq_id, int64_t* len);
+/* Live sequences through the chunk (0 for a free chunk). */
+pkvt_status pkvt_tree_chunk_refcount(const pkvt_tree* tree, int32_t chunk_id, int32_t* refs);
+
+/* ------------------------------------------------------------------------
+ * Plan = context generation (Knowl 5): the host walks the tree and emits the
+ * work of both phases for one decode batch.
+ *
+ * The batch's query rows are q_order[0..b): row r of Q and O belongs to
+ * sequence q_order[r] (distinct live ids, each with >= 1 token).
+ * Sequences are renumbered in depth-first leaf order so that the batch
+ * sequences covered by any node form one contiguous range [i, j) (Knowl 1's
+ * contiguity invariant); a node with j - i >= min_share is "shared" and goes
+ * to phase 1 (Knowl 2: chunks covered by multiple sequences), where chains
+ * of consecutive shared nodes with the same [i, j) are cut into work items of
+ * at most phase1_chunks chunks -- each item is one context tuple (chunk list,
+ * i, j).  Every other chunk is processed per sequence in phase 2, cut into
+ * items of at most phase2_chunks chunks.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t phase1_chunks;  /* max chunks per phase-1 item; 0 = default        */
+    int32_t phase2_chunks;  /* max chunks per phase-2 item; 0 = default        */
+    int32_t min_share;      /* 0 = default 2.  A value above b disables phase 1:
+                               every chunk is read per sequence (plain paged
+                               decode over shared physical chunks).           */
+    int32_t reserved;
+} pkvt_plan_opts;
+
+typedef struct {
+    int32_t b;
+    int32_t phase1_items;   /* context tuples (chunk segment, i, j)            */
+    int32_t phase2_items;
+    int32_t waves;          /* 64-lane work units of the attention kernel      */
+    int32_t workgroups;     /* per head                                        */
+    int32_t slots;          /* partial results per head in the workspace       */
+    int32_t merge_rows;     /* sequences whose partials are merged             */
+    int32_t shared_chunks;  /* distinct chunks read in phase 1                 */
+    int64_t unique_tokens;  /* valid tokens in distinct chunks of the batch    */
+    int64_t logical_tokens; /* sum of the batch's sequence lengths             */
+    int32_t structure_version;
+    int32_t reserved[3];
+} pkvt_plan_info;
+
+/* Build the plan for a batch.  opts may be NULL (defaults).  Reports the
+ * device byte sizes the caller must provide: meta_bytes for the metadata
+ * buffer (pkvt_plan_upload) and workspace_bytes for pkvt_attn_decode (fp32
+ * partial results; 0 when nothing needs merging).  Errors: UNKNOWN_SEQ,
+ * EMPTY_SEQ, INVALID_ARG (b < 1, duplicate ids, bad options). */
+pkvt_status pkvt_plan(pkvt_tree* tree, int32_t b, const int32_t* q_order,
+                      const pkvt_plan_opts* opts, size_t* meta_bytes,
+                      size_t* workspace_bytes);
+pkvt_status pkvt_plan_info_get(const pkvt_tree* tree, pkvt_plan_info* out);
+/* Introspection for tests: copy the current plan's int32 metadata blob (the
+ * exact words pkvt_plan_upload sends) to out.  *n receives its length in
+ * words; BUFFER_TOO_SMALL if cap < *n (nothing copied).  The layout is
+ * internal to the library and versioned by its first word. */
+pkvt_status pkvt_plan_blob(const pkvt_tree* tree, int32_t* out, int32_t cap, int32_t* n);
+
+/* Copy the current plan to the caller's device buffer d_meta (>= meta_bytes)
+ * with an asynchronous host-to-device copy on stream.  Lazy (Knowl 5): when
+ * d_meta already holds this plan nothing is copied, and when only sequence
+ * lengths changed (decode appends that did not open a new chunk) only the
+ * length table is copied.  The library's host staging buffer is not reused
+ * until the previous copy from it has completed.
+ * Errors: STALE_PLAN (no plan / tree changed since pkvt_plan),
+ * BUFFER_TOO_SMALL, HIP. */
+pkvt_status pkvt_plan_upload(pkvt_tree* tree, void* d_meta, size_t meta_bytes, void* stream);
+
+/* Decode attention for the planned batch (Knowl 2), on stream:
+ *   q        : device fp16 [b][h][d], row r = sequence q_order[r]
+ *   k_pool,
+ *   v_pool   : device fp16 pools (layout above); the caller may pass the pools
+ *              of any layer that shares this tree
+ *   out      : device fp16 [b][h][d]; O[r] = softmax(scale * q_r K^T) V over
+ *              every token stored for sequence q_order[r]
+ *   d_meta   : the buffer given to pkvt_plan_upload for the current plan
+ *   workspace: device buffer of >= workspace_bytes (contents need not be
+ *              initialised; it is scratch for this call only)
+ *   scale    : score scale, normally 1/sqrt(d)
+ * Phase 1 (chunk-first, matrix cores) and phase 2 (sequence-first) run in one
+ * launch and leave unnormalised partials (o, m, n) in the workspace; a merge
+ * launch folds them with attn_reduce (Knowl 3) and divides.  Sequences with
+ * a single partial are finalised in place and skip the merge.
+ * Errors: STALE_PLAN (plan not current or not uploaded to d_meta),
+ * BUFFER_TOO_SMALL, INVALID_ARG, HIP. */
+pkvt_status pkvt_attn_decode(const pkvt_tree* tree, const void* d_meta, const void* q,
+                             const void* k_pool, const void* v_pool, void* out,
+                             void* workspace, size_t workspace_bytes, float scale,
+                             void* stream);
+
+/* Write n_tokens tokens' K/V into the pools (the caller's side of arrival
+ * and decode append):
+ *   slots : device int64 [n_tokens] from pkvt_tree_build / pkvt_tree_append;
+ *           entries outside [0, pool_chunks*c) (such as the -1 of tokens
+ *           already stored) are skipped.
+ *   k_new, v_new : device fp16 [n_tokens][h][d], natural order.
+ * Errors: INVALID_ARG, HIP. */
+pkvt_status pkvt_kv_scatter(const pkvt_tree* tree, void* k_pool, void* v_pool,
+                            const int64_t* slots, const void* k_new, const void* v_new,
+                            int64_t n_tokens, void* stream);
+
+const char* pkvt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKVT_H */

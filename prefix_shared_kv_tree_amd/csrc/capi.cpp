@@ -1,0 +1,339 @@
+// C ABI of libpkvt (declared in include/pkvt.h): argument checking, the
+// lazy metadata upload and kernel launches.  No device memory is allocated
+// here; the only HIP allocation is the pinned host staging buffer of the
+// metadata upload, made on the first upload.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "kernels.h"
+#include "pkvt.h"
+#include "plan.h"
+#include "tree.h"
+
+struct pkvt_tree {
+    pkvt::Tree tree;
+    pkvt::Plan plan;
+    // what the last upload put where
+    const void* uploaded_ptr = nullptr;
+    int64_t uploaded_serial = -1;
+    int64_t uploaded_len_version = -1;
+    // pinned staging for the host-to-device copy
+    int32_t* staging = nullptr;
+    size_t staging_words = 0;
+    hipEvent_t staging_done = nullptr;
+    bool copy_in_flight = false;
+
+    pkvt_tree(int32_t h, int32_t d, int32_t c, int32_t n) : tree(h, d, c, n) {}
+    ~pkvt_tree() {
+        if (copy_in_flight) (void)hipEventSynchronize(staging_done);
+        if (staging) (void)hipHostFree(staging);
+        if (staging_done) (void)hipEventDestroy(staging_done);
+    }
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkvt_status fail(pkvt_status code, const std::string& msg) {
+    g_last_error = msg;
+    return code;
+}
+
+pkvt_status hip_fail(hipError_t e, const char* what) {
+    return fail(PKVT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool shape_ok(int32_t d, int32_t c) {
+    return (d == 64 || d == 128) && (c == 16 || c == 32 || c == 64 || c == 128);
+}
+
+bool plan_current(const pkvt_tree* t) {
+    return t->plan.valid && t->plan.struct_version == t->tree.structure_version() &&
+           t->plan.len_version == t->tree.length_version();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkvt_last_error(void) { return g_last_error.c_str(); }
+
+pkvt_status pkvt_pool_bytes(int32_t n_heads, int32_t head_dim, int32_t chunk_size,
+                            int32_t pool_chunks, size_t* bytes) {
+    if (!bytes || n_heads < 1 || pool_chunks < 1)
+        return fail(PKVT_ERR_INVALID_ARG, "pool_bytes: bad arguments");
+    if (!shape_ok(head_dim, chunk_size))
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "pool_bytes: head_dim must be 64 or 128 and "
+                                                "chunk_size one of 16, 32, 64, 128");
+    *bytes = static_cast<size_t>(pool_chunks) * n_heads * chunk_size * head_dim * 2;
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_tree_create(int32_t n_heads, int32_t head_dim, int32_t chunk_size,
+                             int32_t pool_chunks, pkvt_tree** out) {
+    if (!out) return fail(PKVT_ERR_INVALID_ARG, "tree_create: out is NULL");
+    *out = nullptr;
+    if (n_heads < 1 || head_dim < 1 || chunk_size < 1 || chunk_size > 4096 || pool_chunks < 1)
+        return fail(PKVT_ERR_INVALID_ARG, "tree_create: need n_heads, head_dim, pool_chunks >= 1 "
+                                          "and chunk_size in [1, 4096]");
+    try {
+        *out = new pkvt_tree(n_heads, head_dim, chunk_size, pool_chunks);
+    } catch (const std::bad_alloc&) {
+        return fail(PKVT_ERR_HOST_MEMORY, "tree_create: out of host memory");
+    }
+    return PKVT_OK;
+}
+
+void pkvt_tree_destroy(pkvt_tree* tree) { delete tree; }
+
+#define PKVT_GUARD(expr)                                                         \
+    try {                                                                        \
+        expr;                                                                    \
+    } catch (const std::bad_alloc&) {                                            \
+        return fail(PKVT_ERR_HOST_MEMORY, "out of host memory");                 \
+    } catch (const std::exception& e) {                                          \
+        return fail(PKVT_ERR_INVALID_ARG, e.what());                             \
+    }
+
+pkvt_status pkvt_tree_build(pkvt_tree* t, int32_t n_seqs, const int32_t* tokens,
+                            const int64_t* offsets, int32_t* seq_ids, int64_t* slots) {
+    if (!t) return fail(PKVT_ERR_INVALID_ARG, "tree_build: tree is NULL");
+    std::string err;
+    int rc = 0;
+    PKVT_GUARD(rc = t->tree.build(n_seqs, tokens, offsets, seq_ids, slots, err));
+    return rc ? fail(rc, err) : PKVT_OK;
+}
+
+pkvt_status pkvt_tree_append(pkvt_tree* t, int32_t n, const int32_t* seq_ids,
+                             const int32_t* tokens, int64_t* slots) {
+    if (!t) return fail(PKVT_ERR_INVALID_ARG, "tree_append: tree is NULL");
+    std::string err;
+    int rc = 0;
+    PKVT_GUARD(rc = t->tree.append(n, seq_ids, tokens, slots, err));
+    return rc ? fail(rc, err) : PKVT_OK;
+}
+
+pkvt_status pkvt_tree_remove(pkvt_tree* t, int32_t seq_id) {
+    if (!t) return fail(PKVT_ERR_INVALID_ARG, "tree_remove: tree is NULL");
+    std::string err;
+    int rc = 0;
+    PKVT_GUARD(rc = t->tree.remove(seq_id, err));
+    return rc ? fail(rc, err) : PKVT_OK;
+}
+
+pkvt_status pkvt_tree_stats(const pkvt_tree* t, pkvt_stats* out) {
+    if (!t || !out) return fail(PKVT_ERR_INVALID_ARG, "tree_stats: NULL argument");
+    std::memset(out, 0, sizeof(*out));
+    out->capacity = t->tree.N;
+    out->used_chunks = t->tree.used_chunks();
+    out->free_chunks = t->tree.N - out->used_chunks;
+    out->shared_chunks = t->tree.shared_chunks();
+    out->live_seqs = t->tree.live_seqs();
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_tree_chunk_path(const pkvt_tree* t, int32_t seq_id, int32_t* ids, int32_t cap,
+                                 int32_t* n) {
+    if (!t || !n || (cap > 0 && !ids)) return fail(PKVT_ERR_INVALID_ARG, "chunk_path: NULL argument");
+    const pkvt::Seq* s = t->tree.find_seq(seq_id);
+    if (!s) return fail(PKVT_ERR_UNKNOWN_SEQ, "chunk_path: unknown sequence id " + std::to_string(seq_id));
+    *n = static_cast<int32_t>(s->path.size());
+    if (cap < *n) return fail(PKVT_ERR_BUFFER_TOO_SMALL, "chunk_path: cap smaller than the path");
+    std::memcpy(ids, s->path.data(), sizeof(int32_t) * s->path.size());
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_tree_seq_len(const pkvt_tree* t, int32_t seq_id, int64_t* len) {
+    if (!t || !len) return fail(PKVT_ERR_INVALID_ARG, "seq_len: NULL argument");
+    const pkvt::Seq* s = t->tree.find_seq(seq_id);
+    if (!s) return fail(PKVT_ERR_UNKNOWN_SEQ, "seq_len: unknown sequence id " + std::to_string(seq_id));
+    *len = s->len;
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_tree_chunk_refcount(const pkvt_tree* t, int32_t chunk_id, int32_t* refs) {
+    if (!t || !refs) return fail(PKVT_ERR_INVALID_ARG, "chunk_refcount: NULL argument");
+    if (chunk_id < 0 || chunk_id >= t->tree.N)
+        return fail(PKVT_ERR_INVALID_ARG, "chunk_refcount: chunk id out of range");
+    const pkvt::Node& x = t->tree.node(chunk_id);
+    *refs = x.live ? x.refs : 0;
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_plan(pkvt_tree* t, int32_t b, const int32_t* q_order, const pkvt_plan_opts* opts,
+                      size_t* meta_bytes, size_t* workspace_bytes) {
+    if (!t) return fail(PKVT_ERR_INVALID_ARG, "plan: tree is NULL");
+    pkvt::PlanOpts o;
+    if (opts) {
+        o.phase1_chunks = opts->phase1_chunks;
+        o.phase2_chunks = opts->phase2_chunks;
+        o.min_share = opts->min_share;
+    }
+    std::string err;
+    int rc = 0;
+    PKVT_GUARD(rc = pkvt::make_plan(t->tree, b, q_order, o, t->plan, err));
+    if (rc) return fail(rc, err);
+    if (meta_bytes) *meta_bytes = t->plan.blob.size() * sizeof(int32_t);
+    if (workspace_bytes)
+        *workspace_bytes = static_cast<size_t>(t->plan.n_slots) * t->tree.H * (t->tree.D + 2) *
+                           sizeof(float);
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_plan_info_get(const pkvt_tree* t, pkvt_plan_info* out) {
+    if (!t || !out) return fail(PKVT_ERR_INVALID_ARG, "plan_info: NULL argument");
+    if (!t->plan.valid) return fail(PKVT_ERR_STALE_PLAN, "plan_info: no plan");
+    std::memset(out, 0, sizeof(*out));
+    const pkvt::Plan& p = t->plan;
+    out->b = p.b;
+    out->phase1_items = p.phase1_items;
+    out->phase2_items = p.phase2_items;
+    out->waves = p.n_waves;
+    out->workgroups = p.n_wg;
+    out->slots = p.n_slots;
+    out->merge_rows = p.n_merge;
+    out->shared_chunks = p.shared_chunks;
+    out->unique_tokens = p.unique_tokens;
+    out->logical_tokens = p.logical_tokens;
+    out->structure_version = static_cast<int32_t>(p.serial & 0x7fffffff);
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_plan_blob(const pkvt_tree* t, int32_t* out, int32_t cap, int32_t* n) {
+    if (!t || !n || (cap > 0 && !out)) return fail(PKVT_ERR_INVALID_ARG, "plan_blob: NULL argument");
+    if (!t->plan.valid) return fail(PKVT_ERR_STALE_PLAN, "plan_blob: no plan");
+    *n = static_cast<int32_t>(t->plan.blob.size());
+    if (cap < *n) return fail(PKVT_ERR_BUFFER_TOO_SMALL, "plan_blob: cap smaller than the plan");
+    std::memcpy(out, t->plan.blob.data(), t->plan.blob.size() * sizeof(int32_t));
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_plan_upload(pkvt_tree* t, void* d_meta, size_t meta_bytes, void* stream) {
+    if (!t || !d_meta) return fail(PKVT_ERR_INVALID_ARG, "plan_upload: NULL argument");
+    if (!plan_current(t)) return fail(PKVT_ERR_STALE_PLAN, "plan_upload: no plan for the current tree");
+    if (!shape_ok(t->tree.D, t->tree.C))
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "plan_upload: the kernels need head_dim 64 or 128 "
+                                                "and chunk_size 16, 32, 64 or 128");
+    const pkvt::Plan& p = t->plan;
+    const size_t words = p.blob.size();
+    if (meta_bytes < words * sizeof(int32_t))
+        return fail(PKVT_ERR_BUFFER_TOO_SMALL, "plan_upload: meta buffer smaller than the plan");
+    size_t first = 0, count = words;
+    if (t->uploaded_ptr == d_meta && t->uploaded_serial == p.serial) {
+        if (t->uploaded_len_version == p.len_version) return PKVT_OK;    // already there
+        first = static_cast<size_t>(p.blob[pkvt::kOffSeqlen]);           // lengths only
+        count = static_cast<size_t>(p.b);
+    }
+    hipError_t e;
+    if (t->copy_in_flight) {
+        if ((e = hipEventSynchronize(t->staging_done)) != hipSuccess) return hip_fail(e, "plan_upload");
+        t->copy_in_flight = false;
+    }
+    if (!t->staging_done && (e = hipEventCreateWithFlags(&t->staging_done, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "plan_upload: event");
+    if (t->staging_words < words) {
+        if (t->staging) (void)hipHostFree(t->staging);
+        t->staging = nullptr;
+        t->staging_words = 0;
+        if ((e = hipHostMalloc(reinterpret_cast<void**>(&t->staging), words * sizeof(int32_t),
+                               hipHostMallocDefault)) != hipSuccess)
+            return hip_fail(e, "plan_upload: pinned staging");
+        t->staging_words = words;
+    }
+    std::memcpy(t->staging + first, p.blob.data() + first, count * sizeof(int32_t));
+    auto s = static_cast<hipStream_t>(stream);
+    if ((e = hipMemcpyAsync(static_cast<int32_t*>(d_meta) + first, t->staging + first,
+                            count * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
+        return hip_fail(e, "plan_upload: copy");
+    if ((e = hipEventRecord(t->staging_done, s)) != hipSuccess) return hip_fail(e, "plan_upload: record");
+    t->copy_in_flight = true;
+    t->uploaded_ptr = d_meta;
+    t->uploaded_serial = p.serial;
+    t->uploaded_len_version = p.len_version;
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_attn_decode(const pkvt_tree* t, const void* d_meta, const void* q,
+                             const void* k_pool, const void* v_pool, void* out, void* workspace,
+                             size_t workspace_bytes, float scale, void* stream) {
+    if (!t || !d_meta || !q || !k_pool || !v_pool || !out)
+        return fail(PKVT_ERR_INVALID_ARG, "attn_decode: NULL argument");
+    if (!std::isfinite(scale)) return fail(PKVT_ERR_INVALID_ARG, "attn_decode: scale is not finite");
+    if (!plan_current(t)) return fail(PKVT_ERR_STALE_PLAN, "attn_decode: plan is older than the tree");
+    if (!shape_ok(t->tree.D, t->tree.C))
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "attn_decode: unsupported head_dim / chunk_size");
+    const pkvt::Plan& p = t->plan;
+    if (t->uploaded_ptr != d_meta || t->uploaded_serial != p.serial ||
+        t->uploaded_len_version != p.len_version)
+        return fail(PKVT_ERR_STALE_PLAN, "attn_decode: the current plan is not uploaded to d_meta");
+    const int32_t H = t->tree.H, D = t->tree.D, C = t->tree.C;
+    const size_t need = static_cast<size_t>(p.n_slots) * H * (D + 2) * sizeof(float);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PKVT_ERR_BUFFER_TOO_SMALL, "attn_decode: workspace smaller than the plan needs");
+    const int32_t* m = static_cast<const int32_t*>(d_meta);
+    float* part_o = static_cast<float*>(workspace);
+    float* part_ml = part_o ? part_o + static_cast<size_t>(p.n_slots) * H * D : nullptr;
+    auto s = static_cast<hipStream_t>(stream);
+
+    pkvt::AttnArgs a{};
+    a.wg = m + p.blob[pkvt::kOffWg];
+    a.waves = m + p.blob[pkvt::kOffWaves];
+    a.chunks = m + p.blob[pkvt::kOffChunks];
+    a.rows = m + p.blob[pkvt::kOffRows];
+    a.seqlen = m + p.blob[pkvt::kOffSeqlen];
+    a.q = q;
+    a.kpool = k_pool;
+    a.vpool = v_pool;
+    a.out = out;
+    a.part_o = part_o;
+    a.part_ml = part_ml;
+    a.H = H;
+    a.n_wg = p.n_wg;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    hipError_t e = pkvt::launch_attn(a, D, C, s);
+    if (e != hipSuccess) return hip_fail(e, "attn_decode: attention kernel");
+    if (p.n_merge > 0) {
+        pkvt::MergeArgs mg{};
+        mg.merge_rows = m + p.blob[pkvt::kOffMerge];
+        mg.mptr = m + p.blob[pkvt::kOffMptr];
+        mg.mslots = m + p.blob[pkvt::kOffMslots];
+        mg.rows = a.rows;
+        mg.part_o = part_o;
+        mg.part_ml = part_ml;
+        mg.out = out;
+        mg.H = H;
+        mg.n_merge = p.n_merge;
+        e = pkvt::launch_merge(mg, D, s);
+        if (e != hipSuccess) return hip_fail(e, "attn_decode: merge kernel");
+    }
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_kv_scatter(const pkvt_tree* t, void* k_pool, void* v_pool, const int64_t* slots,
+                            const void* k_new, const void* v_new, int64_t n_tokens, void* stream) {
+    if (!t || n_tokens < 0) return fail(PKVT_ERR_INVALID_ARG, "kv_scatter: bad arguments");
+    if (!shape_ok(t->tree.D, t->tree.C))
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "kv_scatter: unsupported head_dim / chunk_size");
+    if (n_tokens == 0) return PKVT_OK;
+    if (!k_pool || !v_pool || !slots || !k_new || !v_new)
+        return fail(PKVT_ERR_INVALID_ARG, "kv_scatter: NULL argument");
+    pkvt::ScatterArgs a{};
+    a.kpool = k_pool;
+    a.vpool = v_pool;
+    a.slots = slots;
+    a.knew = k_new;
+    a.vnew = v_new;
+    a.n_tokens = n_tokens;
+    a.slot_limit = static_cast<int64_t>(t->tree.N) * t->tree.C;
+    a.H = t->tree.H;
+    hipError_t e = pkvt::launch_scatter(a, t->tree.D, t->tree.C, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kv_scatter");
+    return PKVT_OK;
+}
+
+}  // extern "C"

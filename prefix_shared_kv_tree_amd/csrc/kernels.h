@@ -1,0 +1,55 @@
+// Launch interface between the C ABI (capi.cpp) and the HIP kernels
+// (attn.hip).  Plain pointers only; fp16 tensors are passed as void*.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace pkvt {
+
+struct AttnArgs {
+    const int32_t* wg;        // [n_wg][4] wave task per wave slot (-1 idle)
+    const int32_t* waves;     // [n_waves][8] WaveDesc
+    const int32_t* chunks;    // chunk ids
+    const int32_t* rows;      // [b] depth-first position -> query row
+    const int32_t* seqlen;    // [b] tokens per depth-first position
+    const void* q;            // fp16 [b][H][D]
+    const void* kpool;        // fp16 [N][H][D/8][C][8]
+    const void* vpool;        // fp16 [N][H][C/4][D][4]
+    void* out;                // fp16 [b][H][D]
+    float* part_o;            // [n_slots][H][D]
+    float* part_ml;           // [n_slots][H][2]  (m in log2 units, n)
+    int32_t H;
+    int32_t n_wg;
+    float scale_log2e;        // score scale * log2(e)
+};
+
+struct MergeArgs {
+    const int32_t* merge_rows;  // [n_merge] depth-first positions
+    const int32_t* mptr;        // [b+1]
+    const int32_t* mslots;      // partial slots
+    const int32_t* rows;        // [b] depth-first position -> query row
+    const float* part_o;
+    const float* part_ml;
+    void* out;
+    int32_t H;
+    int32_t n_merge;
+};
+
+struct ScatterArgs {
+    void* kpool;
+    void* vpool;
+    const int64_t* slots;
+    const void* knew;         // fp16 [n][H][D]
+    const void* vnew;
+    int64_t n_tokens;
+    int64_t slot_limit;       // pool_chunks * C
+    int32_t H;
+};
+
+hipError_t launch_attn(const AttnArgs& a, int D, int C, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, int D, hipStream_t s);
+hipError_t launch_scatter(const ScatterArgs& a, int D, int C, hipStream_t s);
+
+}  // namespace pkvt

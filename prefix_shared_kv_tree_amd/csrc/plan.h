@@ -1,0 +1,84 @@
+// Context generation for one decode batch: the host side of the two-phase
+// partition ("ChunkAttention ..." chapterpal digest, Knowl 2 and Knowl 5).
+//
+// The plan is a flat int32 blob that is copied to device memory once and
+// re-used for every layer and every decode step until the tree structure
+// changes (lazy context copy, Knowl 5).  Layout (word offsets in the header):
+//
+//   header   [kHeaderWords]
+//   wg       [n_wg][4]         wave task index per wave slot, -1 = idle
+//   waves    [n_waves][8]      WaveDesc
+//   chunks   [...]             chunk ids referenced by the waves
+//   rows     [b]               depth-first position -> query row of Q / O
+//   merge    [n_merge]         depth-first positions whose partials are merged
+//   mptr     [b+1]             CSR over depth-first positions ...
+//   mslots   [...]             ... of partial slot indices
+//   seqlen   [b]               tokens stored per depth-first position (last,
+//                              so that a length-only update copies one range)
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tree.h"
+
+namespace pkvt {
+
+// One 64-lane unit of work of the attention kernel: up to 16 query rows
+// against a list of chunks of one head (the head comes from the grid).
+struct WaveDesc {
+    int32_t chunk_off;   // first entry in the chunks section
+    int32_t n_chunks;
+    int32_t key_base;    // index, within its sequence, of the first key (len_row >= 0)
+    int32_t len_row;     // depth-first row whose length bounds the keys, -1 = all full
+    int32_t row_lo;      // depth-first position of query row 0
+    int32_t n_rows;      // 1..16
+    int32_t out;         // partial slot of row 0, or -1: write O directly (n_rows == 1)
+    int32_t pad;
+};
+static_assert(sizeof(WaveDesc) == 32, "WaveDesc is 8 int32");
+
+enum HeaderField {
+    kMagic = 0, kSerial, kB, kNWaves, kNWg, kNSlots, kNMerge,
+    kOffWg, kOffWaves, kOffChunks, kOffRows, kOffMerge, kOffMptr, kOffMslots, kOffSeqlen,
+    kTotalWords, kHeaderWords = 16
+};
+constexpr int32_t kPlanMagic = 0x504b5654;   // "PKVT"
+constexpr int32_t kWavesPerWg = 4;
+constexpr int32_t kRowsPerWave = 16;
+constexpr int32_t kKeysPerStep = 64;
+
+struct PlanOpts {
+    int32_t phase1_chunks = 0;
+    int32_t phase2_chunks = 0;
+    int32_t min_share = 2;
+    bool operator==(const PlanOpts& o) const {
+        return phase1_chunks == o.phase1_chunks && phase2_chunks == o.phase2_chunks &&
+               min_share == o.min_share;
+    }
+};
+
+struct Plan {
+    bool valid = false;
+    int64_t serial = 0;               // identifies the structure part of the blob
+    int64_t struct_version = -1;      // tree versions the plan was built from
+    int64_t len_version = -1;
+    int32_t b = 0;
+    std::vector<int32_t> q_order;
+    PlanOpts opts;
+    std::vector<int32_t> blob;
+    // summary
+    int32_t phase1_items = 0, phase2_items = 0, n_waves = 0, n_wg = 0, n_slots = 0, n_merge = 0;
+    int32_t shared_chunks = 0;
+    int64_t unique_tokens = 0, logical_tokens = 0;
+    std::vector<int32_t> dfs_seq;     // depth-first position -> sequence id (tests)
+
+    int32_t off(HeaderField f) const { return blob[f]; }
+};
+
+// Build (or refresh) the plan.  Returns a PKVT_* status.
+int make_plan(const Tree& tree, int32_t b, const int32_t* q_order, const PlanOpts& opts,
+              Plan& plan, std::string& err);
+
+}  // namespace pkvt

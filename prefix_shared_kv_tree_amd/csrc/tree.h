@@ -1,0 +1,85 @@
+// Host prefix tree over a fixed pool of KV chunks.
+//
+// Follows "ChunkAttention: Efficient Self-Attention with Prefix-Aware KV Cache
+// and Two-Phase Partition" (chapterpal digest), Knowl 1: the KV cache is cut
+// along the sequence axis into chunks of c tokens; chunks are nodes of a
+// prefix tree (a forest: every distinct first chunk is a root child); every
+// root-to-leaf path is one sequence; a pool allocator hands out fixed-size
+// chunks and takes freed ones back without releasing memory.
+//
+// Readings of the page (it leaves them open):
+//   * whole-chunk matching from token 0: only FULL chunks are shared, a
+//     partial tail chunk is private, decode never writes into a shared chunk;
+//   * a chunk filled by decode appends becomes matchable; nodes are never
+//     merged; among live full children with equal tokens a lookup takes the
+//     earliest created one.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+namespace pkvt {
+
+struct Node {
+    int32_t parent = -1;                 // node id of the parent (the root is id N)
+    int32_t fill = 0;                    // tokens stored in the chunk
+    int32_t refs = 0;                    // live sequences whose path holds this node
+    int64_t created = 0;                 // creation counter (lookup tie-break)
+    bool live = false;
+    uint64_t key_hash = 0;               // hash of the c tokens, valid when full
+    std::vector<int32_t> children;       // creation order
+    std::vector<int32_t> tokens;         // the fill tokens
+    // full live children keyed by token hash, each bucket in creation order
+    std::unordered_map<uint64_t, std::vector<int32_t>> full_children;
+};
+
+struct Seq {
+    std::vector<int32_t> path;           // node (= chunk) ids, root to leaf
+    int64_t len = 0;
+};
+
+class Tree {
+public:
+    Tree(int32_t h, int32_t d, int32_t c, int32_t pool_chunks);
+
+    int32_t H, D, C, N;
+    int32_t root() const { return N; }
+
+    // Return codes are the PKVT_* status values; err receives a message.
+    int build(int32_t n_seqs, const int32_t* tokens, const int64_t* offsets,
+              int32_t* seq_ids, int64_t* slots, std::string& err);
+    int append(int32_t n, const int32_t* seq_ids, const int32_t* tokens,
+               int64_t* slots, std::string& err);
+    int remove(int32_t seq_id, std::string& err);
+
+    const Seq* find_seq(int32_t id) const;
+    const Node& node(int32_t id) const { return nodes_[id]; }
+    int32_t used_chunks() const { return N - (int32_t)free_.size(); }
+    int32_t shared_chunks() const;
+    int32_t live_seqs() const { return (int32_t)seqs_.size(); }
+
+    // Bumped on every change of which chunks form which paths.
+    int64_t structure_version() const { return struct_version_; }
+    // Bumped on every decode append (sequence lengths change).
+    int64_t length_version() const { return len_version_; }
+
+private:
+    std::vector<Node> nodes_;            // N chunk nodes + the root at index N
+    std::vector<int32_t> free_;          // stack of free chunk ids
+    std::unordered_map<int32_t, Seq> seqs_;
+    int32_t next_seq_ = 0;
+    int64_t next_created_ = 0;
+    int64_t struct_version_ = 0;
+    int64_t len_version_ = 0;
+
+    uint64_t hash_tokens(const int32_t* t) const;
+    int32_t find_full_child(int32_t parent, const int32_t* t) const;
+    void index_full(int32_t id);
+    void unindex_full(int32_t id);
+    int32_t alloc_node(int32_t parent, const int32_t* t, int32_t n);
+    void free_node(int32_t id);
+};
+
+}  // namespace pkvt

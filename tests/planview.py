@@ -1,0 +1,112 @@
+"""Test helper: decode a plan blob (pkvt_plan_blob) and check it against the
+tree's own paths.  Knows the blob layout documented in csrc/plan.h."""
+from __future__ import annotations
+
+from collections import defaultdict
+
+import numpy as np
+
+H_MAGIC, H_SERIAL, H_B, H_NWAVES, H_NWG, H_NSLOTS, H_NMERGE = range(7)
+H_OFF_WG, H_OFF_WAVES, H_OFF_CHUNKS, H_OFF_ROWS, H_OFF_MERGE, H_OFF_MPTR, H_OFF_MSLOTS, \
+    H_OFF_SEQLEN, H_TOTAL = range(7, 16)
+MAGIC = 0x504B5654
+
+
+def parse(blob: np.ndarray) -> dict:
+    b = int(blob[H_B])
+    nw, ng = int(blob[H_NWAVES]), int(blob[H_NWG])
+    waves = blob[blob[H_OFF_WAVES]:blob[H_OFF_WAVES] + nw * 8].reshape(nw, 8)
+    chunks_base = int(blob[H_OFF_CHUNKS])
+    mptr = blob[blob[H_OFF_MPTR]:blob[H_OFF_MPTR] + b + 1]
+    return dict(
+        magic=int(blob[H_MAGIC]), b=b, n_slots=int(blob[H_NSLOTS]),
+        wg=blob[blob[H_OFF_WG]:blob[H_OFF_WG] + ng * 4].reshape(ng, 4),
+        waves=waves,
+        wave_chunks=[blob[chunks_base + w[0]:chunks_base + w[0] + w[1]] for w in waves],
+        rows=blob[blob[H_OFF_ROWS]:blob[H_OFF_ROWS] + b],
+        merge=blob[blob[H_OFF_MERGE]:blob[H_OFF_MERGE] + int(blob[H_NMERGE])],
+        mptr=mptr,
+        mslots=blob[blob[H_OFF_MSLOTS]:blob[H_OFF_MSLOTS] + int(mptr[-1])],
+        seqlen=blob[blob[H_OFF_SEQLEN]:blob[H_OFF_SEQLEN] + b],
+        total=int(blob[H_TOTAL]),
+    )
+
+
+def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: int = 2,
+               max_rows: int = 16):
+    """paths / lens: seq id -> chunk path / token count (from the tree).
+    Raises AssertionError on any violation."""
+    assert plan["magic"] == MAGIC
+    b = plan["b"]
+    q_order = [int(x) for x in q_order]
+    rows = [int(r) for r in plan["rows"]]
+    assert sorted(rows) == list(range(b)), "rows is not a permutation"
+    seq_at = [q_order[r] for r in rows]                  # depth-first position -> seq id
+    for p in range(b):
+        assert plan["seqlen"][p] == lens[seq_at[p]]
+    # batch coverage of every chunk
+    cover = defaultdict(set)
+    for p in range(b):
+        for x in paths[seq_at[p]]:
+            cover[int(x)].add(p)
+    # contiguity: the positions covering any chunk form one range
+    for x, ps in cover.items():
+        assert max(ps) - min(ps) + 1 == len(ps), f"chunk {x} covers a non-contiguous range"
+    # every (position, path chunk) is visited exactly once
+    seen = defaultdict(int)
+    chunk_rows = defaultdict(set)
+    slot_rows = {}
+    direct = set()
+    for wi, (w, ch) in enumerate(zip(plan["waves"], plan["wave_chunks"])):
+        chunk_off, n_chunks, key_base, len_row, row_lo, n_rows, out, _ = [int(v) for v in w]
+        assert n_chunks == len(ch) >= 1 and 1 <= n_rows <= max_rows
+        multi = None
+        for x in ch:
+            x = int(x)
+            for p in range(row_lo, row_lo + n_rows):
+                assert x in [int(y) for y in paths[seq_at[p]]], "wave reads a chunk not on the row's path"
+                seen[(p, x)] += 1
+                chunk_rows[x].add(p)
+            shared = len(cover[x]) >= min_share
+            assert multi in (None, shared)
+            multi = shared
+        if not multi:
+            assert n_rows == 1
+        # key bound: only the wave that ends at the leaf uses the length
+        p0 = row_lo
+        path = [int(y) for y in paths[seq_at[p0]]]
+        last = path.index(int(ch[-1]))
+        if last == len(path) - 1 and not multi:
+            assert len_row == p0 and key_base == path.index(int(ch[0])) * c
+        else:
+            assert len_row == -1
+            # all chunks of such a wave are full
+            for x in ch:
+                k = path.index(int(x))
+                assert (k + 1) * c <= lens[seq_at[p0]]
+        if out < 0:
+            assert n_rows == 1
+            direct.add(row_lo)
+        else:
+            for r in range(n_rows):
+                assert out + r not in slot_rows, "slot written twice"
+                slot_rows[out + r] = row_lo + r
+    for p in range(b):
+        for x in paths[seq_at[p]]:
+            assert seen.pop((p, int(x)), 0) == 1, f"chunk {x} of position {p} not visited once"
+    assert not seen
+    for x, ps in chunk_rows.items():
+        assert ps == cover[x]
+    # merge lists
+    assert set(slot_rows) == set(range(plan["n_slots"]))
+    merge = set(int(m) for m in plan["merge"])
+    for p in range(b):
+        sl = [int(s) for s in plan["mslots"][plan["mptr"][p]:plan["mptr"][p + 1]]]
+        assert sorted(sl) == sorted(s for s, q in slot_rows.items() if q == p)
+        if p in direct:
+            assert not sl and p not in merge
+        else:
+            assert sl and p in merge
+    # workgroup table: every wave once
+    used = [int(v) for v in plan["wg"].ravel() if v >= 0]
+    assert sorted(used) == list(range(len(plan["waves"])))
