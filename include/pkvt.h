@@ -151,30 +151,41 @@ pkvt_status pkvt_tree_chunk_refcount(const pkvt_tree* tree, int32_t chunk_id, in
  * of consecutive shared nodes with the same [i, j) are cut into work items of
  * at most phase1_chunks chunks -- each item is one context tuple (chunk list,
  * i, j).  Every other chunk is processed per sequence in phase 2, cut into
- * items of at most phase2_chunks chunks.
+ * items of at most phase2_chunks chunks.  Each (item, group of 16 query
+ * rows, head) is one task of a 64-lane wave; the attention kernel runs a
+ * fixed grid of persistent workgroups of 4 waves and every wave walks a task
+ * list filled longest-first by the planner (the row groups of one phase-1
+ * item share a workgroup, so its chunks are fetched once per CU).  By
+ * default items are cut at the mean per-wave load, so no task is longer
+ * than what a perfectly balanced wave would do.
  * ---------------------------------------------------------------------- */
 typedef struct {
-    int32_t phase1_chunks;  /* max chunks per phase-1 item; 0 = default        */
-    int32_t phase2_chunks;  /* max chunks per phase-2 item; 0 = default        */
+    int32_t phase1_chunks;  /* max chunks per phase-1 item; 0 = derived from
+                               the mean per-wave load (see below)             */
+    int32_t phase2_chunks;  /* max chunks per phase-2 item; 0 = derived       */
     int32_t min_share;      /* 0 = default 2.  A value above b disables phase 1:
                                every chunk is read per sequence (plain paged
                                decode over shared physical chunks).           */
-    int32_t reserved;
+    int32_t workgroups;     /* persistent workgroups of the attention kernel;
+                               0 = 2 per compute unit of the current device
+                               (512 when no device is visible)                */
 } pkvt_plan_opts;
 
 typedef struct {
     int32_t b;
     int32_t phase1_items;   /* context tuples (chunk segment, i, j)            */
     int32_t phase2_items;
-    int32_t waves;          /* 64-lane work units of the attention kernel      */
-    int32_t workgroups;     /* per head                                        */
+    int32_t waves;          /* wave descriptors (item x row group)             */
+    int32_t workgroups;     /* persistent workgroups of the attention kernel   */
     int32_t slots;          /* partial results per head in the workspace       */
     int32_t merge_rows;     /* sequences whose partials are merged             */
     int32_t shared_chunks;  /* distinct chunks read in phase 1                 */
     int64_t unique_tokens;  /* valid tokens in distinct chunks of the batch    */
     int64_t logical_tokens; /* sum of the batch's sequence lengths             */
     int32_t structure_version;
-    int32_t reserved[3];
+    int32_t tasks;          /* wave tasks (waves x heads)                      */
+    int32_t phase1_split;   /* chunks per phase-1 item actually used           */
+    int32_t phase2_split;   /* chunks per phase-2 item actually used           */
 } pkvt_plan_info;
 
 /* Build the plan for a batch.  opts may be NULL (defaults).  Reports the
@@ -223,6 +234,17 @@ pkvt_status pkvt_attn_decode(const pkvt_tree* tree, const void* d_meta, const vo
                              const void* k_pool, const void* v_pool, void* out,
                              void* workspace, size_t workspace_bytes, float scale,
                              void* stream);
+
+/* pkvt_attn_decode with a profiling hook: when attn_event is not NULL it
+ * must be a hipEvent_t (passed as void*) created on the current device; it
+ * is recorded on stream right after the attention kernel is queued and
+ * before the merge kernel, so that the caller can time the two launches
+ * separately with events on the same stream.  Same arguments and errors as
+ * pkvt_attn_decode otherwise. */
+pkvt_status pkvt_attn_decode_ex(const pkvt_tree* tree, const void* d_meta, const void* q,
+                                const void* k_pool, const void* v_pool, void* out,
+                                void* workspace, size_t workspace_bytes, float scale,
+                                void* stream, void* attn_event);
 
 /* Write n_tokens tokens' K/V into the pools (the caller's side of arrival
  * and decode append):

@@ -39,7 +39,7 @@ class Stats(C.Structure):
 
 class PlanOpts(C.Structure):
     _fields_ = [("phase1_chunks", C.c_int32), ("phase2_chunks", C.c_int32),
-                ("min_share", C.c_int32), ("reserved", C.c_int32)]
+                ("min_share", C.c_int32), ("workgroups", C.c_int32)]
 
 
 class PlanInfo(C.Structure):
@@ -47,7 +47,8 @@ class PlanInfo(C.Structure):
                 ("waves", C.c_int32), ("workgroups", C.c_int32), ("slots", C.c_int32),
                 ("merge_rows", C.c_int32), ("shared_chunks", C.c_int32),
                 ("unique_tokens", C.c_int64), ("logical_tokens", C.c_int64),
-                ("structure_version", C.c_int32), ("reserved", C.c_int32 * 3)]
+                ("structure_version", C.c_int32), ("tasks", C.c_int32),
+                ("phase1_split", C.c_int32), ("phase2_split", C.c_int32)]
 
 
 _i32p = C.POINTER(C.c_int32)
@@ -72,6 +73,7 @@ _SIGNATURES = {
     "pkvt_plan_blob": [_vp, _i32p, C.c_int32, _i32p],
     "pkvt_plan_upload": [_vp, _vp, _sz, _vp],
     "pkvt_attn_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp],
+    "pkvt_attn_decode_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp, _vp],
     "pkvt_kv_scatter": [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int64, _vp],
     "pkvt_last_error": [],
 }
@@ -209,10 +211,10 @@ def pkvt_tree_chunk_refcount(tree: int, chunk_id: int) -> int:
 # ---- plan ---------------------------------------------------------------------
 
 def pkvt_plan(tree: int, q_order, phase1_chunks: int = 0, phase2_chunks: int = 0,
-              min_share: int = 0) -> Tuple[int, int]:
+              min_share: int = 0, workgroups: int = 0) -> Tuple[int, int]:
     """Plan a batch; returns (meta_bytes, workspace_bytes)."""
     q = _i32(q_order)
-    opts = PlanOpts(phase1_chunks, phase2_chunks, min_share, 0)
+    opts = PlanOpts(phase1_chunks, phase2_chunks, min_share, workgroups)
     mb, wb = _sz(), _sz()
     _check("pkvt_plan", load().pkvt_plan(tree, q.size, _p32(q) if q.size else None,
                                          C.byref(opts), C.byref(mb), C.byref(wb)))
@@ -246,6 +248,14 @@ def pkvt_attn_decode(tree: int, d_meta: int, q: int, k_pool: int, v_pool: int, o
     _check("pkvt_attn_decode", load().pkvt_attn_decode(tree, d_meta, q, k_pool, v_pool, out,
                                                        workspace or None, workspace_bytes,
                                                        float(scale), stream or None))
+
+
+def pkvt_attn_decode_ex(tree: int, d_meta: int, q: int, k_pool: int, v_pool: int, out: int,
+                        workspace: int, workspace_bytes: int, scale: float, stream: int = 0,
+                        attn_event: int = 0) -> None:
+    _check("pkvt_attn_decode_ex", load().pkvt_attn_decode_ex(
+        tree, d_meta, q, k_pool, v_pool, out, workspace or None, workspace_bytes, float(scale),
+        stream or None, attn_event or None))
 
 
 def pkvt_kv_scatter(tree: int, k_pool: int, v_pool: int, slots: int, k_new: int, v_new: int,

@@ -12,13 +12,20 @@
 //
 // One kernel serves both phases.  Its unit of work is a wave task: up to 16
 // query rows of one head against a list of chunks.  A phase-1 item with R
-// rows becomes ceil(R/16) wave tasks placed in one workgroup, so the waves
-// that read the same shared chunks share the CU's caches; a phase-2 item is
-// one wave task with one query row.  Each wave streams its chunks 64 keys at
-// a time through the matrix cores:
+// rows gives ceil(R/16) tasks per head that the planner places on the waves
+// of one workgroup, so the waves reading the same shared chunks share the
+// CU's caches; a phase-2 item gives one single-row task per head.  The grid
+// is a fixed set of persistent workgroups; every wave walks its own task
+// list (filled longest-first by the planner) and streams the tasks' chunks
+// 64 keys at a time through the matrix cores:
 //
 //   S^T (keys x rows)  = K  . Q^T    v_mfma_f32_16x16x32_f16, K as the A operand
 //   O^T (dims x rows) += V^T . P^T   v_mfma_f32_16x16x32_f16, V^T as the A operand
+//
+// The loads of the next step -- or of the next task's first step, with its
+// queries -- are issued as soon as the registers they land in are free, so
+// a wave keeps about one step (32 KiB of K and V) in flight across task
+// boundaries too.  K and V are read once, with non-temporal loads.
 //
 // With one query row (phase 2) 15 of the 16 MFMA columns idle; that costs
 // nothing measurable, because a decode step does ~1 FLOP per byte while the
@@ -53,121 +60,151 @@ __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_rea
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wave-uniform description of one task.
+struct Task {
+    const int32_t* chunks;   // the task's chunk ids
+    int n_valid;             // keys to attend over
+    int n_steps;             // ceil(n_valid / 64)
+    int row_lo;              // depth-first position of query row 0
+    int n_rows;
+    int out;                 // partial slot of row 0, or -1: write O
+    int head;
+};
+
+template <int C>
+__device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
+    const int wave_id = a.tasks[2 * idx];
+    Task t;
+    t.head = a.tasks[2 * idx + 1];
+    const int32_t* wd = a.waves + 8 * wave_id;
+    const int n_chunks = wd[1];
+    const int key_base = wd[2];
+    const int len_row = wd[3];
+    t.chunks = a.chunks + wd[0];
+    t.row_lo = wd[4];
+    t.n_rows = wd[5];
+    t.out = wd[6];
+    int n_valid = n_chunks * C;
+    if (len_row >= 0) n_valid = min(n_valid, a.seqlen[len_row] - key_base);
+    t.n_valid = n_valid;
+    t.n_steps = (n_valid + kStep - 1) / kStep;
+    return t;
+}
+
 template <int D, int C>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void attn_kernel(AttnArgs a) {
     static_assert(D % 32 == 0 && C % 16 == 0, "tile shape");
     constexpr int KS = D / 32;     // 32-dim k-steps of Q K^T
     constexpr int DT = D / 16;     // 16-dim output tiles of P V
     const int H = a.H;
-    const int g = blockIdx.x / H;
-    const int head = blockIdx.x - g * H;
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int col = lane & 15;     // MFMA row/column index held by this lane
     const int grp = lane >> 4;     // which 8-element k slice of the fragment
-
-    const int task = a.wg[g * kWaves + wave];
-    if (task < 0) return;
-    const int32_t* wd = a.waves + task * 8;
-    const int n_chunks = wd[1];
-    const int key_base = wd[2];
-    const int len_row = wd[3];
-    const int row_lo = wd[4];
-    const int n_rows = wd[5];
-    const int out_slot = wd[6];
-    const int32_t* chunks = a.chunks + wd[0];
-    int n_valid = n_chunks * C;
-    if (len_row >= 0) n_valid = min(n_valid, a.seqlen[len_row] - key_base);
-    const int n_steps = (n_valid + kStep - 1) / kStep;
+    const int lane_id = blockIdx.x * kWaves + wave;
+    const int first = a.lists[2 * lane_id];
+    const int count = a.lists[2 * lane_id + 1];
+    if (count == 0) return;
 
     const _Float16* __restrict__ kpool = static_cast<const _Float16*>(a.kpool);
     const _Float16* __restrict__ vpool = static_cast<const _Float16*>(a.vpool);
     const size_t slice = static_cast<size_t>(C) * D;          // halves per (chunk, head)
 
-    // Q^T as the B operand: lane (grp, col) holds row col, dims 32*ks + 8*grp .. +7.
-    const bool row_ok = col < n_rows;
-    const int qrow = row_ok ? a.rows[row_lo + col] : 0;
-    h8 qb[KS];
-    {
+    h8 qb[KS];        // Q^T (B operand): row col, dims 32*ks + 8*grp .. +7
+    h8 kr[4][KS];     // K of one step: tile t = keys 16t .. 16t+15
+    h4 vr[DT][2][2];  // V of one step: [dim tile][key half][4-key piece]
+
+    auto query_row = [&](const Task& t) { return col < t.n_rows ? a.rows[t.row_lo + col] : -1; };
+    auto load_q = [&](const Task& t, int qrow) {
         const _Float16* qp = static_cast<const _Float16*>(a.q) +
-                             (static_cast<size_t>(qrow) * H + head) * D + 8 * grp;
+                             (static_cast<size_t>(qrow < 0 ? 0 : qrow) * H + t.head) * D + 8 * grp;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            qb[ks] = row_ok ? *reinterpret_cast<const h8*>(qp + 32 * ks) : h8{};
-    }
-
-    // K fragments of one step: tile t holds keys 16t .. 16t+15 of the step.
-    h8 kr[4][KS];
-    // V fragments: [dim tile][key half-step][4-key piece]
-    h4 vr[DT][2][2];
-
-    auto load_k = [&](int step) {
+            qb[ks] = qrow >= 0 ? *reinterpret_cast<const h8*>(qp + 32 * ks) : h8{};
+    };
+    // Byte offsets: a uniform part (chunk slice, key tile, k-step / dim tile)
+    // plus one per-lane constant, so every load is SGPR base + VGPR offset.
+    const uint32_t k_lane = static_cast<uint32_t>(col + grp * C) * 16u;   // key col, dims 8*grp..
+    const uint32_t v_lane = static_cast<uint32_t>(grp * D + col) * 8u;    // keys 4*grp.., dim col
+    auto slice_of = [&](const _Float16* pool, int chunk, int head) {
+        return reinterpret_cast<const char*>(pool + (static_cast<size_t>(chunk) * H + head) * slice);
+    };
+    auto load_k = [&](const Task& t, int step) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int key = step * kStep + 16 * t;
-            if (key < n_valid) {
-                const int chunk = chunks[key / C];
-                const _Float16* base = kpool + (static_cast<size_t>(chunk) * H + head) * slice +
-                                       static_cast<size_t>(key % C + col) * 8;
+        for (int tt = 0; tt < 4; ++tt) {
+            const int key = step * kStep + 16 * tt;
+            if (key < t.n_valid) {
+                const char* base = slice_of(kpool, t.chunks[key / C], t.head) + (key % C) * 16;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    kr[t][ks] = *reinterpret_cast<const h8*>(
-                        base + static_cast<size_t>(4 * ks + grp) * C * 8);
+                    kr[tt][ks] = __builtin_nontemporal_load(
+                        reinterpret_cast<const h8*>(base + ks * (C * 64) + k_lane));
             } else {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kr[t][ks] = h8{};
+                for (int ks = 0; ks < KS; ++ks) kr[tt][ks] = h8{};
             }
         }
     };
-    auto load_v = [&](int step) {
+    auto load_v = [&](const Task& t, int step) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int key = step * kStep + 16 * t;
-            if (key < n_valid) {
-                const int chunk = chunks[key / C];
-                const _Float16* base = vpool + (static_cast<size_t>(chunk) * H + head) * slice +
-                                       static_cast<size_t>(((key % C) / 4 + grp) * D + col) * 4;
+        for (int tt = 0; tt < 4; ++tt) {
+            const int key = step * kStep + 16 * tt;
+            if (key < t.n_valid) {
+                const char* base = slice_of(vpool, t.chunks[key / C], t.head) +
+                                   ((key % C) / 4) * (D * 8);
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
-                    vr[dt][t >> 1][t & 1] = *reinterpret_cast<const h4*>(base + 64 * dt);
+                    vr[dt][tt >> 1][tt & 1] = __builtin_nontemporal_load(
+                        reinterpret_cast<const h4*>(base + dt * 128 + v_lane));
             } else {
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) vr[dt][t >> 1][t & 1] = h4{};
+                for (int dt = 0; dt < DT; ++dt) vr[dt][tt >> 1][tt & 1] = h4{};
             }
         }
     };
 
-    f4 o[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    Task cur = fetch_task<C>(a, first);
+    int cur_qrow = query_row(cur);
+    load_q(cur, cur_qrow);
+    load_k(cur, 0);
+    load_v(cur, 0);
+    int ti = 0;
+    bool has_next = count > 1;
+    Task nxt = cur;
+    int nxt_qrow = -1;
+    if (has_next) {
+        nxt = fetch_task<C>(a, first + 1);
+        nxt_qrow = query_row(nxt);
+    }
 
-    load_k(0);
-    load_v(0);
-    for (int step = 0; step < n_steps; ++step) {
-        // ---- S^T = K Q^T for the 64 keys of this step --------------------------
-        f4 s[4];
+    f4 o[DT];
+    float m_run, l_run;
+    f4 s[4];
+
+    // S^T = K Q^T for the 64 keys of a step
+    auto qk = [&]() {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            s[t] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < 4; ++tt) {
+            s[tt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                s[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[t][ks], qb[ks], s[t], 0, 0, 0);
+                s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[tt][ks], qb[ks], s[tt], 0, 0, 0);
         }
-        if (step + 1 < n_steps) load_k(step + 1);
-
-        // ---- online softmax (partial_attn per step, attn_reduce into the run) ----
+    };
+    // online softmax of the step (partial_attn) folded into the run
+    // (attn_reduce), then O^T += V^T P^T
+    auto softmax_pv = [&](int step, int n_valid) {
         const int key0 = step * kStep;
         const bool tail = key0 + kStep > n_valid;
         float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float x = s[t][i] * a.scale_log2e;
-                if (tail && key0 + 16 * t + 4 * grp + i >= n_valid) x = -INFINITY;
-                s[t][i] = x;
+                float x = s[tt][i] * a.scale_log2e;
+                if (tail && key0 + 16 * tt + 4 * grp + i >= n_valid) x = -INFINITY;
+                s[tt][i] = x;
                 mx = fmaxf(mx, x);
             }
         }
@@ -187,20 +224,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         l_run = l_run * alpha + lsum;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-
         if (tail) {
             // keys past the end hold stale pool contents: zero them so that
             // 0 * garbage cannot produce a NaN inside the MFMA
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (key0 + 16 * t + 4 * grp + i >= n_valid)
+                    if (key0 + 16 * tt + 4 * grp + i >= n_valid)
 #pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) vr[dt][t >> 1][t & 1][i] = 0;
+                        for (int dt = 0; dt < DT; ++dt) vr[dt][tt >> 1][tt & 1][i] = 0;
         }
-
-        // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -210,38 +244,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                 o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[hs], o[dt], 0, 0, 0);
             }
         }
-        if (step + 1 < n_steps) load_v(step + 1);
-    }
+    };
 
-    // n of row col = sum over the four lane groups
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    if (!row_ok) return;
-    if (out_slot < 0) {
-        const float inv = 1.0f / l_tot;
-        _Float16* op = static_cast<_Float16*>(a.out) +
-                       (static_cast<size_t>(qrow) * H + head) * D + 4 * grp;
+    for (;;) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            h4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = static_cast<_Float16>(o[dt][i] * inv);
-            *reinterpret_cast<h4*>(op + 16 * dt) = v;
+        for (int dt = 0; dt < DT; ++dt) o[dt] = f4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        // all steps but the last: the next step's K and V follow right behind
+        const int n_steps = cur.n_steps;
+        for (int step = 0; step + 1 < n_steps; ++step) {
+            qk();
+            load_k(cur, step + 1);
+            softmax_pv(step, cur.n_valid);
+            load_v(cur, step + 1);
         }
-    } else {
-        const size_t slot = static_cast<size_t>(out_slot + col);
-        float* po = a.part_o + (slot * H + head) * D + 4 * grp;
+        // last step: the next task's queries and K/V follow instead
+        qk();
+        if (has_next) {
+            load_q(nxt, nxt_qrow);
+            load_k(nxt, 0);
+        }
+        softmax_pv(n_steps - 1, cur.n_valid);
+
+        // ---- task epilogue: n of row col = sum over the four lane groups --------
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (cur_qrow >= 0) {
+            if (cur.out < 0) {
+                const float inv = 1.0f / l_tot;
+                _Float16* op = static_cast<_Float16*>(a.out) +
+                               (static_cast<size_t>(cur_qrow) * H + cur.head) * D + 4 * grp;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f4*>(po + 16 * dt) = o[dt];
-        if (grp == 0) {
-            float* pm = a.part_ml + (slot * H + head) * 2;
-            pm[0] = m_run;
-            pm[1] = l_tot;
+                for (int dt = 0; dt < DT; ++dt) {
+                    h4 v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = static_cast<_Float16>(o[dt][i] * inv);
+                    *reinterpret_cast<h4*>(op + 16 * dt) = v;
+                }
+            } else {
+                const size_t slot = static_cast<size_t>(cur.out + col);
+                float* po = a.part_o + (slot * H + cur.head) * D + 4 * grp;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f4*>(po + 16 * dt) = o[dt];
+                if (grp == 0) {
+                    float* pm = a.part_ml + (slot * H + cur.head) * 2;
+                    pm[0] = m_run;
+                    pm[1] = l_tot;
+                }
+            }
+        }
+        if (!has_next) break;
+        load_v(nxt, 0);
+        cur = nxt;
+        cur_qrow = nxt_qrow;
+        ++ti;
+        has_next = ti + 1 < count;
+        if (has_next) {
+            nxt = fetch_task<C>(a, first + ti + 1);
+            nxt_qrow = query_row(nxt);
         }
     }
 }
 
 // Fold every partial of one (sequence, head) with attn_reduce and divide.
+// One wave per (sequence, head): the lanes first read the partials' (m, n)
+// in parallel and agree on the common max M; then every partial's o row is
+// read with independent loads (each lane owns D/64 dims) and accumulated
+// with weight exp2(m - M); finally o / n.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     constexpr int J = D / 64;
@@ -252,26 +322,64 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int mr = idx / a.H;
     const int head = idx - mr * a.H;
     const int p = a.merge_rows[mr];
-    const int s0 = a.mptr[p], s1 = a.mptr[p + 1];
+    const int s0 = a.mptr[p];
+    const int n = a.mptr[p + 1] - s0;
     float M = -INFINITY;
-    for (int s = s0; s < s1; ++s)
-        M = fmaxf(M, a.part_ml[(static_cast<size_t>(a.mslots[s]) * a.H + head) * 2]);
+    for (int base = 0; base < n; base += 64) {
+        const int s = base + lane;
+        if (s < n) {
+            const size_t slot = static_cast<size_t>(a.mslots[s0 + s]);
+            M = fmaxf(M, a.part_ml[(slot * a.H + head) * 2]);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float acc[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) acc[j] = 0.f;
     float L = 0.f;
-    for (int s = s0; s < s1; ++s) {
-        const size_t base = static_cast<size_t>(a.mslots[s]) * a.H + head;
-        const float w = fast_exp2(a.part_ml[base * 2] - M);
-        L += w * a.part_ml[base * 2 + 1];
+    for (int base = 0; base < n; base += 64) {
+        const int s = base + lane;
+        int my_slot = 0;
+        float my_w = 0.f;
+        if (s < n) {
+            my_slot = a.mslots[s0 + s];
+            const float* ml = a.part_ml + (static_cast<size_t>(my_slot) * a.H + head) * 2;
+            my_w = fast_exp2(ml[0] - M);
+            L += my_w * ml[1];
+        }
+        const int cnt = min(64, n - base);
+        int k = 0;
+        for (; k + 4 <= cnt; k += 4) {       // four independent row loads in flight
+            float v[4][J], w[4];
 #pragma unroll
-        for (int j = 0; j < J; ++j) acc[j] += w * a.part_o[base * D + lane + 64 * j];
+            for (int u = 0; u < 4; ++u) {
+                const size_t slot = static_cast<size_t>(__shfl(my_slot, k + u));
+                w[u] = __shfl(my_w, k + u);
+                const float* po = a.part_o + (slot * a.H + head) * D + J * lane;
+#pragma unroll
+                for (int j = 0; j < J; ++j) v[u][j] = po[j];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < J; ++j) acc[j] += w[u] * v[u][j];
+        }
+        for (; k < cnt; ++k) {
+            const size_t slot = static_cast<size_t>(__shfl(my_slot, k));
+            const float w = __shfl(my_w, k);
+            const float* po = a.part_o + (slot * a.H + head) * D + J * lane;
+#pragma unroll
+            for (int j = 0; j < J; ++j) acc[j] += w * po[j];
+        }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     const float inv = 1.0f / L;
     _Float16* op = static_cast<_Float16*>(a.out) +
-                   (static_cast<size_t>(a.rows[p]) * a.H + head) * D;
+                   (static_cast<size_t>(a.rows[p]) * a.H + head) * D + J * lane;
 #pragma unroll
-    for (int j = 0; j < J; ++j) op[lane + 64 * j] = static_cast<_Float16>(acc[j] * inv);
+    for (int j = 0; j < J; ++j) op[j] = static_cast<_Float16>(acc[j] * inv);
 }
 
 // Write tokens' K/V (natural [token][head][dim]) into their pool slots.
@@ -302,7 +410,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
 
 template <int D, int C>
 hipError_t attn_dc(const AttnArgs& a, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(a.n_wg) * static_cast<unsigned>(a.H);
+    const unsigned grid = static_cast<unsigned>(a.n_wg);
     if (grid == 0) return hipSuccess;
     attn_kernel<D, C><<<dim3(grid), dim3(256), 0, s>>>(a);
     return hipGetLastError();

@@ -52,6 +52,24 @@ bool shape_ok(int32_t d, int32_t c) {
     return (d == 64 || d == 128) && (c == 16 || c == 32 || c == 64 || c == 128);
 }
 
+// Two resident workgroups of 4 waves per compute unit: the attention kernel
+// is built for 2 waves per SIMD.  Falls back to a 256-CU device when no GPU
+// is visible (host-only use of the planner).
+int32_t default_workgroups() {
+    static int32_t cached = -1;
+    if (cached > 0) return cached;
+    int n = 0, dev = 0, cus = 0;
+    if (hipGetDeviceCount(&n) == hipSuccess && n > 0 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0) {
+        cached = 2 * cus;
+    } else {
+        (void)hipGetLastError();
+        cached = pkvt::kDefaultWorkgroups;
+    }
+    return cached;
+}
+
 bool plan_current(const pkvt_tree* t) {
     return t->plan.valid && t->plan.struct_version == t->tree.structure_version() &&
            t->plan.len_version == t->tree.length_version();
@@ -173,7 +191,10 @@ pkvt_status pkvt_plan(pkvt_tree* t, int32_t b, const int32_t* q_order, const pkv
         o.phase1_chunks = opts->phase1_chunks;
         o.phase2_chunks = opts->phase2_chunks;
         o.min_share = opts->min_share;
+        o.workgroups = opts->workgroups;
     }
+    if (o.workgroups < 0) return fail(PKVT_ERR_INVALID_ARG, "plan: workgroups must be >= 0");
+    if (o.workgroups == 0) o.workgroups = default_workgroups();
     std::string err;
     int rc = 0;
     PKVT_GUARD(rc = pkvt::make_plan(t->tree, b, q_order, o, t->plan, err));
@@ -201,6 +222,9 @@ pkvt_status pkvt_plan_info_get(const pkvt_tree* t, pkvt_plan_info* out) {
     out->unique_tokens = p.unique_tokens;
     out->logical_tokens = p.logical_tokens;
     out->structure_version = static_cast<int32_t>(p.serial & 0x7fffffff);
+    out->tasks = p.n_tasks;
+    out->phase1_split = p.split1_chunks;
+    out->phase2_split = p.split2_chunks;
     return PKVT_OK;
 }
 
@@ -261,6 +285,14 @@ pkvt_status pkvt_plan_upload(pkvt_tree* t, void* d_meta, size_t meta_bytes, void
 pkvt_status pkvt_attn_decode(const pkvt_tree* t, const void* d_meta, const void* q,
                              const void* k_pool, const void* v_pool, void* out, void* workspace,
                              size_t workspace_bytes, float scale, void* stream) {
+    return pkvt_attn_decode_ex(t, d_meta, q, k_pool, v_pool, out, workspace, workspace_bytes,
+                               scale, stream, nullptr);
+}
+
+pkvt_status pkvt_attn_decode_ex(const pkvt_tree* t, const void* d_meta, const void* q,
+                                const void* k_pool, const void* v_pool, void* out,
+                                void* workspace, size_t workspace_bytes, float scale,
+                                void* stream, void* attn_event) {
     if (!t || !d_meta || !q || !k_pool || !v_pool || !out)
         return fail(PKVT_ERR_INVALID_ARG, "attn_decode: NULL argument");
     if (!std::isfinite(scale)) return fail(PKVT_ERR_INVALID_ARG, "attn_decode: scale is not finite");
@@ -281,7 +313,8 @@ pkvt_status pkvt_attn_decode(const pkvt_tree* t, const void* d_meta, const void*
     auto s = static_cast<hipStream_t>(stream);
 
     pkvt::AttnArgs a{};
-    a.wg = m + p.blob[pkvt::kOffWg];
+    a.lists = m + p.blob[pkvt::kOffLists];
+    a.tasks = m + p.blob[pkvt::kOffTasks];
     a.waves = m + p.blob[pkvt::kOffWaves];
     a.chunks = m + p.blob[pkvt::kOffChunks];
     a.rows = m + p.blob[pkvt::kOffRows];
@@ -293,10 +326,12 @@ pkvt_status pkvt_attn_decode(const pkvt_tree* t, const void* d_meta, const void*
     a.part_o = part_o;
     a.part_ml = part_ml;
     a.H = H;
-    a.n_wg = p.n_wg;
+    a.n_wg = p.n_tasks > 0 ? p.n_wg : 0;
     a.scale_log2e = scale * 1.4426950408889634f;
     hipError_t e = pkvt::launch_attn(a, D, C, s);
     if (e != hipSuccess) return hip_fail(e, "attn_decode: attention kernel");
+    if (attn_event && (e = hipEventRecord(static_cast<hipEvent_t>(attn_event), s)) != hipSuccess)
+        return hip_fail(e, "attn_decode: event record");
     if (p.n_merge > 0) {
         pkvt::MergeArgs mg{};
         mg.merge_rows = m + p.blob[pkvt::kOffMerge];

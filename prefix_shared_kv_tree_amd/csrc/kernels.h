@@ -9,7 +9,8 @@
 namespace pkvt {
 
 struct AttnArgs {
-    const int32_t* wg;        // [n_wg][4] wave task per wave slot (-1 idle)
+    const int32_t* lists;     // [4*n_wg][2] per wave lane: first task, task count
+    const int32_t* tasks;     // [n_tasks][2] (wave descriptor, head)
     const int32_t* waves;     // [n_waves][8] WaveDesc
     const int32_t* chunks;    // chunk ids
     const int32_t* rows;      // [b] depth-first position -> query row
@@ -21,7 +22,7 @@ struct AttnArgs {
     float* part_o;            // [n_slots][H][D]
     float* part_ml;           // [n_slots][H][2]  (m in log2 units, n)
     int32_t H;
-    int32_t n_wg;
+    int32_t n_wg;             // persistent workgroups (grid size)
     float scale_log2e;        // score scale * log2(e)
 };
 

@@ -12,9 +12,16 @@
 //    items of at most phase2_chunks chunks.
 // 4. A sequence with exactly one item, a phase-2 one, is finalised by that
 //    item; every other sequence's partials are merged afterwards.
+// 5. Every (item, row group of 16, head) is a wave task.  The attention
+//    kernel runs G persistent workgroups of 4 waves; each wave walks a task
+//    list.  Lists are filled longest-task-first: the row groups of one
+//    phase-1 item go to the 4 waves of one workgroup, so they stream the
+//    same chunks together, and phase-2 tasks go to the least loaded wave.
+//    Items are cut so that no task is longer than the mean per-wave load.
 #include "plan.h"
 
 #include <algorithm>
+#include <queue>
 #include <unordered_map>
 
 #include "pkvt.h"
@@ -23,8 +30,13 @@ namespace pkvt {
 
 namespace {
 
-constexpr int32_t kDefaultPhase1Steps = 8;   // 64-key steps per phase-1 item
-constexpr int32_t kDefaultPhase2Steps = 4;   // 64-key steps per phase-2 item
+// task cost in quarter steps: 4 per 64-key step plus a start-up share
+int64_t task_cost(int32_t keys) { return 4 * ((keys + kKeysPerStep - 1) / kKeysPerStep) + 1; }
+
+int32_t steps_to_chunks(int64_t steps, int32_t C) {
+    const int64_t ch = steps * kKeysPerStep / C;
+    return static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(ch, 1 << 30)));
+}
 
 struct Range { int32_t i = 0, j = 0; };
 
@@ -62,12 +74,8 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         err = "plan: min_share must be >= 2 (or 0 for the default); chunk limits >= 0";
         return PKVT_ERR_INVALID_ARG;
     }
-    const int32_t steps_to_chunks = std::max(1, kKeysPerStep / t.C);
-    const int32_t s1 = opts.phase1_chunks ? opts.phase1_chunks
-                                          : std::max(1, kDefaultPhase1Steps * kKeysPerStep / t.C);
-    const int32_t s2 = opts.phase2_chunks ? opts.phase2_chunks
-                                          : std::max(1, kDefaultPhase2Steps * kKeysPerStep / t.C);
-    (void)steps_to_chunks;
+    const int32_t G = opts.workgroups > 0 ? opts.workgroups : kDefaultWorkgroups;
+    const int32_t lanes = G * kWavesPerWg;
 
     // ---- validate the batch --------------------------------------------------
     std::vector<const Seq*> seqs(b);
@@ -137,17 +145,12 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         err = "plan: internal error, depth-first order lost rows";
         return PKVT_ERR_INVALID_ARG;
     }
-    std::vector<int32_t> pos_of_row(b);
-    for (int32_t p = 0; p < b; ++p) pos_of_row[dfs_row[p]] = p;
     auto cov = [&](int32_t x) { const Range& r = range[x]; return r.j - r.i; };
 
-    // ---- 2. phase-1 segments and items ------------------------------------------
-    std::vector<Item> items1;
-    std::vector<int32_t> src_count(b, 0);
-    int32_t shared_chunks = 0;
+    // ---- 2. phase-1 segments ----------------------------------------------------
+    std::vector<std::vector<int32_t>> segs;
+    std::vector<Range> seg_range;
     {
-        std::vector<std::vector<int32_t>> segs;
-        std::vector<Range> seg_range;
         std::unordered_map<int32_t, int32_t> seg_of;
         for (int32_t x : preorder) {
             if (cov(x) < opts.min_share) continue;
@@ -163,32 +166,76 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
                 seg_range.push_back(range[x]);
             }
         }
+    }
+    // private suffix of every sequence: path[k0[p] ..)
+    std::vector<int32_t> k0(b);
+    for (int32_t p = 0; p < b; ++p) {
+        const std::vector<int32_t>& path = seqs[dfs_row[p]]->path;
+        int32_t k = static_cast<int32_t>(path.size());
+        while (k > 0 && cov(path[k - 1]) < opts.min_share) --k;
+        k0[p] = k;
+    }
+
+    // ---- item size ----------------------------------------------------------------
+    // T = the mean per-wave load in 64-key steps with nothing cut.  Phase-1
+    // items are cut at T.  Phase-2 items are cut at T when nothing is shared
+    // (all tasks then tend to be alike and need no merge); with a shared
+    // prefix the phase-1 units make the per-wave loads uneven and finer
+    // phase-2 pieces (4 steps, or T/4 if larger) fill the gaps better.
+    int32_t s1 = opts.phase1_chunks, s2 = opts.phase2_chunks;
+    if (s1 == 0 || s2 == 0) {
+        auto steps_of = [](int64_t keys) { return (keys + kKeysPerStep - 1) / kKeysPerStep; };
+        int64_t steps = 0;
         for (size_t s = 0; s < segs.size(); ++s) {
-            shared_chunks += static_cast<int32_t>(segs[s].size());
-            for (size_t a = 0; a < segs[s].size(); a += s1) {
-                Item it;
-                it.chunks.assign(segs[s].begin() + a,
-                                 segs[s].begin() + std::min(segs[s].size(), a + s1));
-                it.row_lo = seg_range[s].i;
-                it.n_rows = seg_range[s].j - seg_range[s].i;
-                for (int32_t p = seg_range[s].i; p < seg_range[s].j; ++p) src_count[p]++;
-                items1.push_back(std::move(it));
-            }
+            const int64_t waves = (seg_range[s].j - seg_range[s].i + kRowsPerWave - 1) / kRowsPerWave;
+            steps += waves * steps_of(static_cast<int64_t>(segs[s].size()) * t.C);
+        }
+        for (int32_t p = 0; p < b; ++p)
+            steps += steps_of(seqs[dfs_row[p]]->len - static_cast<int64_t>(k0[p]) * t.C);
+        const int64_t mean = std::max<int64_t>(1, (steps * t.H + lanes - 1) / lanes);
+        if (s1 == 0) s1 = steps_to_chunks(mean, t.C);
+        if (s2 == 0) {
+            const int64_t fine = std::min<int64_t>(mean, std::max<int64_t>(4, (mean + 3) / 4));
+            s2 = steps_to_chunks(segs.empty() ? mean : fine, t.C);
         }
     }
 
-    // ---- 3. phase-2 items --------------------------------------------------------
+    // ---- 3. items ------------------------------------------------------------------
+    std::vector<Item> items1;
+    std::vector<int32_t> src_count(b, 0);
+    int32_t shared_chunks = 0;
+    // a run of n chunks is cut into ceil(n / limit) items of near-equal size
+    auto cuts = [](int32_t n, int32_t limit) {
+        std::vector<int32_t> at{0};
+        const int32_t k = (n + limit - 1) / limit;
+        for (int32_t i = 0; i < k; ++i) at.push_back(at.back() + n / k + (i < n % k ? 1 : 0));
+        return at;
+    };
+    for (size_t s = 0; s < segs.size(); ++s) {
+        shared_chunks += static_cast<int32_t>(segs[s].size());
+        const std::vector<int32_t> at = cuts(static_cast<int32_t>(segs[s].size()), s1);
+        for (size_t q = 0; q + 1 < at.size(); ++q) {
+            Item it;
+            it.chunks.assign(segs[s].begin() + at[q], segs[s].begin() + at[q + 1]);
+            it.row_lo = seg_range[s].i;
+            it.n_rows = seg_range[s].j - seg_range[s].i;
+            for (int32_t p = seg_range[s].i; p < seg_range[s].j; ++p) src_count[p]++;
+            items1.push_back(std::move(it));
+        }
+    }
     std::vector<Item> items2;
     for (int32_t p = 0; p < b; ++p) {
         const std::vector<int32_t>& path = seqs[dfs_row[p]]->path;
-        int32_t k0 = static_cast<int32_t>(path.size());
-        while (k0 > 0 && cov(path[k0 - 1]) < opts.min_share) --k0;
-        for (int32_t a = k0; a < static_cast<int32_t>(path.size()); a += s2) {
+        const int32_t n = static_cast<int32_t>(path.size());
+        if (k0[p] == n) continue;
+        const std::vector<int32_t> at = cuts(n - k0[p], s2);
+        for (size_t q = 0; q + 1 < at.size(); ++q) {
             Item it;
-            const int32_t e = std::min<int32_t>(static_cast<int32_t>(path.size()), a + s2);
+            const int32_t a = k0[p] + at[q];
+            const int32_t e = k0[p] + at[q + 1];
             it.chunks.assign(path.begin() + a, path.begin() + e);
             it.key_base = a * t.C;
-            it.len_row = (e == static_cast<int32_t>(path.size())) ? p : -1;
+            it.len_row = (e == n) ? p : -1;
             it.row_lo = p;
             it.n_rows = 1;
             src_count[p]++;
@@ -214,67 +261,94 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         }
     }
 
-    // ---- 5. waves and workgroups (longest first) -------------------------------------
+    // ---- 5. wave descriptors and per-lane task lists ---------------------------------
     std::vector<WaveDesc> waves;
-    std::vector<std::vector<int32_t>> chunk_lists;
-    struct Unit { std::vector<int32_t> waves; int32_t cost; };
-    std::vector<Unit> units1;
-    std::vector<int32_t> waves2;
+    std::vector<const std::vector<int32_t>*> wave_chunks;
+    std::vector<int64_t> wave_cost;
     auto add_wave = [&](const Item& it, int32_t row_off) {
         WaveDesc w{};
-        w.chunk_off = 0;                                   // filled at emission
         w.n_chunks = static_cast<int32_t>(it.chunks.size());
         w.key_base = it.key_base;
         w.len_row = it.len_row;
         w.row_lo = it.row_lo + row_off;
         w.n_rows = std::min(kRowsPerWave, it.n_rows - row_off);
         w.out = it.out < 0 ? -1 : it.out + row_off;
+        int64_t keys = static_cast<int64_t>(w.n_chunks) * t.C;
+        if (it.len_row >= 0)
+            keys = std::min<int64_t>(keys, seqs[dfs_row[it.len_row]]->len - it.key_base);
         waves.push_back(w);
-        chunk_lists.push_back(it.chunks);
+        wave_chunks.push_back(&it.chunks);
+        wave_cost.push_back(task_cost(static_cast<int32_t>(keys)));
         return static_cast<int32_t>(waves.size()) - 1;
     };
+    struct Unit { std::vector<int32_t> waves; int64_t cost; };
+    std::vector<Unit> units;                 // phase-1: row groups of one item, <= 4 waves
     for (const Item& it : items1) {
         for (int32_t r0 = 0; r0 < it.n_rows; r0 += kRowsPerWave * kWavesPerWg) {
             Unit u;
-            u.cost = static_cast<int32_t>(it.chunks.size());
             for (int32_t r = r0; r < std::min(it.n_rows, r0 + kRowsPerWave * kWavesPerWg);
                  r += kRowsPerWave)
                 u.waves.push_back(add_wave(it, r));
-            units1.push_back(std::move(u));
+            u.cost = wave_cost[u.waves[0]];
+            units.push_back(std::move(u));
         }
     }
-    for (const Item& it : items2) waves2.push_back(add_wave(it, 0));
-    std::stable_sort(units1.begin(), units1.end(),
-                     [](const Unit& a, const Unit& c) { return a.cost > c.cost; });
-    std::stable_sort(waves2.begin(), waves2.end(), [&](int32_t a, int32_t c) {
-        return waves[a].n_chunks > waves[c].n_chunks;
-    });
-    std::vector<Unit> wgs;
-    size_t next2 = 0;
-    for (Unit& u : units1) {
-        while (u.waves.size() < static_cast<size_t>(kWavesPerWg) && next2 < waves2.size()) {
-            u.cost = std::max(u.cost, waves[waves2[next2]].n_chunks);
-            u.waves.push_back(waves2[next2++]);
+    std::vector<int32_t> singles;            // phase-2 waves
+    for (const Item& it : items2) singles.push_back(add_wave(it, 0));
+
+    std::vector<std::vector<std::pair<int32_t, int32_t>>> lists(lanes);   // (wave, head)
+    std::vector<int64_t> load(lanes, 0);
+    {
+        // phase-1 units x heads -> the workgroup whose busiest wave is least loaded
+        std::vector<std::pair<int64_t, int32_t>> ut;         // (cost, unit*H + head)
+        for (size_t u = 0; u < units.size(); ++u)
+            for (int32_t h = 0; h < t.H; ++h)
+                ut.push_back({units[u].cost, static_cast<int32_t>(u) * t.H + h});
+        std::stable_sort(ut.begin(), ut.end(),
+                         [](const auto& a, const auto& c) { return a.first > c.first; });
+        using QE = std::pair<int64_t, int32_t>;
+        std::priority_queue<QE, std::vector<QE>, std::greater<QE>> wgq;
+        for (int32_t g = 0; g < G; ++g) wgq.push({0, g});
+        for (const auto& e : ut) {
+            const auto top = wgq.top();
+            wgq.pop();
+            const int32_t g = top.second;
+            const Unit& u = units[e.second / t.H];
+            const int32_t h = e.second % t.H;
+            int64_t start = 0;
+            for (int32_t k = 0; k < kWavesPerWg; ++k) start = std::max(start, load[g * kWavesPerWg + k]);
+            for (size_t k = 0; k < u.waves.size(); ++k) {
+                lists[g * kWavesPerWg + k].push_back({u.waves[k], h});
+                load[g * kWavesPerWg + k] = start + e.first;
+            }
+            int64_t mx = 0;
+            for (int32_t k = 0; k < kWavesPerWg; ++k) mx = std::max(mx, load[g * kWavesPerWg + k]);
+            wgq.push({mx, g});
         }
-        wgs.push_back(std::move(u));
-    }
-    while (next2 < waves2.size()) {
-        Unit u;
-        u.cost = 0;
-        while (u.waves.size() < static_cast<size_t>(kWavesPerWg) && next2 < waves2.size()) {
-            u.cost = std::max(u.cost, waves[waves2[next2]].n_chunks);
-            u.waves.push_back(waves2[next2++]);
+        // phase-2 waves x heads -> the least loaded wave
+        std::vector<std::pair<int64_t, int32_t>> st;         // (cost, single*H + head)
+        for (size_t i = 0; i < singles.size(); ++i)
+            for (int32_t h = 0; h < t.H; ++h)
+                st.push_back({wave_cost[singles[i]], static_cast<int32_t>(i) * t.H + h});
+        std::stable_sort(st.begin(), st.end(),
+                         [](const auto& a, const auto& c) { return a.first > c.first; });
+        std::priority_queue<QE, std::vector<QE>, std::greater<QE>> lq;
+        for (int32_t l = 0; l < lanes; ++l) lq.push({load[l], l});
+        for (const auto& e : st) {
+            const auto top = lq.top();
+            lq.pop();
+            lists[top.second].push_back({singles[e.second / t.H], e.second % t.H});
+            load[top.second] = top.first + e.first;
+            lq.push({load[top.second], top.second});
         }
-        wgs.push_back(std::move(u));
     }
-    std::stable_sort(wgs.begin(), wgs.end(),
-                     [](const Unit& a, const Unit& c) { return a.cost > c.cost; });
 
     // ---- 6. emit the blob -------------------------------------------------------------
-    const int32_t n_wg = static_cast<int32_t>(wgs.size());
     const int32_t n_waves = static_cast<int32_t>(waves.size());
+    int32_t n_tasks = 0;
+    for (auto& l : lists) n_tasks += static_cast<int32_t>(l.size());
     int32_t total_chunks = 0;
-    for (auto& l : chunk_lists) total_chunks += static_cast<int32_t>(l.size());
+    for (auto* l : wave_chunks) total_chunks += static_cast<int32_t>(l->size());
     std::vector<int32_t> merge_rows;
     for (int32_t p = 0; p < b; ++p)
         if (!mslots[p].empty()) merge_rows.push_back(p);
@@ -283,12 +357,12 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
 
     std::vector<int32_t> blob(kHeaderWords, 0);
     auto section = [&](HeaderField f, size_t words) {
-        // keep every section 16-byte aligned
-        while (blob.size() % 4) blob.push_back(0);
+        while (blob.size() % 4) blob.push_back(0);             // 16-byte aligned sections
         blob[f] = static_cast<int32_t>(blob.size());
         blob.resize(blob.size() + words, 0);
     };
-    section(kOffWg, static_cast<size_t>(n_wg) * kWavesPerWg);
+    section(kOffLists, static_cast<size_t>(lanes) * 2);
+    section(kOffTasks, static_cast<size_t>(n_tasks) * 2);
     section(kOffWaves, static_cast<size_t>(n_waves) * 8);
     section(kOffChunks, total_chunks);
     section(kOffRows, b);
@@ -298,23 +372,24 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     section(kOffSeqlen, b);
     while (blob.size() % 4) blob.push_back(0);
 
-    // waves are renumbered in workgroup order so neighbours read neighbours
-    int32_t wslot = 0, coff = 0;
-    for (int32_t g = 0; g < n_wg; ++g) {
-        for (int32_t k = 0; k < kWavesPerWg; ++k) {
-            int32_t* wg = &blob[blob[kOffWg] + g * kWavesPerWg + k];
-            if (k >= static_cast<int32_t>(wgs[g].waves.size())) {
-                *wg = -1;
-                continue;
+    {
+        int32_t at = 0;
+        for (int32_t l = 0; l < lanes; ++l) {
+            blob[blob[kOffLists] + 2 * l] = at;
+            blob[blob[kOffLists] + 2 * l + 1] = static_cast<int32_t>(lists[l].size());
+            for (const auto& e : lists[l]) {
+                blob[blob[kOffTasks] + 2 * at] = e.first;
+                blob[blob[kOffTasks] + 2 * at + 1] = e.second;
+                ++at;
             }
-            const int32_t src = wgs[g].waves[k];
-            WaveDesc w = waves[src];
-            w.chunk_off = coff;
-            for (int32_t id : chunk_lists[src]) blob[blob[kOffChunks] + coff++] = id;
-            std::copy(reinterpret_cast<const int32_t*>(&w),
-                      reinterpret_cast<const int32_t*>(&w) + 8,
-                      &blob[blob[kOffWaves] + wslot * 8]);
-            *wg = wslot++;
+        }
+        int32_t coff = 0;
+        for (int32_t w = 0; w < n_waves; ++w) {
+            WaveDesc d = waves[w];
+            d.chunk_off = coff;
+            for (int32_t id : *wave_chunks[w]) blob[blob[kOffChunks] + coff++] = id;
+            std::copy(reinterpret_cast<const int32_t*>(&d),
+                      reinterpret_cast<const int32_t*>(&d) + 8, &blob[blob[kOffWaves] + w * 8]);
         }
     }
     for (int32_t p = 0; p < b; ++p) blob[blob[kOffRows] + p] = dfs_row[p];
@@ -323,14 +398,15 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         int32_t at = 0;
         for (int32_t p = 0; p < b; ++p) {
             blob[blob[kOffMptr] + p] = at;
-            for (int32_t s : mslots[p]) blob[blob[kOffMslots] + at++] = s;
+            for (int32_t sl : mslots[p]) blob[blob[kOffMslots] + at++] = sl;
         }
         blob[blob[kOffMptr] + b] = at;
     }
     blob[kMagic] = kPlanMagic;
     blob[kB] = b;
     blob[kNWaves] = n_waves;
-    blob[kNWg] = n_wg;
+    blob[kNWg] = G;
+    blob[kNTasks] = n_tasks;
     blob[kNSlots] = n_slots;
     blob[kNMerge] = static_cast<int32_t>(merge_rows.size());
     blob[kTotalWords] = static_cast<int32_t>(blob.size());
@@ -352,9 +428,12 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     plan.phase1_items = static_cast<int32_t>(items1.size());
     plan.phase2_items = static_cast<int32_t>(items2.size());
     plan.n_waves = n_waves;
-    plan.n_wg = n_wg;
+    plan.n_wg = G;
+    plan.n_tasks = n_tasks;
     plan.n_slots = n_slots;
     plan.n_merge = static_cast<int32_t>(merge_rows.size());
+    plan.split1_chunks = s1;
+    plan.split2_chunks = s2;
     plan.shared_chunks = shared_chunks;
     plan.unique_tokens = unique;
     plan.dfs_seq.resize(b);

@@ -6,8 +6,10 @@
 // changes (lazy context copy, Knowl 5).  Layout (word offsets in the header):
 //
 //   header   [kHeaderWords]
-//   wg       [n_wg][4]         wave task index per wave slot, -1 = idle
-//   waves    [n_waves][8]      WaveDesc
+//   lists    [4*G][2]          per wave lane of the G persistent workgroups:
+//                              (first entry in tasks, number of tasks)
+//   tasks    [n_tasks][2]      (wave descriptor index, head), in lane order
+//   waves    [n_waves][8]      WaveDesc (head-independent)
 //   chunks   [...]             chunk ids referenced by the waves
 //   rows     [b]               depth-first position -> query row of Q / O
 //   merge    [n_merge]         depth-first positions whose partials are merged
@@ -40,22 +42,24 @@ struct WaveDesc {
 static_assert(sizeof(WaveDesc) == 32, "WaveDesc is 8 int32");
 
 enum HeaderField {
-    kMagic = 0, kSerial, kB, kNWaves, kNWg, kNSlots, kNMerge,
-    kOffWg, kOffWaves, kOffChunks, kOffRows, kOffMerge, kOffMptr, kOffMslots, kOffSeqlen,
-    kTotalWords, kHeaderWords = 16
+    kMagic = 0, kSerial, kB, kNWaves, kNWg, kNTasks, kNSlots, kNMerge,
+    kOffLists, kOffTasks, kOffWaves, kOffChunks, kOffRows, kOffMerge, kOffMptr, kOffMslots,
+    kOffSeqlen, kTotalWords, kHeaderWords = 20
 };
-constexpr int32_t kPlanMagic = 0x504b5654;   // "PKVT"
+constexpr int32_t kPlanMagic = 0x504b5655;   // "PKVU": lane-list layout
 constexpr int32_t kWavesPerWg = 4;
 constexpr int32_t kRowsPerWave = 16;
 constexpr int32_t kKeysPerStep = 64;
+constexpr int32_t kDefaultWorkgroups = 512;  // 256 CUs x 2 resident workgroups
 
 struct PlanOpts {
-    int32_t phase1_chunks = 0;
+    int32_t phase1_chunks = 0;   // 0 = derived from the balanced per-lane load
     int32_t phase2_chunks = 0;
     int32_t min_share = 2;
+    int32_t workgroups = 0;      // persistent workgroups; 0 = kDefaultWorkgroups
     bool operator==(const PlanOpts& o) const {
         return phase1_chunks == o.phase1_chunks && phase2_chunks == o.phase2_chunks &&
-               min_share == o.min_share;
+               min_share == o.min_share && workgroups == o.workgroups;
     }
 };
 
@@ -69,7 +73,9 @@ struct Plan {
     PlanOpts opts;
     std::vector<int32_t> blob;
     // summary
-    int32_t phase1_items = 0, phase2_items = 0, n_waves = 0, n_wg = 0, n_slots = 0, n_merge = 0;
+    int32_t phase1_items = 0, phase2_items = 0, n_waves = 0, n_wg = 0, n_tasks = 0;
+    int32_t n_slots = 0, n_merge = 0;
+    int32_t split1_chunks = 0, split2_chunks = 0;   // the item sizes actually used
     int32_t shared_chunks = 0;
     int64_t unique_tokens = 0, logical_tokens = 0;
     std::vector<int32_t> dfs_seq;     // depth-first position -> sequence id (tests)

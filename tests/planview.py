@@ -6,21 +6,22 @@ from collections import defaultdict
 
 import numpy as np
 
-H_MAGIC, H_SERIAL, H_B, H_NWAVES, H_NWG, H_NSLOTS, H_NMERGE = range(7)
-H_OFF_WG, H_OFF_WAVES, H_OFF_CHUNKS, H_OFF_ROWS, H_OFF_MERGE, H_OFF_MPTR, H_OFF_MSLOTS, \
-    H_OFF_SEQLEN, H_TOTAL = range(7, 16)
-MAGIC = 0x504B5654
+(H_MAGIC, H_SERIAL, H_B, H_NWAVES, H_NWG, H_NTASKS, H_NSLOTS, H_NMERGE, H_OFF_LISTS,
+ H_OFF_TASKS, H_OFF_WAVES, H_OFF_CHUNKS, H_OFF_ROWS, H_OFF_MERGE, H_OFF_MPTR, H_OFF_MSLOTS,
+ H_OFF_SEQLEN, H_TOTAL) = range(18)
+MAGIC = 0x504B5655
 
 
 def parse(blob: np.ndarray) -> dict:
     b = int(blob[H_B])
-    nw, ng = int(blob[H_NWAVES]), int(blob[H_NWG])
+    nw, ng, nt = int(blob[H_NWAVES]), int(blob[H_NWG]), int(blob[H_NTASKS])
     waves = blob[blob[H_OFF_WAVES]:blob[H_OFF_WAVES] + nw * 8].reshape(nw, 8)
     chunks_base = int(blob[H_OFF_CHUNKS])
     mptr = blob[blob[H_OFF_MPTR]:blob[H_OFF_MPTR] + b + 1]
     return dict(
-        magic=int(blob[H_MAGIC]), b=b, n_slots=int(blob[H_NSLOTS]),
-        wg=blob[blob[H_OFF_WG]:blob[H_OFF_WG] + ng * 4].reshape(ng, 4),
+        magic=int(blob[H_MAGIC]), b=b, n_slots=int(blob[H_NSLOTS]), n_wg=ng,
+        lists=blob[blob[H_OFF_LISTS]:blob[H_OFF_LISTS] + ng * 4 * 2].reshape(ng * 4, 2),
+        tasks=blob[blob[H_OFF_TASKS]:blob[H_OFF_TASKS] + nt * 2].reshape(nt, 2),
         waves=waves,
         wave_chunks=[blob[chunks_base + w[0]:chunks_base + w[0] + w[1]] for w in waves],
         rows=blob[blob[H_OFF_ROWS]:blob[H_OFF_ROWS] + b],
@@ -33,7 +34,7 @@ def parse(blob: np.ndarray) -> dict:
 
 
 def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: int = 2,
-               max_rows: int = 16):
+               max_rows: int = 16, heads: int = 1):
     """paths / lens: seq id -> chunk path / token count (from the tree).
     Raises AssertionError on any violation."""
     assert plan["magic"] == MAGIC
@@ -57,6 +58,7 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
     chunk_rows = defaultdict(set)
     slot_rows = {}
     direct = set()
+    phase1 = []
     for wi, (w, ch) in enumerate(zip(plan["waves"], plan["wave_chunks"])):
         chunk_off, n_chunks, key_base, len_row, row_lo, n_rows, out, _ = [int(v) for v in w]
         assert n_chunks == len(ch) >= 1 and 1 <= n_rows <= max_rows
@@ -72,6 +74,7 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
             multi = shared
         if not multi:
             assert n_rows == 1
+        phase1.append(bool(multi))
         # key bound: only the wave that ends at the leaf uses the length
         p0 = row_lo
         path = [int(y) for y in paths[seq_at[p0]]]
@@ -107,6 +110,27 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
             assert not sl and p not in merge
         else:
             assert sl and p in merge
-    # workgroup table: every wave once
-    used = [int(v) for v in plan["wg"].ravel() if v >= 0]
-    assert sorted(used) == list(range(len(plan["waves"])))
+    # task lists: every (wave, head) exactly once; lists tile the task array
+    lists = plan["lists"]
+    assert lists.shape[0] == 4 * plan["n_wg"]
+    at = 0
+    lane_of = {}
+    for lane, (first, cnt) in enumerate(lists):
+        assert first == at and cnt >= 0
+        for k in range(first, first + cnt):
+            w, h = (int(x) for x in plan["tasks"][k])
+            assert 0 <= h < heads
+            assert (w, h) not in lane_of, "task listed twice"
+            lane_of[(w, h)] = lane
+        at += cnt
+    assert at == len(plan["tasks"])
+    assert set(lane_of) == {(w, h) for w in range(len(plan["waves"])) for h in range(heads)}
+    # the row groups of one phase-1 item (same chunks, same head) share a workgroup
+    items = defaultdict(list)
+    for wi, ch in enumerate(plan["wave_chunks"]):
+        if phase1[wi]:
+            items[tuple(int(x) for x in ch)].append(wi)
+    for ch, ws in items.items():
+        for h in range(heads):
+            wgs = {lane_of[(w, h)] // 4 for w in ws}
+            assert len(wgs) <= (len(ws) + 3) // 4, "row groups of a phase-1 item split up"

@@ -301,7 +301,8 @@ def _plan_and_check(box, order, **kw):
     live = list(order)
     paths = {int(i): list(B.pkvt_tree_chunk_path(box.t, int(i))) for i in live}
     lens = {int(i): B.pkvt_tree_seq_len(box.t, int(i)) for i in live}
-    planview.check_plan(plan, order, paths, lens, box.c, min_share=kw.get("min_share") or 2)
+    planview.check_plan(plan, order, paths, lens, box.c, min_share=kw.get("min_share") or 2,
+                        heads=box.h)
     assert wb == plan["n_slots"] * box.h * (box.d + 2) * 4
     return plan
 
