@@ -133,6 +133,20 @@ def cpu_baseline(w, unique_bytes, budget_s):
     }
 
 
+def copy_probe(torch, mib):
+    """A plain copy of known size (torch's elementwise kernel: `mib` MiB read,
+    `mib` MiB written), launched three times.  Under a counter-collection run
+    its FETCH_SIZE / WRITE_SIZE give the factor that converts those counters
+    to bytes on this machine."""
+    n = mib * 2 ** 20 // 2
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +158,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the run, launch a plain elementwise copy of this many MiB "
+                         "(reads and writes that many bytes) to calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the decode attention of one "
@@ -278,6 +295,8 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, unique_bytes, args.cpu_budget)
     ds.close()
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)
     print(json.dumps(res), flush=True)
 
 

@@ -71,12 +71,21 @@ struct Task {
     int head;
 };
 
+// The plan metadata is read-only for the whole launch.  Reading it through
+// the constant address space lets the compiler use scalar loads: task fields
+// and chunk ids then live in SGPRs, and fetching the next chunk id never
+// waits on the vector loads in flight (a vector load would, since vmcnt
+// retires in order).
+typedef const __attribute__((address_space(4))) int32_t cint;
+__device__ __forceinline__ cint* meta(const int32_t* p) { return (cint*)(p); }
+
 template <int C>
 __device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
-    const int wave_id = a.tasks[2 * idx];
+    cint* tk = meta(a.tasks) + 2 * idx;
+    const int wave_id = tk[0];
     Task t;
-    t.head = a.tasks[2 * idx + 1];
-    const int32_t* wd = a.waves + 8 * wave_id;
+    t.head = tk[1];
+    cint* wd = meta(a.waves) + 8 * wave_id;
     const int n_chunks = wd[1];
     const int key_base = wd[2];
     const int len_row = wd[3];
@@ -85,7 +94,7 @@ __device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
     t.n_rows = wd[5];
     t.out = wd[6];
     int n_valid = n_chunks * C;
-    if (len_row >= 0) n_valid = min(n_valid, a.seqlen[len_row] - key_base);
+    if (len_row >= 0) n_valid = min(n_valid, meta(a.seqlen)[len_row] - key_base);
     t.n_valid = n_valid;
     t.n_steps = (n_valid + kStep - 1) / kStep;
     return t;
@@ -103,8 +112,8 @@ void attn_kernel(AttnArgs a) {
     const int col = lane & 15;     // MFMA row/column index held by this lane
     const int grp = lane >> 4;     // which 8-element k slice of the fragment
     const int lane_id = blockIdx.x * kWaves + wave;
-    const int first = a.lists[2 * lane_id];
-    const int count = a.lists[2 * lane_id + 1];
+    const int first = meta(a.lists)[2 * lane_id];
+    const int count = meta(a.lists)[2 * lane_id + 1];
     if (count == 0) return;
 
     const _Float16* __restrict__ kpool = static_cast<const _Float16*>(a.kpool);
@@ -130,37 +139,37 @@ void attn_kernel(AttnArgs a) {
     auto slice_of = [&](const _Float16* pool, int chunk, int head) {
         return reinterpret_cast<const char*>(pool + (static_cast<size_t>(chunk) * H + head) * slice);
     };
+    // Loads are unconditional so the compiler can count them exactly and wait
+    // for just the step it needs (a branch around a load makes it wait for
+    // everything).  A tile past the end of the keys re-reads the last tile
+    // that has valid keys -- same addresses, so no extra HBM traffic -- and
+    // its scores are forced to -inf and its V entries zeroed below.
+    auto tile_key = [&](const Task& t, int step, int tt) {
+        const int key = step * kStep + 16 * tt;
+        const int last = (t.n_valid - 1) & ~15;
+        return key < last ? key : last;
+    };
     auto load_k = [&](const Task& t, int step) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const int key = step * kStep + 16 * tt;
-            if (key < t.n_valid) {
-                const char* base = slice_of(kpool, t.chunks[key / C], t.head) + (key % C) * 16;
+            const int key = tile_key(t, step, tt);
+            const char* base = slice_of(kpool, meta(t.chunks)[key / C], t.head) + (key % C) * 16;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    kr[tt][ks] = __builtin_nontemporal_load(
-                        reinterpret_cast<const h8*>(base + ks * (C * 64) + k_lane));
-            } else {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) kr[tt][ks] = h8{};
-            }
+            for (int ks = 0; ks < KS; ++ks)
+                kr[tt][ks] = __builtin_nontemporal_load(
+                    reinterpret_cast<const h8*>(base + ks * (C * 64) + k_lane));
         }
     };
     auto load_v = [&](const Task& t, int step) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const int key = step * kStep + 16 * tt;
-            if (key < t.n_valid) {
-                const char* base = slice_of(vpool, t.chunks[key / C], t.head) +
-                                   ((key % C) / 4) * (D * 8);
+            const int key = tile_key(t, step, tt);
+            const char* base = slice_of(vpool, meta(t.chunks)[key / C], t.head) +
+                               ((key % C) / 4) * (D * 8);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    vr[dt][tt >> 1][tt & 1] = __builtin_nontemporal_load(
-                        reinterpret_cast<const h4*>(base + dt * 128 + v_lane));
-            } else {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) vr[dt][tt >> 1][tt & 1] = h4{};
-            }
+            for (int dt = 0; dt < DT; ++dt)
+                vr[dt][tt >> 1][tt & 1] =
+                    __builtin_nontemporal_load(reinterpret_cast<const h4*>(base + dt * 128 + v_lane));
         }
     };
 
@@ -225,15 +234,19 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
         if (tail) {
-            // keys past the end hold stale pool contents: zero them so that
-            // 0 * garbage cannot produce a NaN inside the MFMA
+            // keys past the end hold stale pool contents (possibly NaN bit
+            // patterns): zero their V so that 0 * garbage cannot reach the
+            // MFMA.  One 64-bit mask per 4-key piece a lane holds.
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
+            for (int tt = 0; tt < 4; ++tt) {
+                const int nk = n_valid - (key0 + 16 * tt + 4 * grp);
+                const unsigned long long mk =
+                    nk >= 4 ? ~0ull : (nk <= 0 ? 0ull : (1ull << (16 * nk)) - 1ull);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (key0 + 16 * tt + 4 * grp + i >= n_valid)
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) vr[dt][tt >> 1][tt & 1][i] = 0;
+                for (int dt = 0; dt < DT; ++dt)
+                    vr[dt][tt >> 1][tt & 1] = __builtin_bit_cast(
+                        h4, __builtin_bit_cast(unsigned long long, vr[dt][tt >> 1][tt & 1]) & mk);
+            }
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
