@@ -169,6 +169,10 @@ typedef struct {
     int32_t workgroups;     /* persistent workgroups of the attention kernel;
                                0 = 2 per compute unit of the current device
                                (512 when no device is visible)                */
+    int32_t unit_rows;      /* smallest phase-1 row block run as a workgroup
+                               unit (LDS-shared loads); 0 = default 17.  A
+                               value above 64 runs every phase-1 row group
+                               as a single-wave task.                         */
 } pkvt_plan_opts;
 
 typedef struct {
@@ -186,6 +190,9 @@ typedef struct {
     int32_t tasks;          /* wave tasks (waves x heads)                      */
     int32_t phase1_split;   /* chunks per phase-1 item actually used           */
     int32_t phase2_split;   /* chunks per phase-2 item actually used           */
+    int32_t wg_units;       /* workgroup units: phase-1 row blocks of 17..64
+                               rows whose 4 waves share every K/V load through
+                               LDS                                             */
 } pkvt_plan_info;
 
 /* Build the plan for a batch.  opts may be NULL (defaults).  Reports the

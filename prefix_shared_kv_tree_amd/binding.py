@@ -39,7 +39,7 @@ class Stats(C.Structure):
 
 class PlanOpts(C.Structure):
     _fields_ = [("phase1_chunks", C.c_int32), ("phase2_chunks", C.c_int32),
-                ("min_share", C.c_int32), ("workgroups", C.c_int32)]
+                ("min_share", C.c_int32), ("workgroups", C.c_int32), ("unit_rows", C.c_int32)]
 
 
 class PlanInfo(C.Structure):
@@ -48,7 +48,8 @@ class PlanInfo(C.Structure):
                 ("merge_rows", C.c_int32), ("shared_chunks", C.c_int32),
                 ("unique_tokens", C.c_int64), ("logical_tokens", C.c_int64),
                 ("structure_version", C.c_int32), ("tasks", C.c_int32),
-                ("phase1_split", C.c_int32), ("phase2_split", C.c_int32)]
+                ("phase1_split", C.c_int32), ("phase2_split", C.c_int32),
+                ("wg_units", C.c_int32)]
 
 
 _i32p = C.POINTER(C.c_int32)
@@ -211,10 +212,10 @@ def pkvt_tree_chunk_refcount(tree: int, chunk_id: int) -> int:
 # ---- plan ---------------------------------------------------------------------
 
 def pkvt_plan(tree: int, q_order, phase1_chunks: int = 0, phase2_chunks: int = 0,
-              min_share: int = 0, workgroups: int = 0) -> Tuple[int, int]:
+              min_share: int = 0, workgroups: int = 0, unit_rows: int = 0) -> Tuple[int, int]:
     """Plan a batch; returns (meta_bytes, workspace_bytes)."""
     q = _i32(q_order)
-    opts = PlanOpts(phase1_chunks, phase2_chunks, min_share, workgroups)
+    opts = PlanOpts(phase1_chunks, phase2_chunks, min_share, workgroups, unit_rows)
     mb, wb = _sz(), _sz()
     _check("pkvt_plan", load().pkvt_plan(tree, q.size, _p32(q) if q.size else None,
                                          C.byref(opts), C.byref(mb), C.byref(wb)))

@@ -10,36 +10,41 @@
 // O = o / n.  The score scale 1/sqrt(d) is the attention definition's
 // (CachedAttention digest, "Load-bearing equations").
 //
-// One kernel serves both phases.  Its unit of work is a wave task: up to 16
-// query rows of one head against a list of chunks.  A phase-1 item with R
-// rows gives ceil(R/16) tasks per head that the planner places on the waves
-// of one workgroup, so the waves reading the same shared chunks share the
-// CU's caches; a phase-2 item gives one single-row task per head.  The grid
-// is a fixed set of persistent workgroups; every wave walks its own task
-// list (filled longest-first by the planner) and streams the tasks' chunks
-// 64 keys at a time through the matrix cores:
+// One kernel serves both phases.  The grid is a fixed set of persistent
+// workgroups of 4 waves.  Every step of the streaming loop takes 64 keys of
+// one head through the matrix cores:
 //
 //   S^T (keys x rows)  = K  . Q^T    v_mfma_f32_16x16x32_f16, K as the A operand
 //   O^T (dims x rows) += V^T . P^T   v_mfma_f32_16x16x32_f16, V^T as the A operand
 //
-// The loads of the next step -- or of the next task's first step, with its
-// queries -- are issued as soon as the registers they land in are free, so
-// a wave keeps about one step (32 KiB of K and V) in flight across task
-// boundaries too.  K and V are read once, with non-temporal loads.
+// so one wave covers up to 16 query rows.  Work comes in two forms:
 //
-// With one query row (phase 2) 15 of the 16 MFMA columns idle; that costs
-// nothing measurable, because a decode step does ~1 FLOP per byte while the
-// matrix cores sustain ~300, and it keeps both phases on one code path with
-// the same streaming loads.  The pool layouts are chosen so that the A-operand
-// fragments are whole 16-byte (K) and 8-byte (V) pieces and 16 consecutive
-// lanes read 256 (K) or 128 (V) consecutive bytes:
+//  * Workgroup units (phase-1 row blocks of 17..64 rows).  The unit's waves
+//    split the loads of every step (each reads 1/4 or 1/2 of the step's K
+//    and V into registers, then writes it to LDS), meet at a barrier, and
+//    each wave computes 16 of the rows from the LDS copy.  Every stored byte
+//    of a shared chunk is thus fetched once per row block, by one load
+//    instruction, however many rows read it.  Each workgroup runs its units
+//    first, all 4 waves in lock step.
+//  * Single-wave tasks (phase-2 items, and phase-1 row blocks of <= 16
+//    rows): every wave then walks its own list of tasks, keeping the next
+//    step's K/V -- or the next task's queries and first K/V -- in flight
+//    while it computes the current step.
+//
+// The planner fills both lists longest first.  With one query row (phase 2)
+// 15 of the 16 MFMA columns idle; that costs nothing measurable, because a
+// decode step does ~1 FLOP per byte while the matrix cores sustain ~300, and
+// it keeps both phases on the same streaming loop.  The pool layouts are
+// chosen so that the A-operand fragments are whole 16-byte (K) and 8-byte (V)
+// pieces and 16 consecutive lanes read 256 (K) or 128 (V) consecutive bytes:
 //   K slice [d/8][c][8]: the 8 dims a lane needs for one key are contiguous,
 //                        and consecutive keys are 16 bytes apart;
 //   V slice [c/4][d][4]: 4 consecutive keys of one dim are contiguous, and
 //                        consecutive dims are 8 bytes apart.
 // The online softmax (max, exp2, rescale) runs in fp32 on the S^T fragments;
 // P is rounded to fp16 for the PV product and n sums those rounded weights.
-// Scores are scaled by scale*log2(e) in fp32 so exp2 gives exp.
+// Scores are scaled by scale*log2(e) in fp32 so exp2 gives exp.  K and V are
+// read with non-temporal loads.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -55,21 +60,11 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kStep = 64;          // keys per step of the streaming loop
+constexpr int kVPad = 128;         // LDS padding after each 4-key group of a V image
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Wave-uniform description of one task.
-struct Task {
-    const int32_t* chunks;   // the task's chunk ids
-    int n_valid;             // keys to attend over
-    int n_steps;             // ceil(n_valid / 64)
-    int row_lo;              // depth-first position of query row 0
-    int n_rows;
-    int out;                 // partial slot of row 0, or -1: write O
-    int head;
-};
 
 // The plan metadata is read-only for the whole launch.  Reading it through
 // the constant address space lets the compiler use scalar loads: task fields
@@ -78,6 +73,273 @@ struct Task {
 // retires in order).
 typedef const __attribute__((address_space(4))) int32_t cint;
 __device__ __forceinline__ cint* meta(const int32_t* p) { return (cint*)(p); }
+
+// Start of the 16-key tile tt of a step, clamped to the last tile that holds
+// a valid key.  Loads are issued unconditionally so that the compiler can
+// count them and wait for exactly the step it needs (a branch around a load
+// makes it wait for everything); a tile past the end re-reads the last valid
+// tile -- same addresses, so no extra HBM traffic -- and its scores are
+// forced to -inf and its V entries zeroed by softmax_pv.
+__device__ __forceinline__ int tile_start(int step, int tt, int n_valid) {
+    const int key = step * kStep + 16 * tt;
+    const int last = (n_valid - 1) & ~15;
+    return key < last ? key : last;
+}
+
+// S^T = K Q^T for the 64 keys of a step: tile tt = keys 16tt .. 16tt+15.
+template <int KS>
+__device__ __forceinline__ void qk(f4 (&s)[4], const h8 (&kr)[4][KS], const h8 (&qb)[KS]) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        s[tt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[tt][ks], qb[ks], s[tt], 0, 0, 0);
+    }
+}
+
+// Online softmax of one step (partial_attn) folded into the running state
+// (attn_reduce): lane (col, grp) holds the scores of query row col for keys
+// 16tt + 4grp + i.  Returns P^T as two fp16 B operands (keys of tiles
+// 2hs, 2hs+1) and rescales o to the new running max.
+template <int DT>
+__device__ __forceinline__ void softmax_step(f4 (&s)[4], h8 (&pb)[2], f4 (&o)[DT], float& m_run,
+                                             float& l_run, int step, int n_valid, int grp,
+                                             float scale_log2e) {
+    const int key0 = step * kStep;
+    const bool tail = key0 + kStep > n_valid;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float x = s[tt][i] * scale_log2e;
+            if (tail && key0 + 16 * tt + 4 * grp + i >= n_valid) x = -INFINITY;
+            s[tt][i] = x;
+            mx = fmaxf(mx, x);
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);        // finite: every step has a valid key
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const _Float16 p = static_cast<_Float16>(fast_exp2(s[e >> 2][e & 3] - m_new));
+        pb[e >> 3][e & 7] = p;
+        lsum += static_cast<float>(p);
+    }
+    l_run = l_run * alpha + lsum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+}
+
+// Keys past the end hold stale pool contents (possibly NaN bit patterns):
+// zero the V entries of a 4-key piece that lie past n_valid so that
+// 0 * garbage cannot reach the MFMA.  key = first key of the piece.
+__device__ __forceinline__ h4 mask_v(h4 v, int key, int n_valid) {
+    const int nk = n_valid - key;
+    const unsigned long long mk = nk >= 4 ? ~0ull : (nk <= 0 ? 0ull : (1ull << (16 * nk)) - 1ull);
+    return __builtin_bit_cast(h4, __builtin_bit_cast(unsigned long long, v) & mk);
+}
+
+// O^T += V^T P^T for one 16-dim tile: v[hs][*] holds V of dim 16dt + col for
+// the keys of tiles 2hs and 2hs+1 that the lane's P covers.
+__device__ __forceinline__ f4 pv_tile(f4 o, const h4 (&v)[2][2], const h8 (&pb)[2]) {
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+        const h8 va = __builtin_shufflevector(v[hs][0], v[hs][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[hs], o, 0, 0, 0);
+    }
+    return o;
+}
+
+// softmax_step, then the PV product with a whole step of V in registers.
+template <int DT>
+__device__ __forceinline__ void softmax_pv(f4 (&s)[4], h4 (&vr)[DT][2][2], f4 (&o)[DT],
+                                           float& m_run, float& l_run, int step, int n_valid,
+                                           int grp, float scale_log2e) {
+    h8 pb[2];
+    softmax_step<DT>(s, pb, o, m_run, l_run, step, n_valid, grp, scale_log2e);
+    const int key0 = step * kStep;
+    if (key0 + kStep > n_valid) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                vr[dt][tt >> 1][tt & 1] = mask_v(vr[dt][tt >> 1][tt & 1], key0 + 16 * tt + 4 * grp, n_valid);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = pv_tile(o[dt], vr[dt], pb);
+}
+
+// End of a task for query row col (lane group grp holds dims 16dt + 4grp ..):
+// either the final O = o / n in fp16 (out < 0) or the partial (o, m, n) of
+// slot out + col.  qrow < 0 marks a lane without a row.
+template <int D, int DT>
+__device__ __forceinline__ void finish(const AttnArgs& a, const f4 (&o)[DT], float m_run,
+                                       float l_run, int qrow, int out, int head, int col, int grp) {
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (qrow < 0) return;
+    const int H = a.H;
+    if (out < 0) {
+        const float inv = 1.0f / l_tot;
+        _Float16* op = static_cast<_Float16*>(a.out) + (static_cast<size_t>(qrow) * H + head) * D + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            h4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = static_cast<_Float16>(o[dt][i] * inv);
+            *reinterpret_cast<h4*>(op + 16 * dt) = v;
+        }
+    } else {
+        const size_t slot = static_cast<size_t>(out + col);
+        float* po = a.part_o + (slot * H + head) * D + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f4*>(po + 16 * dt) = o[dt];
+        if (grp == 0) {
+            float* pm = a.part_ml + (slot * H + head) * 2;
+            pm[0] = m_run;
+            pm[1] = l_tot;
+        }
+    }
+}
+
+// Bytes of a workgroup unit's LDS image of one step: K as [tile][d/8][16 keys][8],
+// then V as [tile][4-key group][d][4] with kVPad bytes after every group.
+template <int D>
+struct Img {
+    static constexpr int kBytesK = kStep * D * 2;
+    static constexpr int kGroupV = D * 8 + kVPad;
+    static constexpr int kBytes = kBytesK + (kStep / 4) * kGroupV;
+    static constexpr int kPieces = 16 * D;        // 16-byte pieces of K and V together
+};
+
+// One workgroup unit: query rows [row_lo, row_lo + n_rows) of one head.
+// Wave w loads pieces [w, w + 1) * kPieces / 4 of every step's image and
+// computes rows 16w .. 16w + 15 (if it has any) from the LDS copy.  The trip
+// count comes from the unit descriptor that all 4 waves read, so every wave
+// passes the same number of barriers.
+template <int D, int C>
+__device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, int lane, char* img) {
+    constexpr int KS = D / 32, DT = D / 16;
+    constexpr int kPer = Img<D>::kPieces / kWaves;   // pieces per wave per step
+    constexpr int NL = kPer / 64;                    // 16-byte loads per lane per step
+    static_assert(kPer % 64 == 0 && (2 * D) % 64 == 0, "piece split");
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int H = a.H;
+    const int n_keys = u[0];
+    cint* chunks = meta(a.chunks) + u[1];
+    const int head = u[3];
+    const int row_lo = u[4];
+    const int n_rows = u[5];
+    const int out = u[6];
+    const int role = wave;
+    const bool computes = 16 * role < n_rows;
+    const int n_steps = (n_keys + kStep - 1) / kStep;
+    const size_t slice = static_cast<size_t>(C) * D * 2;      // bytes per (chunk, head)
+    const char* kbase = static_cast<const char*>(a.kpool) + static_cast<size_t>(head) * slice;
+    const char* vbase = static_cast<const char*>(a.vpool) + static_cast<size_t>(head) * slice;
+    const size_t cstride = static_cast<size_t>(H) * slice;    // bytes per chunk
+
+    h8 stg[NL];
+    // piece j of the image: K pieces [0, 8D) as (tile, d/8 piece, key), then
+    // V pieces [8D, 16D) as (tile, byte offset / 16 in the tile's V block)
+    auto stage = [&](int step) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int j0 = role * kPer + i * 64;                   // wave-uniform
+            const bool is_k = j0 < 8 * D;
+            const int jj = is_k ? j0 : j0 - 8 * D;
+            const int ts = tile_start(step, jj / (2 * D), n_keys);
+            const int rem = jj % (2 * D) + lane;
+            const size_t cbytes = static_cast<size_t>(chunks[ts / C]) * cstride;
+            const char* kp = kbase + cbytes + (static_cast<size_t>(rem >> 4) * C + ts % C + (rem & 15)) * 16;
+            const char* vp = vbase + cbytes + static_cast<size_t>((ts % C) / 4) * (D * 8) + rem * 16;
+            stg[i] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(is_k ? kp : vp));
+        }
+    };
+    auto commit = [&]() {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int j = role * kPer + i * 64 + lane;
+            const int jv = j - 8 * D;
+            const int tt = jv / (2 * D);
+            const int rem = jv % (2 * D);
+            const int voff = Img<D>::kBytesK + (tt * 4 + rem / (D / 2)) * Img<D>::kGroupV +
+                             (rem % (D / 2)) * 16;
+            *reinterpret_cast<h8*>(img + (j < 8 * D ? j * 16 : voff)) = stg[i];
+        }
+    };
+
+    h8 qb[KS];
+    int qrow = -1;
+    if (computes) {
+        const int r = 16 * role + col;
+        qrow = r < n_rows ? a.rows[row_lo + r] : -1;
+        const _Float16* qp = static_cast<const _Float16*>(a.q) +
+                             (static_cast<size_t>(qrow < 0 ? 0 : qrow) * H + head) * D + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qb[ks] = qrow >= 0 ? *reinterpret_cast<const h8*>(qp + 32 * ks) : h8{};
+    }
+    f4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    stage(0);
+    for (int step = 0; step < n_steps; ++step) {
+        __syncthreads();                       // every wave is done reading the last image
+        commit();
+        __syncthreads();                       // this step's image is complete
+        if (step + 1 < n_steps) stage(step + 1);
+        if (computes) {
+            // fragments are read from LDS tile by tile, next to the MFMAs
+            // that use them, to keep register pressure low
+            f4 s[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                s[tt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const h8 kf = *reinterpret_cast<const h8*>(
+                        img + ((tt * (D / 8) + 4 * ks + grp) * 16 + col) * 16);
+                    s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qb[ks], s[tt], 0, 0, 0);
+                }
+            }
+            h8 pb[2];
+            softmax_step<DT>(s, pb, o, m_run, l_run, step, n_keys, grp, a.scale_log2e);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                h4 v[2][2];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    v[tt >> 1][tt & 1] = mask_v(
+                        *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
+                                                     (tt * 4 + grp) * Img<D>::kGroupV + (16 * dt + col) * 8),
+                        step * kStep + 16 * tt + 4 * grp, n_keys);
+                o[dt] = pv_tile(o[dt], v, pb);
+            }
+        }
+    }
+    if (computes) finish<D, DT>(a, o, m_run, l_run, qrow, out + 16 * role, head, col, grp);
+}
+
+// Wave-uniform description of one single-wave task.
+struct Task {
+    cint* chunks;            // the task's chunk ids
+    int n_valid;             // keys to attend over
+    int n_steps;             // ceil(n_valid / 64)
+    int row_lo;              // depth-first position of query row 0
+    int n_rows;
+    int out;                 // partial slot of row 0, or -1: write O
+    int head;
+};
 
 template <int C>
 __device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
@@ -89,7 +351,7 @@ __device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
     const int n_chunks = wd[1];
     const int key_base = wd[2];
     const int len_row = wd[3];
-    t.chunks = a.chunks + wd[0];
+    t.chunks = meta(a.chunks) + wd[0];
     t.row_lo = wd[4];
     t.n_rows = wd[5];
     t.out = wd[6];
@@ -106,19 +368,30 @@ void attn_kernel(AttnArgs a) {
     static_assert(D % 32 == 0 && C % 16 == 0, "tile shape");
     constexpr int KS = D / 32;     // 32-dim k-steps of Q K^T
     constexpr int DT = D / 16;     // 16-dim output tiles of P V
+    __shared__ __attribute__((aligned(16))) char lds[Img<D>::kBytes];
     const int H = a.H;
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int col = lane & 15;     // MFMA row/column index held by this lane
     const int grp = lane >> 4;     // which 8-element k slice of the fragment
+
+    // ---- this workgroup's units, all 4 waves together ---------------------------
+    {
+        const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
+        const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
+        for (int k = 0; k < ucount; ++k)
+            run_unit<D, C>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
+    }
+
+    // ---- this wave's single-wave tasks ------------------------------------------
     const int lane_id = blockIdx.x * kWaves + wave;
     const int first = meta(a.lists)[2 * lane_id];
     const int count = meta(a.lists)[2 * lane_id + 1];
     if (count == 0) return;
 
+    const size_t slice = static_cast<size_t>(C) * D;          // halves per (chunk, head)
     const _Float16* __restrict__ kpool = static_cast<const _Float16*>(a.kpool);
     const _Float16* __restrict__ vpool = static_cast<const _Float16*>(a.vpool);
-    const size_t slice = static_cast<size_t>(C) * D;          // halves per (chunk, head)
 
     h8 qb[KS];        // Q^T (B operand): row col, dims 32*ks + 8*grp .. +7
     h8 kr[4][KS];     // K of one step: tile t = keys 16t .. 16t+15
@@ -139,21 +412,11 @@ void attn_kernel(AttnArgs a) {
     auto slice_of = [&](const _Float16* pool, int chunk, int head) {
         return reinterpret_cast<const char*>(pool + (static_cast<size_t>(chunk) * H + head) * slice);
     };
-    // Loads are unconditional so the compiler can count them exactly and wait
-    // for just the step it needs (a branch around a load makes it wait for
-    // everything).  A tile past the end of the keys re-reads the last tile
-    // that has valid keys -- same addresses, so no extra HBM traffic -- and
-    // its scores are forced to -inf and its V entries zeroed below.
-    auto tile_key = [&](const Task& t, int step, int tt) {
-        const int key = step * kStep + 16 * tt;
-        const int last = (t.n_valid - 1) & ~15;
-        return key < last ? key : last;
-    };
     auto load_k = [&](const Task& t, int step) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const int key = tile_key(t, step, tt);
-            const char* base = slice_of(kpool, meta(t.chunks)[key / C], t.head) + (key % C) * 16;
+            const int key = tile_start(step, tt, t.n_valid);
+            const char* base = slice_of(kpool, t.chunks[key / C], t.head) + (key % C) * 16;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 kr[tt][ks] = __builtin_nontemporal_load(
@@ -163,9 +426,8 @@ void attn_kernel(AttnArgs a) {
     auto load_v = [&](const Task& t, int step) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const int key = tile_key(t, step, tt);
-            const char* base = slice_of(vpool, meta(t.chunks)[key / C], t.head) +
-                               ((key % C) / 4) * (D * 8);
+            const int key = tile_start(step, tt, t.n_valid);
+            const char* base = slice_of(vpool, t.chunks[key / C], t.head) + ((key % C) / 4) * (D * 8);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 vr[dt][tt >> 1][tt & 1] =
@@ -190,75 +452,6 @@ void attn_kernel(AttnArgs a) {
     f4 o[DT];
     float m_run, l_run;
     f4 s[4];
-
-    // S^T = K Q^T for the 64 keys of a step
-    auto qk = [&]() {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            s[tt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kr[tt][ks], qb[ks], s[tt], 0, 0, 0);
-        }
-    };
-    // online softmax of the step (partial_attn) folded into the run
-    // (attn_reduce), then O^T += V^T P^T
-    auto softmax_pv = [&](int step, int n_valid) {
-        const int key0 = step * kStep;
-        const bool tail = key0 + kStep > n_valid;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x = s[tt][i] * a.scale_log2e;
-                if (tail && key0 + 16 * tt + 4 * grp + i >= n_valid) x = -INFINITY;
-                s[tt][i] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);        // finite: every step has a valid key
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        h8 pb[2];
-        float lsum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const _Float16 p = static_cast<_Float16>(fast_exp2(s[e >> 2][e & 3] - m_new));
-            pb[e >> 3][e & 7] = p;
-            lsum += static_cast<float>(p);
-        }
-        l_run = l_run * alpha + lsum;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-        if (tail) {
-            // keys past the end hold stale pool contents (possibly NaN bit
-            // patterns): zero their V so that 0 * garbage cannot reach the
-            // MFMA.  One 64-bit mask per 4-key piece a lane holds.
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const int nk = n_valid - (key0 + 16 * tt + 4 * grp);
-                const unsigned long long mk =
-                    nk >= 4 ? ~0ull : (nk <= 0 ? 0ull : (1ull << (16 * nk)) - 1ull);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    vr[dt][tt >> 1][tt & 1] = __builtin_bit_cast(
-                        h4, __builtin_bit_cast(unsigned long long, vr[dt][tt >> 1][tt & 1]) & mk);
-            }
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-            for (int hs = 0; hs < 2; ++hs) {
-                const h8 va = __builtin_shufflevector(vr[dt][hs][0], vr[dt][hs][1],
-                                                      0, 1, 2, 3, 4, 5, 6, 7);
-                o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[hs], o[dt], 0, 0, 0);
-            }
-        }
-    };
-
     for (;;) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -267,46 +460,19 @@ void attn_kernel(AttnArgs a) {
         // all steps but the last: the next step's K and V follow right behind
         const int n_steps = cur.n_steps;
         for (int step = 0; step + 1 < n_steps; ++step) {
-            qk();
+            qk<KS>(s, kr, qb);
             load_k(cur, step + 1);
-            softmax_pv(step, cur.n_valid);
+            softmax_pv<DT>(s, vr, o, m_run, l_run, step, cur.n_valid, grp, a.scale_log2e);
             load_v(cur, step + 1);
         }
         // last step: the next task's queries and K/V follow instead
-        qk();
+        qk<KS>(s, kr, qb);
         if (has_next) {
             load_q(nxt, nxt_qrow);
             load_k(nxt, 0);
         }
-        softmax_pv(n_steps - 1, cur.n_valid);
-
-        // ---- task epilogue: n of row col = sum over the four lane groups --------
-        float l_tot = l_run + __shfl_xor(l_run, 16);
-        l_tot += __shfl_xor(l_tot, 32);
-        if (cur_qrow >= 0) {
-            if (cur.out < 0) {
-                const float inv = 1.0f / l_tot;
-                _Float16* op = static_cast<_Float16*>(a.out) +
-                               (static_cast<size_t>(cur_qrow) * H + cur.head) * D + 4 * grp;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    h4 v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = static_cast<_Float16>(o[dt][i] * inv);
-                    *reinterpret_cast<h4*>(op + 16 * dt) = v;
-                }
-            } else {
-                const size_t slot = static_cast<size_t>(cur.out + col);
-                float* po = a.part_o + (slot * H + cur.head) * D + 4 * grp;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f4*>(po + 16 * dt) = o[dt];
-                if (grp == 0) {
-                    float* pm = a.part_ml + (slot * H + cur.head) * 2;
-                    pm[0] = m_run;
-                    pm[1] = l_tot;
-                }
-            }
-        }
+        softmax_pv<DT>(s, vr, o, m_run, l_run, n_steps - 1, cur.n_valid, grp, a.scale_log2e);
+        finish<D, DT>(a, o, m_run, l_run, cur_qrow, cur.out, cur.head, col, grp);
         if (!has_next) break;
         load_v(nxt, 0);
         cur = nxt;

@@ -192,6 +192,7 @@ pkvt_status pkvt_plan(pkvt_tree* t, int32_t b, const int32_t* q_order, const pkv
         o.phase2_chunks = opts->phase2_chunks;
         o.min_share = opts->min_share;
         o.workgroups = opts->workgroups;
+        o.unit_rows = opts->unit_rows;
     }
     if (o.workgroups < 0) return fail(PKVT_ERR_INVALID_ARG, "plan: workgroups must be >= 0");
     if (o.workgroups == 0) o.workgroups = default_workgroups();
@@ -225,6 +226,7 @@ pkvt_status pkvt_plan_info_get(const pkvt_tree* t, pkvt_plan_info* out) {
     out->tasks = p.n_tasks;
     out->phase1_split = p.split1_chunks;
     out->phase2_split = p.split2_chunks;
+    out->wg_units = p.n_units;
     return PKVT_OK;
 }
 
@@ -316,6 +318,8 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* t, const void* d_meta, const vo
     a.lists = m + p.blob[pkvt::kOffLists];
     a.tasks = m + p.blob[pkvt::kOffTasks];
     a.waves = m + p.blob[pkvt::kOffWaves];
+    a.wg_units = m + p.blob[pkvt::kOffWgUnits];
+    a.units = m + p.blob[pkvt::kOffUnits];
     a.chunks = m + p.blob[pkvt::kOffChunks];
     a.rows = m + p.blob[pkvt::kOffRows];
     a.seqlen = m + p.blob[pkvt::kOffSeqlen];
@@ -326,7 +330,7 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* t, const void* d_meta, const vo
     a.part_o = part_o;
     a.part_ml = part_ml;
     a.H = H;
-    a.n_wg = p.n_tasks > 0 ? p.n_wg : 0;
+    a.n_wg = (p.n_tasks > 0 || p.n_units > 0) ? p.n_wg : 0;
     a.scale_log2e = scale * 1.4426950408889634f;
     hipError_t e = pkvt::launch_attn(a, D, C, s);
     if (e != hipSuccess) return hip_fail(e, "attn_decode: attention kernel");

@@ -12,6 +12,8 @@ struct AttnArgs {
     const int32_t* lists;     // [4*n_wg][2] per wave lane: first task, task count
     const int32_t* tasks;     // [n_tasks][2] (wave descriptor, head)
     const int32_t* waves;     // [n_waves][8] WaveDesc
+    const int32_t* wg_units;  // [n_wg][2] per workgroup: first unit, unit count
+    const int32_t* units;     // [n_units][16] UnitDesc
     const int32_t* chunks;    // chunk ids
     const int32_t* rows;      // [b] depth-first position -> query row
     const int32_t* seqlen;    // [b] tokens per depth-first position

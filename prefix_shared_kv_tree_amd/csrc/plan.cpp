@@ -12,12 +12,14 @@
 //    items of at most phase2_chunks chunks.
 // 4. A sequence with exactly one item, a phase-2 one, is finalised by that
 //    item; every other sequence's partials are merged afterwards.
-// 5. Every (item, row group of 16, head) is a wave task.  The attention
-//    kernel runs G persistent workgroups of 4 waves; each wave walks a task
-//    list.  Lists are filled longest-task-first: the row groups of one
-//    phase-1 item go to the 4 waves of one workgroup, so they stream the
-//    same chunks together, and phase-2 tasks go to the least loaded wave.
-//    Items are cut so that no task is longer than the mean per-wave load.
+// 5. The attention kernel runs G persistent workgroups of 4 waves.  Work is
+//    handed out longest first.  A phase-1 item's rows are cut into blocks
+//    of up to 64; a block of more than 16 rows is a workgroup unit per head,
+//    whose 4 waves split the loads of every step and share them through
+//    LDS; it goes to the workgroup whose busiest wave is least loaded.  Every other (item, head)
+//    -- phase 2, and phase-1 blocks of <= 16 rows -- is a single-wave task
+//    that goes to the least loaded wave.  Items are cut so that no task is
+//    longer than the mean per-wave load.
 #include "plan.h"
 
 #include <algorithm>
@@ -70,8 +72,11 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     }
     PlanOpts opts = in_opts;
     if (opts.min_share == 0) opts.min_share = 2;
-    if (opts.min_share < 2 || opts.phase1_chunks < 0 || opts.phase2_chunks < 0) {
-        err = "plan: min_share must be >= 2 (or 0 for the default); chunk limits >= 0";
+    if (opts.unit_rows == 0) opts.unit_rows = kRowsPerWave + 1;
+    if (opts.min_share < 2 || opts.phase1_chunks < 0 || opts.phase2_chunks < 0 ||
+        opts.unit_rows <= kRowsPerWave) {
+        err = "plan: min_share must be >= 2 (or 0 for the default); chunk limits >= 0; "
+              "unit_rows > 16 (or 0 for the default)";
         return PKVT_ERR_INVALID_ARG;
     }
     const int32_t G = opts.workgroups > 0 ? opts.workgroups : kDefaultWorkgroups;
@@ -261,10 +266,16 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         }
     }
 
-    // ---- 5. wave descriptors and per-lane task lists ---------------------------------
+    // ---- 5. wave descriptors, workgroup units and per-lane task lists -----------------
     std::vector<WaveDesc> waves;
     std::vector<const std::vector<int32_t>*> wave_chunks;
     std::vector<int64_t> wave_cost;
+    auto item_keys = [&](const Item& it) {
+        int64_t keys = static_cast<int64_t>(it.chunks.size()) * t.C;
+        if (it.len_row >= 0)
+            keys = std::min<int64_t>(keys, seqs[dfs_row[it.len_row]]->len - it.key_base);
+        return keys;
+    };
     auto add_wave = [&](const Item& it, int32_t row_off) {
         WaveDesc w{};
         w.n_chunks = static_cast<int32_t>(it.chunks.size());
@@ -273,59 +284,55 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         w.row_lo = it.row_lo + row_off;
         w.n_rows = std::min(kRowsPerWave, it.n_rows - row_off);
         w.out = it.out < 0 ? -1 : it.out + row_off;
-        int64_t keys = static_cast<int64_t>(w.n_chunks) * t.C;
-        if (it.len_row >= 0)
-            keys = std::min<int64_t>(keys, seqs[dfs_row[it.len_row]]->len - it.key_base);
         waves.push_back(w);
         wave_chunks.push_back(&it.chunks);
-        wave_cost.push_back(task_cost(static_cast<int32_t>(keys)));
+        wave_cost.push_back(task_cost(static_cast<int32_t>(item_keys(it))));
         return static_cast<int32_t>(waves.size()) - 1;
     };
-    struct Unit { std::vector<int32_t> waves; int64_t cost; };
-    std::vector<Unit> units;                 // phase-1: row groups of one item, <= 4 waves
+    // Phase-1 rows are cut into blocks of kRowsPerUnit.  A block of at least
+    // unit_rows rows (default: more than one row group) becomes one workgroup
+    // unit per head, in which the 4 waves split every step's loads and share
+    // the data through LDS.  Smaller blocks are cut into single-wave tasks of
+    // up to 16 rows, like phase 2.
+    struct Unit { const Item* it; int32_t r0, rows, head, keys; int64_t cost; };
+    std::vector<Unit> units;
+    std::vector<int32_t> singles;            // single-wave tasks (x heads)
     for (const Item& it : items1) {
-        for (int32_t r0 = 0; r0 < it.n_rows; r0 += kRowsPerWave * kWavesPerWg) {
-            Unit u;
-            for (int32_t r = r0; r < std::min(it.n_rows, r0 + kRowsPerWave * kWavesPerWg);
-                 r += kRowsPerWave)
-                u.waves.push_back(add_wave(it, r));
-            u.cost = wave_cost[u.waves[0]];
-            units.push_back(std::move(u));
+        const int32_t keys = static_cast<int32_t>(item_keys(it));
+        for (int32_t r0 = 0; r0 < it.n_rows; r0 += kRowsPerUnit) {
+            const int32_t rb = std::min(kRowsPerUnit, it.n_rows - r0);
+            if (rb < opts.unit_rows) {
+                for (int32_t r = r0; r < r0 + rb; r += kRowsPerWave) singles.push_back(add_wave(it, r));
+                continue;
+            }
+            for (int32_t h = 0; h < t.H; ++h) units.push_back({&it, r0, rb, h, keys, task_cost(keys)});
         }
     }
-    std::vector<int32_t> singles;            // phase-2 waves
     for (const Item& it : items2) singles.push_back(add_wave(it, 0));
 
+    std::vector<std::vector<int32_t>> wg_units(G);
     std::vector<std::vector<std::pair<int32_t, int32_t>>> lists(lanes);   // (wave, head)
     std::vector<int64_t> load(lanes, 0);
     {
-        // phase-1 units x heads -> the workgroup whose busiest wave is least loaded
-        std::vector<std::pair<int64_t, int32_t>> ut;         // (cost, unit*H + head)
-        for (size_t u = 0; u < units.size(); ++u)
-            for (int32_t h = 0; h < t.H; ++h)
-                ut.push_back({units[u].cost, static_cast<int32_t>(u) * t.H + h});
-        std::stable_sort(ut.begin(), ut.end(),
-                         [](const auto& a, const auto& c) { return a.first > c.first; });
         using QE = std::pair<int64_t, int32_t>;
+        // workgroup units, longest first -> the workgroup whose busiest wave is least loaded
+        std::vector<int32_t> order(units.size());
+        for (size_t i = 0; i < order.size(); ++i) order[i] = static_cast<int32_t>(i);
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int32_t a, int32_t c) { return units[a].cost > units[c].cost; });
         std::priority_queue<QE, std::vector<QE>, std::greater<QE>> wgq;
         for (int32_t g = 0; g < G; ++g) wgq.push({0, g});
-        for (const auto& e : ut) {
+        for (int32_t ui : order) {
             const auto top = wgq.top();
             wgq.pop();
             const int32_t g = top.second;
-            const Unit& u = units[e.second / t.H];
-            const int32_t h = e.second % t.H;
             int64_t start = 0;
             for (int32_t k = 0; k < kWavesPerWg; ++k) start = std::max(start, load[g * kWavesPerWg + k]);
-            for (size_t k = 0; k < u.waves.size(); ++k) {
-                lists[g * kWavesPerWg + k].push_back({u.waves[k], h});
-                load[g * kWavesPerWg + k] = start + e.first;
-            }
-            int64_t mx = 0;
-            for (int32_t k = 0; k < kWavesPerWg; ++k) mx = std::max(mx, load[g * kWavesPerWg + k]);
-            wgq.push({mx, g});
+            for (int32_t k = 0; k < kWavesPerWg; ++k) load[g * kWavesPerWg + k] = start + units[ui].cost;
+            wg_units[g].push_back(ui);
+            wgq.push({start + units[ui].cost, g});
         }
-        // phase-2 waves x heads -> the least loaded wave
+        // single-wave tasks x heads, longest first -> the least loaded wave
         std::vector<std::pair<int64_t, int32_t>> st;         // (cost, single*H + head)
         for (size_t i = 0; i < singles.size(); ++i)
             for (int32_t h = 0; h < t.H; ++h)
@@ -345,10 +352,12 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
 
     // ---- 6. emit the blob -------------------------------------------------------------
     const int32_t n_waves = static_cast<int32_t>(waves.size());
+    const int32_t n_units = static_cast<int32_t>(units.size());
     int32_t n_tasks = 0;
     for (auto& l : lists) n_tasks += static_cast<int32_t>(l.size());
     int32_t total_chunks = 0;
     for (auto* l : wave_chunks) total_chunks += static_cast<int32_t>(l->size());
+    for (const Unit& u : units) total_chunks += static_cast<int32_t>(u.it->chunks.size());
     std::vector<int32_t> merge_rows;
     for (int32_t p = 0; p < b; ++p)
         if (!mslots[p].empty()) merge_rows.push_back(p);
@@ -364,6 +373,8 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     section(kOffLists, static_cast<size_t>(lanes) * 2);
     section(kOffTasks, static_cast<size_t>(n_tasks) * 2);
     section(kOffWaves, static_cast<size_t>(n_waves) * 8);
+    section(kOffWgUnits, static_cast<size_t>(G) * 2);
+    section(kOffUnits, static_cast<size_t>(n_units) * 8);
     section(kOffChunks, total_chunks);
     section(kOffRows, b);
     section(kOffMerge, merge_rows.size());
@@ -391,6 +402,26 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
             std::copy(reinterpret_cast<const int32_t*>(&d),
                       reinterpret_cast<const int32_t*>(&d) + 8, &blob[blob[kOffWaves] + w * 8]);
         }
+        int32_t ua = 0;
+        for (int32_t g = 0; g < G; ++g) {
+            blob[blob[kOffWgUnits] + 2 * g] = ua;
+            blob[blob[kOffWgUnits] + 2 * g + 1] = static_cast<int32_t>(wg_units[g].size());
+            for (int32_t ui : wg_units[g]) {
+                const Unit& u = units[ui];
+                UnitDesc d{};
+                d.n_keys = u.keys;
+                d.chunk_off = coff;
+                d.n_chunks = static_cast<int32_t>(u.it->chunks.size());
+                for (int32_t id : u.it->chunks) blob[blob[kOffChunks] + coff++] = id;
+                d.head = u.head;
+                d.row_lo = u.it->row_lo + u.r0;
+                d.n_rows = u.rows;
+                d.out = u.it->out + u.r0;
+                std::copy(reinterpret_cast<const int32_t*>(&d),
+                          reinterpret_cast<const int32_t*>(&d) + 8, &blob[blob[kOffUnits] + ua * 8]);
+                ++ua;
+            }
+        }
     }
     for (int32_t p = 0; p < b; ++p) blob[blob[kOffRows] + p] = dfs_row[p];
     for (size_t m = 0; m < merge_rows.size(); ++m) blob[blob[kOffMerge] + m] = merge_rows[m];
@@ -407,6 +438,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     blob[kNWaves] = n_waves;
     blob[kNWg] = G;
     blob[kNTasks] = n_tasks;
+    blob[kNUnits] = n_units;
     blob[kNSlots] = n_slots;
     blob[kNMerge] = static_cast<int32_t>(merge_rows.size());
     blob[kTotalWords] = static_cast<int32_t>(blob.size());
@@ -430,6 +462,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     plan.n_waves = n_waves;
     plan.n_wg = G;
     plan.n_tasks = n_tasks;
+    plan.n_units = n_units;
     plan.n_slots = n_slots;
     plan.n_merge = static_cast<int32_t>(merge_rows.size());
     plan.split1_chunks = s1;

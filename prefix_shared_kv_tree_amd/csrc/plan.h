@@ -10,7 +10,9 @@
 //                              (first entry in tasks, number of tasks)
 //   tasks    [n_tasks][2]      (wave descriptor index, head), in lane order
 //   waves    [n_waves][8]      WaveDesc (head-independent)
-//   chunks   [...]             chunk ids referenced by the waves
+//   wgunits  [G][2]            per workgroup: (first entry in units, count)
+//   units    [n_units][8]      UnitDesc, in workgroup order
+//   chunks   [...]             chunk ids referenced by the waves and units
 //   rows     [b]               depth-first position -> query row of Q / O
 //   merge    [n_merge]         depth-first positions whose partials are merged
 //   mptr     [b+1]             CSR over depth-first positions ...
@@ -41,12 +43,29 @@ struct WaveDesc {
 };
 static_assert(sizeof(WaveDesc) == 32, "WaveDesc is 8 int32");
 
+// A workgroup unit: query rows [row_lo, row_lo + n_rows), 17 <= n_rows <= 64,
+// of one head against a list of full chunks.  All 4 waves of one workgroup
+// run it in lock step (two barriers per 64-key step): each loads a quarter
+// of every step into LDS and computes 16 of the rows from there.
+struct UnitDesc {
+    int32_t n_keys;      // n_chunks * C
+    int32_t chunk_off;   // first entry in the chunks section
+    int32_t n_chunks;
+    int32_t head;
+    int32_t row_lo;      // depth-first position of row 0
+    int32_t n_rows;
+    int32_t out;         // partial slot of row 0
+    int32_t pad;
+};
+static_assert(sizeof(UnitDesc) == 32, "UnitDesc is 8 int32");
+
 enum HeaderField {
     kMagic = 0, kSerial, kB, kNWaves, kNWg, kNTasks, kNSlots, kNMerge,
     kOffLists, kOffTasks, kOffWaves, kOffChunks, kOffRows, kOffMerge, kOffMptr, kOffMslots,
-    kOffSeqlen, kTotalWords, kHeaderWords = 20
+    kOffSeqlen, kTotalWords, kNUnits, kOffWgUnits, kOffUnits, kHeaderWords = 24
 };
-constexpr int32_t kPlanMagic = 0x504b5655;   // "PKVU": lane-list layout
+constexpr int32_t kPlanMagic = 0x504b5657;   // "PKVW": lane lists + workgroup units
+constexpr int32_t kRowsPerUnit = 64;         // query rows of one workgroup-unit block
 constexpr int32_t kWavesPerWg = 4;
 constexpr int32_t kRowsPerWave = 16;
 constexpr int32_t kKeysPerStep = 64;
@@ -57,9 +76,10 @@ struct PlanOpts {
     int32_t phase2_chunks = 0;
     int32_t min_share = 2;
     int32_t workgroups = 0;      // persistent workgroups; 0 = kDefaultWorkgroups
+    int32_t unit_rows = 0;       // smallest row block run as a workgroup unit; 0 = 17
     bool operator==(const PlanOpts& o) const {
         return phase1_chunks == o.phase1_chunks && phase2_chunks == o.phase2_chunks &&
-               min_share == o.min_share && workgroups == o.workgroups;
+               min_share == o.min_share && workgroups == o.workgroups && unit_rows == o.unit_rows;
     }
 };
 
@@ -73,7 +93,7 @@ struct Plan {
     PlanOpts opts;
     std::vector<int32_t> blob;
     // summary
-    int32_t phase1_items = 0, phase2_items = 0, n_waves = 0, n_wg = 0, n_tasks = 0;
+    int32_t phase1_items = 0, phase2_items = 0, n_waves = 0, n_wg = 0, n_tasks = 0, n_units = 0;
     int32_t n_slots = 0, n_merge = 0;
     int32_t split1_chunks = 0, split2_chunks = 0;   // the item sizes actually used
     int32_t shared_chunks = 0;

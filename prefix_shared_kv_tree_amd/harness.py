@@ -50,7 +50,7 @@ class DecodeSetup:
 
     def __init__(self, w, layers: Optional[int] = None, pool_slack: int = 0, device: str = "cuda",
                  phase1_chunks: int = 0, phase2_chunks: int = 0, min_share: int = 0,
-                 pool_chunks: Optional[int] = None):
+                 pool_chunks: Optional[int] = None, unit_rows: int = 0):
         import torch
         self.torch = torch
         self.w = w
@@ -85,13 +85,14 @@ class DecodeSetup:
         self.q = torch.from_numpy(np.ascontiguousarray(w.q)).to(device)
         self.out = torch.empty_like(self.q)
         self.scale = 1.0 / math.sqrt(w.d)
-        self.replan(phase1_chunks, phase2_chunks, min_share)
+        self.replan(phase1_chunks, phase2_chunks, min_share, unit_rows=unit_rows)
 
     def replan(self, phase1_chunks: int = 0, phase2_chunks: int = 0, min_share: int = 0,
-               q_order=None):
+               q_order=None, unit_rows: int = 0):
         torch = self.torch
         order = self.seq_ids if q_order is None else np.asarray(q_order, np.int32)
-        mb, wb = B.pkvt_plan(self.tree, order, phase1_chunks, phase2_chunks, min_share)
+        mb, wb = B.pkvt_plan(self.tree, order, phase1_chunks, phase2_chunks, min_share,
+                             unit_rows=unit_rows)
         self.meta = torch.empty(max(mb // 4, 1), dtype=torch.int32, device=self.device)
         self.meta_bytes = mb
         self.ws = torch.empty(max(wb // 4, 1), dtype=torch.float32, device=self.device)

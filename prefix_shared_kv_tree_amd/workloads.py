@@ -161,7 +161,7 @@ def make_config(name: str, layers: int = 1, seed: Optional[int] = None,
 
 def random_tree(seed: int, h: int = 2, d: int = 16, c: int = 4, max_b: int = 6,
                 max_len: int = 80, vocab: int = VOCAB, layers: int = 1,
-                unaligned: bool = True) -> Workload:
+                unaligned: bool = True, min_b: int = 1) -> Workload:
     """A small random prefix forest with ragged lengths.
 
     Each new sequence either starts a fresh root (probability 0.2) or picks a
@@ -174,7 +174,7 @@ def random_tree(seed: int, h: int = 2, d: int = 16, c: int = 4, max_b: int = 6,
     additionally needs equal token prefixes to carry equal K/V values.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
-    b = int(rng.integers(1, max_b + 1))
+    b = int(rng.integers(min_b, max_b + 1))
     seg_tokens: List[np.ndarray] = []
     paths: List[List[int]] = []
 
@@ -228,6 +228,51 @@ def random_tree(seed: int, h: int = 2, d: int = 16, c: int = 4, max_b: int = 6,
     it = iter(tok_list)
     return _finish(f"random{seed}", rng, h, d, c, [len(t) for t in tok_list], paths,
                    layers, token_fn=lambda L: next(it))
+
+
+def one_prefix(seed: int, b: int, prefix: int, suffix, h: int = 2, d: int = 64, c: int = 16,
+               layers: int = 1) -> Workload:
+    """b sequences that share one prefix of ``prefix`` tokens, each followed
+    by a private suffix (``suffix`` tokens, or a list of b lengths)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    suf = [int(suffix)] * b if np.isscalar(suffix) else [int(x) for x in suffix]
+    seg_lens = [prefix] + suf
+    paths = [[0, 1 + u] if suf[u] > 0 else [0] for u in range(b)]
+    return _finish(f"one_prefix{b}x{prefix}", rng, h, d, c, seg_lens, paths, layers)
+
+
+def layered_tree(seed: int, b: int, n_roots: int, h: int = 2, d: int = 64, c: int = 16,
+                 max_chunks: int = 3, layers: int = 1) -> Workload:
+    """A three-level forest with wide nodes: the b sequences are split into
+    n_roots contiguous groups that each share a root segment, every group
+    into 1..4 contiguous branches that each share a branch segment, and every
+    sequence ends in a private suffix.  Segment lengths are random: roots
+    1..max_chunks whole chunks, branches 0..max_chunks chunks plus sometimes a
+    partial chunk (whose tail then cannot be shared), suffixes 1..2c tokens."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seg_lens: List[int] = []
+    paths: List[List[int]] = []
+    bounds = np.linspace(0, b, n_roots + 1).astype(int)
+    for r in range(n_roots):
+        lo, hi = int(bounds[r]), int(bounds[r + 1])
+        if hi <= lo:
+            continue
+        seg_lens.append(c * int(rng.integers(1, max_chunks + 1)))
+        root = len(seg_lens) - 1
+        n_br = int(rng.integers(1, 5))
+        cuts = sorted(set([lo, hi] + [int(x) for x in rng.integers(lo, hi, size=n_br - 1)]))
+        for a, e in zip(cuts[:-1], cuts[1:]):
+            L = c * int(rng.integers(0, max_chunks + 1))
+            if rng.random() < 0.3:
+                L += int(rng.integers(1, c))
+            br = None
+            if L > 0:
+                seg_lens.append(L)
+                br = len(seg_lens) - 1
+            for _ in range(a, e):
+                seg_lens.append(int(rng.integers(1, 2 * c + 1)))
+                paths.append([root] + ([br] if br is not None else []) + [len(seg_lens) - 1])
+    return _finish(f"layered{b}", rng, h, d, c, seg_lens, paths, layers)
 
 
 def unshare(w: Workload, token_offset: int = 1 << 20) -> Workload:

@@ -8,8 +8,9 @@ import numpy as np
 
 (H_MAGIC, H_SERIAL, H_B, H_NWAVES, H_NWG, H_NTASKS, H_NSLOTS, H_NMERGE, H_OFF_LISTS,
  H_OFF_TASKS, H_OFF_WAVES, H_OFF_CHUNKS, H_OFF_ROWS, H_OFF_MERGE, H_OFF_MPTR, H_OFF_MSLOTS,
- H_OFF_SEQLEN, H_TOTAL) = range(18)
-MAGIC = 0x504B5655
+ H_OFF_SEQLEN, H_TOTAL, H_NUNITS, H_OFF_WGUNITS, H_OFF_UNITS) = range(21)
+MAGIC = 0x504B5657
+ROWS_PER_UNIT = 64
 
 
 def parse(blob: np.ndarray) -> dict:
@@ -18,8 +19,13 @@ def parse(blob: np.ndarray) -> dict:
     waves = blob[blob[H_OFF_WAVES]:blob[H_OFF_WAVES] + nw * 8].reshape(nw, 8)
     chunks_base = int(blob[H_OFF_CHUNKS])
     mptr = blob[blob[H_OFF_MPTR]:blob[H_OFF_MPTR] + b + 1]
+    nu = int(blob[H_NUNITS])
+    units = blob[blob[H_OFF_UNITS]:blob[H_OFF_UNITS] + nu * 8].reshape(nu, 8)
     return dict(
         magic=int(blob[H_MAGIC]), b=b, n_slots=int(blob[H_NSLOTS]), n_wg=ng,
+        wg_units=blob[blob[H_OFF_WGUNITS]:blob[H_OFF_WGUNITS] + ng * 2].reshape(ng, 2),
+        units=units,
+        unit_chunks=[blob[chunks_base + u[1]:chunks_base + u[1] + u[2]] for u in units],
         lists=blob[blob[H_OFF_LISTS]:blob[H_OFF_LISTS] + ng * 4 * 2].reshape(ng * 4, 2),
         tasks=blob[blob[H_OFF_TASKS]:blob[H_OFF_TASKS] + nt * 2].reshape(nt, 2),
         waves=waves,
@@ -34,7 +40,7 @@ def parse(blob: np.ndarray) -> dict:
 
 
 def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: int = 2,
-               max_rows: int = 16, heads: int = 1):
+               max_rows: int = 16, heads: int = 1, unit_rows: int = 17):
     """paths / lens: seq id -> chunk path / token count (from the tree).
     Raises AssertionError on any violation."""
     assert plan["magic"] == MAGIC
@@ -94,6 +100,35 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
             for r in range(n_rows):
                 assert out + r not in slot_rows, "slot written twice"
                 slot_rows[out + r] = row_lo + r
+    # workgroup units: (row block, chunks) x every head exactly once; the row
+    # blocks are the 64-row cuts of a phase-1 item with more than 16 rows
+    unit_heads = defaultdict(list)
+    wgu = plan["wg_units"]
+    at = 0
+    for g, (first, cnt) in enumerate(wgu):
+        assert first == at and cnt >= 0
+        at += cnt
+    assert at == len(plan["units"])
+    for u, ch in zip(plan["units"], plan["unit_chunks"]):
+        n_keys, chunk_off, n_chunks, head, row_lo, n_rows, out, _ = [int(v) for v in u]
+        assert n_chunks == len(ch) >= 1 and n_keys == n_chunks * c
+        assert max(max_rows + 1, unit_rows) <= n_rows <= ROWS_PER_UNIT
+        assert 0 <= head < heads and out >= 0
+        unit_heads[(row_lo, n_rows, out, tuple(int(x) for x in ch))].append(head)
+    for (row_lo, n_rows, out, ch), hs in unit_heads.items():
+        assert sorted(hs) == list(range(heads)), "unit heads missing or repeated"
+        for x in ch:
+            assert len(cover[x]) >= min_share, "a unit reads an unshared chunk"
+            for p in range(row_lo, row_lo + n_rows):
+                assert x in [int(y) for y in paths[seq_at[p]]], "unit reads a chunk not on the row's path"
+                # full chunks only
+                k = [int(y) for y in paths[seq_at[p]]].index(x)
+                assert (k + 1) * c <= lens[seq_at[p]]
+                seen[(p, x)] += 1
+                chunk_rows[x].add(p)
+        for r in range(n_rows):
+            assert out + r not in slot_rows, "slot written twice"
+            slot_rows[out + r] = row_lo + r
     for p in range(b):
         for x in paths[seq_at[p]]:
             assert seen.pop((p, int(x)), 0) == 1, f"chunk {x} of position {p} not visited once"
@@ -125,12 +160,7 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
         at += cnt
     assert at == len(plan["tasks"])
     assert set(lane_of) == {(w, h) for w in range(len(plan["waves"])) for h in range(heads)}
-    # the row groups of one phase-1 item (same chunks, same head) share a workgroup
-    items = defaultdict(list)
-    for wi, ch in enumerate(plan["wave_chunks"]):
+    # single-wave phase-1 tasks are the <= 16-row remainders of 64-row cuts
+    for wi, w in enumerate(plan["waves"]):
         if phase1[wi]:
-            items[tuple(int(x) for x in ch)].append(wi)
-    for ch, ws in items.items():
-        for h in range(heads):
-            wgs = {lane_of[(w, h)] // 4 for w in ws}
-            assert len(wgs) <= (len(ws) + 3) // 4, "row groups of a phase-1 item split up"
+            assert int(w[5]) <= max_rows

@@ -302,7 +302,7 @@ def _plan_and_check(box, order, **kw):
     paths = {int(i): list(B.pkvt_tree_chunk_path(box.t, int(i))) for i in live}
     lens = {int(i): B.pkvt_tree_seq_len(box.t, int(i)) for i in live}
     planview.check_plan(plan, order, paths, lens, box.c, min_share=kw.get("min_share") or 2,
-                        heads=box.h)
+                        heads=box.h, unit_rows=kw.get("unit_rows") or 17)
     assert wb == plan["n_slots"] * box.h * (box.d + 2) * 4
     return plan
 
@@ -320,6 +320,32 @@ def test_plan_invariants_random(seed):
         p2 = int(rng.integers(0, 4))
         ms = int(rng.choice([0, 2, 3, 100]))
         _plan_and_check(box, order, phase1_chunks=p1, phase2_chunks=p2, min_share=ms)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_plan_invariants_wide(seed):
+    """Many sequences per shared node: phase-1 row blocks of 17..64 rows
+    become workgroup units, longer ones are cut at 64 rows."""
+    rng = np.random.default_rng(100 + seed)
+    h = int(rng.integers(1, 4))
+    w = W.layered_tree(100 + seed, int(rng.integers(20, 161)), int(rng.integers(1, 4)), h=h, c=4)
+    box = TreeBox(h=h, c=4, n=8192)
+    ids, _ = B.pkvt_tree_build(box.t, w.all_seq_tokens())
+    cover = {}
+    for i in ids:
+        for x in B.pkvt_tree_chunk_path(box.t, int(i)):
+            cover[int(x)] = cover.get(int(x), 0) + 1
+    for p1, p2, ms in [(0, 0, 0), (1, 1, 0), (3, 2, 5), (0, 0, 17)]:
+        plan = _plan_and_check(box, [int(x) for x in rng.permutation(ids)],
+                               phase1_chunks=p1, phase2_chunks=p2, min_share=ms)
+        wide = any(n >= max(17, ms) for n in cover.values())
+        assert (len(plan["units"]) > 0) == wide
+    order = [int(x) for x in ids]
+    assert len(_plan_and_check(box, order, unit_rows=65)["units"]) == 0
+    plan = _plan_and_check(box, order, unit_rows=40)
+    assert all(int(u[5]) >= 40 for u in plan["units"])
+    with pytest.raises(B.PkvtError):
+        B.pkvt_plan(box.t, order, unit_rows=16)
 
 
 def test_plan_invariants_after_dynamic_ops():

@@ -79,6 +79,47 @@ def test_random_trees(seed):
         ds.close()
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_wide_trees(seed):
+    """Many sequences per shared node, so phase-1 row blocks of 17..64 rows
+    run as workgroup units (LDS-shared loads) and longer blocks are cut."""
+    _torch()
+    rng = np.random.default_rng(200 + seed)
+    d = int(rng.choice([64, 128]))
+    c = int(rng.choice([16, 32, 64, 128]))
+    h = int(rng.integers(1, 4))
+    b = int(rng.integers(20, 141))
+    n_roots = int(rng.integers(1, 4))
+    print(f"\n[case] wide tree seed={seed} b={b} roots={n_roots} h={h} d={d} c={c}", flush=True)
+    w = W.layered_tree(200 + seed, b, n_roots, h=h, d=d, c=c)
+    ref = A.attention_batch(w)
+    for p1, p2, ms in [(0, 0, 0), (1, 1, 0), (3, 2, 18)]:
+        ds = _setup(w, phase1_chunks=p1, phase2_chunks=p2, min_share=ms)
+        err = _err(_run(ds), ref)
+        print(f"[case]   p1={p1} p2={p2} min_share={ms} err={err:.3e} info={ds.info}", flush=True)
+        assert err <= TOL
+        ds.close()
+
+
+@pytest.mark.parametrize("rows", [17, 32, 33, 48, 64, 65, 81, 130])
+@pytest.mark.parametrize("d,c,n_chunks", [(64, 16, 5), (128, 32, 3), (128, 64, 2)])
+def test_unit_row_counts(rows, d, c, n_chunks):
+    """One shared prefix read by `rows` sequences: unit row blocks of every
+    size class, and prefixes whose length is not a multiple of 64 keys (the
+    last step of a unit then has whole tiles past the end)."""
+    _torch()
+    print(f"\n[case] unit rows={rows} d={d} c={c} prefix_chunks={n_chunks}", flush=True)
+    suffix = [(u * 7) % (2 * c) for u in range(rows)]
+    w = W.one_prefix(300 + rows, rows, n_chunks * c, suffix, h=2, d=d, c=c)
+    ref = A.attention_batch(w)
+    ds = _setup(w, phase1_chunks=n_chunks)
+    assert ds.info["wg_units"] > 0
+    err = _err(_run(ds), ref)
+    print(f"[case]   err={err:.3e} info={ds.info}", flush=True)
+    assert err <= TOL
+    ds.close()
+
+
 def test_single_key_bit_exact():
     _torch()
     print("\n[case] single-key sequences", flush=True)
