@@ -133,6 +133,125 @@ def cpu_baseline(w, unique_bytes, budget_s):
     }
 
 
+KERNEL_SRC = os.path.join(ROOT, "prefix_shared_kv_tree_amd", "csrc", "attn.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+ATTN_KERNEL = "attn_kernel"
+
+
+def kernel_source_sha256():
+    """Identifies the attention kernel the counters were taken on."""
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def algorithmic_bytes(w, info):
+    """Bytes one launch must move at least: the batch's distinct stored KV
+    (every shared chunk once, valid tokens only), Q, and the attention
+    kernel's outputs (partials for merged rows, O for rows finalised in
+    place).  Returns (unique KV bytes, attention-kernel bytes)."""
+    H, D = w.h, w.d
+    unique = info["unique_tokens"] * H * D * 2 * 2
+    q_bytes = w.b * H * D * 2
+    direct_rows = w.b - info["merge_rows"]
+    out_bytes = info["slots"] * H * (D + 2) * 4 + direct_rows * H * D * 2
+    return unique, unique + q_bytes + out_bytes
+
+
+def profile_traffic(config):
+    """HBM bytes per attention launch from the committed counter summary of
+    this workload, or None when there is none or the kernel source changed
+    since the counters were taken."""
+    path = os.path.join(PROFILES, f"{ATTN_KERNEL}_{config}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    start = text.find("```json pmc-summary")
+    if start < 0:
+        return None
+    body = text[text.index("\n", start) + 1:text.index("```", start + 3)]
+    rec = json.loads(body)
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return rec
+
+
+def _counter_means(csv_path, kernel_substr):
+    import csv as _csv
+    from collections import defaultdict
+    acc = defaultdict(list)
+    for r in _csv.DictReader(open(csv_path)):
+        if kernel_substr in r["Kernel_Name"]:
+            acc[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def summarize_pmc(args):
+    """Turn rocprofv3 counter CSVs of one bench run per counter set into the
+    committed summary (markdown with a machine-readable JSON block)."""
+    from prefix_shared_kv_tree_amd import binding as B
+    from prefix_shared_kv_tree_amd import workloads as W
+    w = W.make_config(args.config, with_kv=False)
+    t = B.pkvt_tree_create(w.h, w.d, w.c, 1 << 20)
+    ids, _ = B.pkvt_tree_build(t, w.all_seq_tokens())
+    B.pkvt_plan(t, ids)
+    info = B.pkvt_plan_info_get(t)
+    B.pkvt_tree_destroy(t)
+    unique, attn_bytes = algorithmic_bytes(w, info)
+    fetch, n_fetch = _counter_means(args.fetch_csv, ATTN_KERNEL)
+    write, n_write = _counter_means(args.write_csv, ATTN_KERNEL)
+    copy_bytes = args.copy_mib * 2 ** 20
+    cf, _ = _counter_means(args.fetch_csv, "neg_kernel")
+    cw, _ = _counter_means(args.write_csv, "neg_kernel")
+    # the copy runs three times after a fill: take the copies' own rows
+    f_fetch = copy_bytes / (cf["FETCH_SIZE"] * 1024)
+    f_write = copy_bytes / (cw["WRITE_SIZE"] * 1024)
+    fetch_b = fetch["FETCH_SIZE"] * 1024 * f_fetch
+    write_b = write["WRITE_SIZE"] * 1024 * f_write
+    rec = {
+        "workload": args.config,
+        "kernel": f"{ATTN_KERNEL}<{w.d},{w.c}>",
+        "kernel_source_sha256": kernel_source_sha256(),
+        "dispatches": {"fetch": n_fetch.get("FETCH_SIZE", 0), "write": n_write.get("WRITE_SIZE", 0)},
+        "fetch_kib_raw": round(fetch["FETCH_SIZE"], 1),
+        "write_kib_raw": round(write["WRITE_SIZE"], 1),
+        "copy_fetch_factor": round(f_fetch, 4),
+        "copy_write_factor": round(f_write, 4),
+        "fetch_bytes": int(fetch_b),
+        "write_bytes": int(write_b),
+        "traffic_bytes": int(fetch_b + write_b),
+        "algorithmic_bytes": int(attn_bytes),
+        "traffic_over_algorithmic": round((fetch_b + write_b) / attn_bytes, 4),
+    }
+    if args.mfma_csv:
+        m, _ = _counter_means(args.mfma_csv, ATTN_KERNEL)
+        rec["mfma_counters"] = {k: round(v, 1) for k, v in m.items()}
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in m:
+            rec["mfma_f16_flops_issued"] = int(m["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512)
+    out = [f"# {rec['kernel']} -- HBM traffic per launch, workload {args.config}", "",
+           f"Workload: {W.CONFIG_DESCRIPTIONS[args.config]}.", "",
+           "Commands (GPU box, repository root as $R):", "", "```"]
+    out += [c for c in args.command]
+    out += ["```", "",
+            "FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch and scaled by what",
+            f"the same counters read for a plain elementwise copy of {args.copy_mib} MiB",
+            "(torch.neg: that many bytes read and written) in the same run:",
+            f"fetch factor {rec['copy_fetch_factor']}, write factor {rec['copy_write_factor']}.", "",
+            "| quantity | value |", "|---|---|",
+            f"| FETCH_SIZE (KiB, mean of {rec['dispatches']['fetch']} dispatches) | {rec['fetch_kib_raw']} |",
+            f"| WRITE_SIZE (KiB, mean of {rec['dispatches']['write']} dispatches) | {rec['write_kib_raw']} |",
+            f"| HBM bytes read per launch | {rec['fetch_bytes']:,} |",
+            f"| HBM bytes written per launch | {rec['write_bytes']:,} |",
+            f"| traffic per launch | {rec['traffic_bytes']:,} |",
+            f"| algorithmic bytes per launch | {rec['algorithmic_bytes']:,} |",
+            f"| traffic / algorithmic | {rec['traffic_over_algorithmic']} |"]
+    if "mfma_counters" in rec:
+        out += ["", "MFMA counters (mean per dispatch): " +
+                ", ".join(f"{k} = {v}" for k, v in rec["mfma_counters"].items())]
+    out += ["", "```json pmc-summary", json.dumps(rec, indent=1), "```", ""]
+    print("\n".join(out))
+
+
 def copy_probe(torch, mib):
     """A plain copy of known size (torch's elementwise kernel: `mib` MiB read,
     `mib` MiB written), launched three times.  Under a counter-collection run
@@ -161,7 +280,17 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the run, launch a plain elementwise copy of this many MiB "
                          "(reads and writes that many bytes) to calibrate HBM byte counters")
+    ap.add_argument("--summarize-pmc", action="store_true",
+                    help="(no GPU) print the counter summary of --config from rocprofv3 CSVs")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--mfma-csv")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the decode attention of one "
               "GPU's share and has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
@@ -227,12 +356,9 @@ def main():
 
     # algorithmic bytes of one attention-kernel launch
     H, D = w.h, w.d
-    q_bytes = w.b * H * D * 2
-    n_slots = info["slots"]
-    direct_rows = w.b - info["merge_rows"]
-    out_bytes = n_slots * H * (D + 2) * 4 + direct_rows * H * D * 2
-    attn_bytes = unique_bytes + q_bytes + out_bytes
+    _, attn_bytes = algorithmic_bytes(w, info)
     achieved = attn_bytes / (attn_avg_us * 1e-6) / 1e9
+    traffic = profile_traffic(args.config)
 
     res = {
         "metric": METRIC,
@@ -277,8 +403,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
-            "kernel": "attn_kernel<128,64>",
+            "traffic": traffic["traffic_bytes"] if traffic else None,
+            "kernel": f"attn_kernel<{D},{w.c}>",
             "algorithmic_bytes_per_launch": int(attn_bytes),
         },
         "workload_gen_s": round(gen_s, 1),

@@ -86,6 +86,22 @@ __device__ __forceinline__ int tile_start(int step, int tt, int n_valid) {
     return key < last ? key : last;
 }
 
+// A task's chunk ids are held one per lane in a VGPR (the planner cuts every
+// task to at most 64 chunks), loaded once when the task is fetched.  The id
+// of the chunk holding a 16-key tile is then a readlane -- no memory access
+// and no wait inside the streaming loop.  (A scalar load per step would
+// force a wait for every scalar load in flight, as they complete out of
+// order.)  The tile's chunk is that of its first key, clamped to the chunk
+// of the last valid key, i.e. the chunk of tile_start(step, tt, n_valid).
+__device__ __forceinline__ int lane_ids(cint* chunks, int n_chunks, int lane) {
+    return lane < n_chunks ? chunks[lane] : 0;
+}
+
+template <int C>
+__device__ __forceinline__ int tile_id(int ids, int step, int tt, int n_valid) {
+    return __builtin_amdgcn_readlane(ids, min((step * kStep + 16 * tt) / C, (n_valid - 1) / C));
+}
+
 // S^T = K Q^T for the 64 keys of a step: tile tt = keys 16tt .. 16tt+15.
 template <int KS>
 __device__ __forceinline__ void qk(f4 (&s)[4], const h8 (&kr)[4][KS], const h8 (&qb)[KS]) {
@@ -233,7 +249,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
     const int grp = lane >> 4;
     const int H = a.H;
     const int n_keys = u[0];
-    cint* chunks = meta(a.chunks) + u[1];
+    const int ids = lane_ids(meta(a.chunks) + u[1], u[2], lane);
     const int head = u[3];
     const int row_lo = u[4];
     const int n_rows = u[5];
@@ -249,7 +265,12 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
     h8 stg[NL];
     // piece j of the image: K pieces [0, 8D) as (tile, d/8 piece, key), then
     // V pieces [8D, 16D) as (tile, byte offset / 16 in the tile's V block)
+    // A wave's pieces cover two tiles, ta and ta + 1 (of K for waves 0-1, of
+    // V for waves 2-3); loads i < NL/2 fall in tile ta.
+    const int ta = 2 * (role & 1);
     auto stage = [&](int step) {
+        const int id_a = tile_id<C>(ids, step, ta, n_keys);
+        const int id_b = tile_id<C>(ids, step, ta + 1, n_keys);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int j0 = role * kPer + i * 64;                   // wave-uniform
@@ -257,7 +278,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
             const int jj = is_k ? j0 : j0 - 8 * D;
             const int ts = tile_start(step, jj / (2 * D), n_keys);
             const int rem = jj % (2 * D) + lane;
-            const size_t cbytes = static_cast<size_t>(chunks[ts / C]) * cstride;
+            const size_t cbytes = static_cast<size_t>(i < NL / 2 ? id_a : id_b) * cstride;
             const char* kp = kbase + cbytes + (static_cast<size_t>(rem >> 4) * C + ts % C + (rem & 15)) * 16;
             const char* vp = vbase + cbytes + static_cast<size_t>((ts % C) / 4) * (D * 8) + rem * 16;
             stg[i] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(is_k ? kp : vp));
@@ -332,7 +353,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 
 // Wave-uniform description of one single-wave task.
 struct Task {
-    cint* chunks;            // the task's chunk ids
+    int ids;                 // the task's chunk ids, one per lane (lane_ids)
     int n_valid;             // keys to attend over
     int n_steps;             // ceil(n_valid / 64)
     int row_lo;              // depth-first position of query row 0
@@ -351,7 +372,7 @@ __device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
     const int n_chunks = wd[1];
     const int key_base = wd[2];
     const int len_row = wd[3];
-    t.chunks = meta(a.chunks) + wd[0];
+    t.ids = lane_ids(meta(a.chunks) + wd[0], n_chunks, static_cast<int>(threadIdx.x & 63));
     t.row_lo = wd[4];
     t.n_rows = wd[5];
     t.out = wd[6];
@@ -416,7 +437,7 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const int key = tile_start(step, tt, t.n_valid);
-            const char* base = slice_of(kpool, t.chunks[key / C], t.head) + (key % C) * 16;
+            const char* base = slice_of(kpool, tile_id<C>(t.ids, step, tt, t.n_valid), t.head) + (key % C) * 16;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 kr[tt][ks] = __builtin_nontemporal_load(
@@ -427,7 +448,8 @@ void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const int key = tile_start(step, tt, t.n_valid);
-            const char* base = slice_of(vpool, t.chunks[key / C], t.head) + ((key % C) / 4) * (D * 8);
+            const char* base = slice_of(vpool, tile_id<C>(t.ids, step, tt, t.n_valid), t.head) +
+                               ((key % C) / 4) * (D * 8);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 vr[dt][tt >> 1][tt & 1] =

@@ -32,8 +32,14 @@ namespace pkvt {
 
 namespace {
 
-// task cost in quarter steps: 4 per 64-key step plus a start-up share
-int64_t task_cost(int32_t keys) { return 4 * ((keys + kKeysPerStep - 1) / kKeysPerStep) + 1; }
+int64_t steps_of(int64_t keys) { return (keys + kKeysPerStep - 1) / kKeysPerStep; }
+
+// Cost in quarter steps of a single-wave task: 4 per 64-key step plus a
+// start-up share.  A workgroup-unit step costs each of the unit's 4 waves
+// kUnitStepCost quarter steps: its waves issue a quarter of the loads each
+// (measured under load: a unit step takes ~0.4 of a single-wave step).
+int64_t task_cost(int64_t keys) { return 4 * steps_of(keys) + 1; }
+int64_t unit_cost(int64_t keys) { return kUnitStepCost * steps_of(keys) + 1; }
 
 int32_t steps_to_chunks(int64_t steps, int32_t C) {
     const int64_t ch = steps * kKeysPerStep / C;
@@ -182,28 +188,38 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     }
 
     // ---- item size ----------------------------------------------------------------
-    // T = the mean per-wave load in 64-key steps with nothing cut.  Phase-1
+    // T = the mean per-wave load in 64-key steps with nothing cut (a unit
+    // step counted at its cost relative to a single-wave step).  Phase-1
     // items are cut at T.  Phase-2 items are cut at T when nothing is shared
     // (all tasks then tend to be alike and need no merge); with a shared
     // prefix the phase-1 units make the per-wave loads uneven and finer
     // phase-2 pieces (4 steps, or T/4 if larger) fill the gaps better.
     int32_t s1 = opts.phase1_chunks, s2 = opts.phase2_chunks;
     if (s1 == 0 || s2 == 0) {
-        auto steps_of = [](int64_t keys) { return (keys + kKeysPerStep - 1) / kKeysPerStep; };
-        int64_t steps = 0;
+        int64_t quarters = 0;
         for (size_t s = 0; s < segs.size(); ++s) {
-            const int64_t waves = (seg_range[s].j - seg_range[s].i + kRowsPerWave - 1) / kRowsPerWave;
-            steps += waves * steps_of(static_cast<int64_t>(segs[s].size()) * t.C);
+            const int64_t st = steps_of(static_cast<int64_t>(segs[s].size()) * t.C);
+            const int32_t rows = seg_range[s].j - seg_range[s].i;
+            for (int32_t r0 = 0; r0 < rows; r0 += kRowsPerUnit) {
+                const int32_t rb = std::min(kRowsPerUnit, rows - r0);
+                if (rb >= opts.unit_rows)
+                    quarters += kWavesPerWg * kUnitStepCost * st;
+                else
+                    quarters += 4 * st * ((rb + kRowsPerWave - 1) / kRowsPerWave);
+            }
         }
         for (int32_t p = 0; p < b; ++p)
-            steps += steps_of(seqs[dfs_row[p]]->len - static_cast<int64_t>(k0[p]) * t.C);
-        const int64_t mean = std::max<int64_t>(1, (steps * t.H + lanes - 1) / lanes);
+            quarters += 4 * steps_of(seqs[dfs_row[p]]->len - static_cast<int64_t>(k0[p]) * t.C);
+        const int64_t mean = std::max<int64_t>(1, (quarters * t.H + 4 * lanes - 1) / (4 * lanes));
         if (s1 == 0) s1 = steps_to_chunks(mean, t.C);
         if (s2 == 0) {
             const int64_t fine = std::min<int64_t>(mean, std::max<int64_t>(4, (mean + 3) / 4));
             s2 = steps_to_chunks(segs.empty() ? mean : fine, t.C);
         }
     }
+    // the kernel holds a task's chunk ids one per lane of a 64-lane wave
+    s1 = std::min(s1, kMaxItemChunks);
+    s2 = std::min(s2, kMaxItemChunks);
 
     // ---- 3. items ------------------------------------------------------------------
     std::vector<Item> items1;
@@ -286,7 +302,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         w.out = it.out < 0 ? -1 : it.out + row_off;
         waves.push_back(w);
         wave_chunks.push_back(&it.chunks);
-        wave_cost.push_back(task_cost(static_cast<int32_t>(item_keys(it))));
+        wave_cost.push_back(task_cost(item_keys(it)));
         return static_cast<int32_t>(waves.size()) - 1;
     };
     // Phase-1 rows are cut into blocks of kRowsPerUnit.  A block of at least
@@ -305,7 +321,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
                 for (int32_t r = r0; r < r0 + rb; r += kRowsPerWave) singles.push_back(add_wave(it, r));
                 continue;
             }
-            for (int32_t h = 0; h < t.H; ++h) units.push_back({&it, r0, rb, h, keys, task_cost(keys)});
+            for (int32_t h = 0; h < t.H; ++h) units.push_back({&it, r0, rb, h, keys, unit_cost(keys)});
         }
     }
     for (const Item& it : items2) singles.push_back(add_wave(it, 0));
@@ -314,39 +330,61 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     std::vector<std::vector<std::pair<int32_t, int32_t>>> lists(lanes);   // (wave, head)
     std::vector<int64_t> load(lanes, 0);
     {
+        // Workgroups g and g + G/2 share a compute unit and the hardware
+        // favours the older one (g < G/2): while both run, the younger one's
+        // waves progress at about kYoungSpeedPct % of the older one's speed.
+        // Work goes, longest first, to whichever wave (or workgroup, for
+        // units) would finish it first at its speed.
         using QE = std::pair<int64_t, int32_t>;
-        // workgroup units, longest first -> the workgroup whose busiest wave is least loaded
+        using MinHeap = std::priority_queue<QE, std::vector<QE>, std::greater<QE>>;
+        auto young = [&](int32_t g) { return G > 1 && g >= G / 2; };
+        // pick from two heaps (older, younger) the entry whose load + cost
+        // ends first at its class's speed
+        auto pick = [&](MinHeap* hq, int64_t cost) {
+            int cls = -1;
+            int64_t best = 0;
+            for (int c = 0; c < 2; ++c) {
+                if (hq[c].empty()) continue;
+                const int64_t fin = (hq[c].top().first + cost) * 100 / (c ? kYoungSpeedPct : 100);
+                if (cls < 0 || fin < best) {
+                    cls = c;
+                    best = fin;
+                }
+            }
+            const QE e = hq[cls].top();
+            hq[cls].pop();
+            return std::make_pair(cls, e);
+        };
+        // workgroup units, longest first
         std::vector<int32_t> order(units.size());
         for (size_t i = 0; i < order.size(); ++i) order[i] = static_cast<int32_t>(i);
         std::stable_sort(order.begin(), order.end(),
                          [&](int32_t a, int32_t c) { return units[a].cost > units[c].cost; });
-        std::priority_queue<QE, std::vector<QE>, std::greater<QE>> wgq;
-        for (int32_t g = 0; g < G; ++g) wgq.push({0, g});
+        MinHeap wgq[2];
+        for (int32_t g = 0; g < G; ++g) wgq[young(g)].push({0, g});
         for (int32_t ui : order) {
-            const auto top = wgq.top();
-            wgq.pop();
-            const int32_t g = top.second;
-            int64_t start = 0;
-            for (int32_t k = 0; k < kWavesPerWg; ++k) start = std::max(start, load[g * kWavesPerWg + k]);
-            for (int32_t k = 0; k < kWavesPerWg; ++k) load[g * kWavesPerWg + k] = start + units[ui].cost;
+            const auto pk = pick(wgq, units[ui].cost);
+            const int32_t g = pk.second.second;
+            const int64_t end = pk.second.first + units[ui].cost;
+            for (int32_t k = 0; k < kWavesPerWg; ++k) load[g * kWavesPerWg + k] = end;
             wg_units[g].push_back(ui);
-            wgq.push({start + units[ui].cost, g});
+            wgq[pk.first].push({end, g});
         }
-        // single-wave tasks x heads, longest first -> the least loaded wave
+        // single-wave tasks x heads, longest first
         std::vector<std::pair<int64_t, int32_t>> st;         // (cost, single*H + head)
         for (size_t i = 0; i < singles.size(); ++i)
             for (int32_t h = 0; h < t.H; ++h)
                 st.push_back({wave_cost[singles[i]], static_cast<int32_t>(i) * t.H + h});
         std::stable_sort(st.begin(), st.end(),
                          [](const auto& a, const auto& c) { return a.first > c.first; });
-        std::priority_queue<QE, std::vector<QE>, std::greater<QE>> lq;
-        for (int32_t l = 0; l < lanes; ++l) lq.push({load[l], l});
+        MinHeap lq[2];
+        for (int32_t l = 0; l < lanes; ++l) lq[young(l / kWavesPerWg)].push({load[l], l});
         for (const auto& e : st) {
-            const auto top = lq.top();
-            lq.pop();
-            lists[top.second].push_back({singles[e.second / t.H], e.second % t.H});
-            load[top.second] = top.first + e.first;
-            lq.push({load[top.second], top.second});
+            const auto pk = pick(lq, e.first);
+            const int32_t l = pk.second.second;
+            lists[l].push_back({singles[e.second / t.H], e.second % t.H});
+            load[l] = pk.second.first + e.first;
+            lq[pk.first].push({load[l], l});
         }
     }
 

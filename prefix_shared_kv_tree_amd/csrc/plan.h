@@ -70,6 +70,9 @@ constexpr int32_t kWavesPerWg = 4;
 constexpr int32_t kRowsPerWave = 16;
 constexpr int32_t kKeysPerStep = 64;
 constexpr int32_t kDefaultWorkgroups = 512;  // 256 CUs x 2 resident workgroups
+constexpr int32_t kMaxItemChunks = 64;       // chunks per work item (one per wave lane)
+constexpr int32_t kUnitStepCost = 2;         // quarter steps per wave of a unit step (4 = a task step)
+constexpr int32_t kYoungSpeedPct = 60;       // speed of a compute unit's younger workgroup, % of the older
 
 struct PlanOpts {
     int32_t phase1_chunks = 0;   // 0 = derived from the balanced per-lane load
