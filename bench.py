@@ -28,6 +28,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0     # MI355X dense fp16 matrix peak
+SIMDS = 256 * 4                   # MI355X: 256 compute units x 4 SIMDs
 METRIC = "decode attn µs/layer + effective KV GB/s (% HBM peak), shared prefix 1K–4K"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -83,7 +85,8 @@ def time_region(ds, B, ev, stream, steps, warmup, per_kernel):
     torch.cuda.synchronize()
     n_ev = steps + 1
     ends = ev.create(n_ev)
-    mids = ev.create(steps) if per_kernel else [0] * steps
+    mids = ev.create(steps) if per_kernel else [0] * steps       # after each attention kernel
+    starts = ev.create(steps) if per_kernel else [0] * steps     # before each attention kernel
     ws = ds.ws.data_ptr() if ds.ws_bytes else 0
     t0 = time.perf_counter()
     ev.record(ends[0], stream)
@@ -91,7 +94,8 @@ def time_region(ds, B, ev, stream, steps, warmup, per_kernel):
         layer = i % L
         B.pkvt_attn_decode_ex(ds.tree, ds.meta.data_ptr(), ds.q.data_ptr(),
                               ds.k_pools[layer].data_ptr(), ds.v_pools[layer].data_ptr(),
-                              ds.out.data_ptr(), ws, ds.ws_bytes, ds.scale, stream, mids[i])
+                              ds.out.data_ptr(), ws, ds.ws_bytes, ds.scale, stream, starts[i],
+                              mids[i])
         if per_kernel:
             ev.record(ends[i + 1], stream)
     if not per_kernel:
@@ -103,10 +107,11 @@ def time_region(ds, B, ev, stream, steps, warmup, per_kernel):
     if per_kernel:
         for i in range(steps):
             step_ms.append(ev.ms(ends[i], ends[i + 1]))
-            attn_ms.append(ev.ms(ends[i], mids[i]))
+            attn_ms.append(ev.ms(starts[i], mids[i]))
     ev.destroy(ends)
     if per_kernel:
         ev.destroy(mids)
+        ev.destroy(starts)
     return total, wall, step_ms, attn_ms
 
 
@@ -223,11 +228,28 @@ def summarize_pmc(args):
         "algorithmic_bytes": int(attn_bytes),
         "traffic_over_algorithmic": round((fetch_b + write_b) / attn_bytes, 4),
     }
+    kernel_ns = None
+    if args.trace_csv:
+        import csv as _csv
+        for r in _csv.DictReader(open(args.trace_csv)):
+            if ATTN_KERNEL in r["Name"]:
+                kernel_ns = float(r["AverageNs"])
+                rec["kernel_avg_us_trace"] = round(kernel_ns / 1e3, 2)
+                rec["traffic_gbps_at_trace_avg"] = round(rec["traffic_bytes"] / kernel_ns, 1)
     if args.mfma_csv:
         m, _ = _counter_means(args.mfma_csv, ATTN_KERNEL)
         rec["mfma_counters"] = {k: round(v, 1) for k, v in m.items()}
         if "SQ_INSTS_VALU_MFMA_MOPS_F16" in m:
-            rec["mfma_f16_flops_issued"] = int(m["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512)
+            # the counter counts f16 MFMA math operations divided by 512
+            flops = m["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512
+            rec["mfma_f16_flops_issued"] = int(flops)
+            if kernel_ns:
+                rec["mfma_tflops"] = round(flops / kernel_ns / 1e3, 2)
+                rec["mfma_frac_of_dense_f16_peak"] = round(flops / kernel_ns / 1e3 / MFMA_F16_PEAK_TFLOPS, 4)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "GRBM_GUI_ACTIVE" in m:
+            # busy cycles summed over all SIMDs; GRBM_GUI_ACTIVE summed over the 8 XCDs
+            cycles = m["GRBM_GUI_ACTIVE"] / 8
+            rec["mfma_busy_frac"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS), 4)
     out = [f"# {rec['kernel']} -- HBM traffic per launch, workload {args.config}", "",
            f"Workload: {W.CONFIG_DESCRIPTIONS[args.config]}.", "",
            "Commands (GPU box, repository root as $R):", "", "```"]
@@ -245,11 +267,56 @@ def summarize_pmc(args):
             f"| traffic per launch | {rec['traffic_bytes']:,} |",
             f"| algorithmic bytes per launch | {rec['algorithmic_bytes']:,} |",
             f"| traffic / algorithmic | {rec['traffic_over_algorithmic']} |"]
+    if kernel_ns:
+        out += [f"| attention kernel average, kernel trace (us) | {rec['kernel_avg_us_trace']} |",
+                f"| traffic / average duration (GB/s) | {rec['traffic_gbps_at_trace_avg']} |"]
     if "mfma_counters" in rec:
         out += ["", "MFMA counters (mean per dispatch): " +
                 ", ".join(f"{k} = {v}" for k, v in rec["mfma_counters"].items())]
+        if "mfma_tflops" in rec:
+            out += [f"MFMA f16 FLOPs issued per launch: {rec['mfma_f16_flops_issued']:,} "
+                    f"(SQ_INSTS_VALU_MFMA_MOPS_F16 x 512) = {rec['mfma_tflops']} TFLOP/s over the "
+                    f"traced average duration = {rec['mfma_frac_of_dense_f16_peak'] * 100:.2f} % of the "
+                    f"{MFMA_F16_PEAK_TFLOPS:.0f} TFLOP/s dense f16 peak."]
+        if "mfma_busy_frac" in rec:
+            out += [f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x {SIMDS} SIMDs) = "
+                    f"{rec['mfma_busy_frac'] * 100:.2f} % of SIMD cycles with the MFMA unit busy."]
     out += ["", "```json pmc-summary", json.dumps(rec, indent=1), "```", ""]
     print("\n".join(out))
+
+
+def summarize_trace(args):
+    """Turn a rocprofv3 --kernel-trace --stats CSV (and the bench JSON line
+    printed by the same run) into the committed kernel-trace summary."""
+    import csv as _csv
+    from prefix_shared_kv_tree_amd import workloads as W
+    rows = list(_csv.DictReader(open(args.trace_csv)))
+    bench = None
+    if args.bench_log:
+        for line in open(args.bench_log):
+            if line.startswith('{"metric"'):
+                bench = json.loads(line)
+    out = [f"# {ATTN_KERNEL} -- kernel trace, workload {args.config}", "",
+           f"Workload: {W.CONFIG_DESCRIPTIONS[args.config]}.", "",
+           "Commands (GPU box, repository root as $R):", "", "```"] + list(args.command) + [
+           "```", "",
+           "| kernel | calls | total ns | avg ns | % | min ns | max ns | stddev |",
+           "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("pkvt::(anonymous namespace)::", "")
+        name = name if len(name) <= 70 else name[:67] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
+                   f"{r['Percentage']} | {r['MinNs']} | {r['MaxNs']} | {float(r['StdDev']):.0f} |")
+    attn = [r for r in rows if ATTN_KERNEL in r["Name"]][0]
+    avg = float(attn["AverageNs"]) / 1e3
+    if bench:
+        out += ["", f"Same run, bench.py's own HIP-event figures: us_per_layer = {bench['us_per_layer']}, "
+                f"attention kernel (events recorded right before and after it on its stream) = "
+                f"{bench['attn_kernel_us']} us, roofline achieved = {bench['roofline']['achieved']} GB/s "
+                f"of {bench['roofline']['peak']} GB/s.",
+                f"rocprofv3 average for {ATTN_KERNEL}: {avg:.2f} us; the event figure is within "
+                f"{abs(bench['attn_kernel_us'] - avg) / avg * 100:.1f} % of it."]
+    print("\n".join(out + [""]))
 
 
 def copy_probe(torch, mib):
@@ -271,7 +338,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=600)
     ap.add_argument("--warmup", type=int, default=60)
-    ap.add_argument("--config", default="c3", choices=["tiny", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c3", choices=["tiny", "c2", "c3", "c4", "c5", "phase1"])
     ap.add_argument("--phase1-chunks", type=int, default=0)
     ap.add_argument("--phase2-chunks", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -285,11 +352,18 @@ def main():
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")
     ap.add_argument("--mfma-csv")
+    ap.add_argument("--trace-csv")
+    ap.add_argument("--summarize-trace", action="store_true",
+                    help="(no GPU) print the kernel-trace summary of --config from a rocprofv3 stats CSV")
+    ap.add_argument("--bench-log")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--command", action="append", default=[])
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the decode attention of one "

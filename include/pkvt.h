@@ -242,16 +242,17 @@ pkvt_status pkvt_attn_decode(const pkvt_tree* tree, const void* d_meta, const vo
                              void* workspace, size_t workspace_bytes, float scale,
                              void* stream);
 
-/* pkvt_attn_decode with a profiling hook: when attn_event is not NULL it
- * must be a hipEvent_t (passed as void*) created on the current device; it
- * is recorded on stream right after the attention kernel is queued and
- * before the merge kernel, so that the caller can time the two launches
- * separately with events on the same stream.  Same arguments and errors as
- * pkvt_attn_decode otherwise. */
+/* pkvt_attn_decode with profiling hooks: attn_start_event and
+ * attn_end_event, when not NULL, must be hipEvent_t values (passed as void*)
+ * created on the current device; they are recorded on stream right before
+ * the attention kernel is queued and right after it (before the merge
+ * kernel), so that the caller can time the attention kernel alone with
+ * events on the same stream.  Same arguments and errors as pkvt_attn_decode
+ * otherwise. */
 pkvt_status pkvt_attn_decode_ex(const pkvt_tree* tree, const void* d_meta, const void* q,
                                 const void* k_pool, const void* v_pool, void* out,
                                 void* workspace, size_t workspace_bytes, float scale,
-                                void* stream, void* attn_event);
+                                void* stream, void* attn_start_event, void* attn_end_event);
 
 /* Write n_tokens tokens' K/V into the pools (the caller's side of arrival
  * and decode append):

@@ -74,7 +74,7 @@ _SIGNATURES = {
     "pkvt_plan_blob": [_vp, _i32p, C.c_int32, _i32p],
     "pkvt_plan_upload": [_vp, _vp, _sz, _vp],
     "pkvt_attn_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp],
-    "pkvt_attn_decode_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp, _vp],
+    "pkvt_attn_decode_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp, _vp, _vp],
     "pkvt_kv_scatter": [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int64, _vp],
     "pkvt_last_error": [],
 }
@@ -253,10 +253,10 @@ def pkvt_attn_decode(tree: int, d_meta: int, q: int, k_pool: int, v_pool: int, o
 
 def pkvt_attn_decode_ex(tree: int, d_meta: int, q: int, k_pool: int, v_pool: int, out: int,
                         workspace: int, workspace_bytes: int, scale: float, stream: int = 0,
-                        attn_event: int = 0) -> None:
+                        attn_start_event: int = 0, attn_end_event: int = 0) -> None:
     _check("pkvt_attn_decode_ex", load().pkvt_attn_decode_ex(
         tree, d_meta, q, k_pool, v_pool, out, workspace or None, workspace_bytes, float(scale),
-        stream or None, attn_event or None))
+        stream or None, attn_start_event or None, attn_end_event or None))
 
 
 def pkvt_kv_scatter(tree: int, k_pool: int, v_pool: int, slots: int, k_new: int, v_new: int,

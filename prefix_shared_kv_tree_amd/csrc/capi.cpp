@@ -288,13 +288,13 @@ pkvt_status pkvt_attn_decode(const pkvt_tree* t, const void* d_meta, const void*
                              const void* k_pool, const void* v_pool, void* out, void* workspace,
                              size_t workspace_bytes, float scale, void* stream) {
     return pkvt_attn_decode_ex(t, d_meta, q, k_pool, v_pool, out, workspace, workspace_bytes,
-                               scale, stream, nullptr);
+                               scale, stream, nullptr, nullptr);
 }
 
 pkvt_status pkvt_attn_decode_ex(const pkvt_tree* t, const void* d_meta, const void* q,
                                 const void* k_pool, const void* v_pool, void* out,
                                 void* workspace, size_t workspace_bytes, float scale,
-                                void* stream, void* attn_event) {
+                                void* stream, void* attn_start_event, void* attn_end_event) {
     if (!t || !d_meta || !q || !k_pool || !v_pool || !out)
         return fail(PKVT_ERR_INVALID_ARG, "attn_decode: NULL argument");
     if (!std::isfinite(scale)) return fail(PKVT_ERR_INVALID_ARG, "attn_decode: scale is not finite");
@@ -332,9 +332,13 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* t, const void* d_meta, const vo
     a.H = H;
     a.n_wg = (p.n_tasks > 0 || p.n_units > 0) ? p.n_wg : 0;
     a.scale_log2e = scale * 1.4426950408889634f;
-    hipError_t e = pkvt::launch_attn(a, D, C, s);
+    hipError_t e;
+    if (attn_start_event &&
+        (e = hipEventRecord(static_cast<hipEvent_t>(attn_start_event), s)) != hipSuccess)
+        return hip_fail(e, "attn_decode: event record");
+    e = pkvt::launch_attn(a, D, C, s);
     if (e != hipSuccess) return hip_fail(e, "attn_decode: attention kernel");
-    if (attn_event && (e = hipEventRecord(static_cast<hipEvent_t>(attn_event), s)) != hipSuccess)
+    if (attn_end_event && (e = hipEventRecord(static_cast<hipEvent_t>(attn_end_event), s)) != hipSuccess)
         return hip_fail(e, "attn_decode: event record");
     if (p.n_merge > 0) {
         pkvt::MergeArgs mg{};

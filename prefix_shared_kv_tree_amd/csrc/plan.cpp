@@ -234,7 +234,17 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     };
     for (size_t s = 0; s < segs.size(); ++s) {
         shared_chunks += static_cast<int32_t>(segs[s].size());
-        const std::vector<int32_t> at = cuts(static_cast<int32_t>(segs[s].size()), s1);
+        // Every phase-1 item writes one partial (o, m, n) per row and head,
+        // read back by the merge: 8 R (d+2) bytes against 4 c d KV bytes
+        // per chunk.  Unless the caller fixed the size, an item is long
+        // enough that its partials cost at most a quarter of its KV bytes.
+        int32_t limit = s1;
+        if (opts.phase1_chunks == 0) {
+            const int64_t rows = seg_range[s].j - seg_range[s].i;
+            const int64_t need = (8 * rows * (t.D + 2) * 4 + 4LL * t.C * t.D - 1) / (4LL * t.C * t.D);
+            limit = static_cast<int32_t>(std::min<int64_t>(kMaxItemChunks, std::max<int64_t>(s1, need)));
+        }
+        const std::vector<int32_t> at = cuts(static_cast<int32_t>(segs[s].size()), limit);
         for (size_t q = 0; q + 1 < at.size(); ++q) {
             Item it;
             it.chunks.assign(segs[s].begin() + at[q], segs[s].begin() + at[q + 1]);

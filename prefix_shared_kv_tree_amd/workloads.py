@@ -32,6 +32,9 @@ VOCAB = 32000
 
 #: Names of the seeded configurations, in index order (seed = 1000 + index).
 CONFIG_NAMES = ("tiny", "c2", "c3", "c4", "c5")
+#: Diagnostic workloads (not among the benchmark configurations); their seeds
+#: continue the index order.
+DIAGNOSTIC_NAMES = ("phase1",)
 
 CONFIG_DESCRIPTIONS = {
     "tiny": "4 decode queries, 2 heads, head_dim 64, chunk 16; one shared "
@@ -45,6 +48,8 @@ CONFIG_DESCRIPTIONS = {
           "256-token suffixes; batch 64",
     "c5": "32 heads, head_dim 128, chunk 64; batch 64, each over its own "
           "private 2048-token context (nothing shared)",
+    "phase1": "diagnostic: 32 heads, head_dim 128, chunk 64; batch 64 whose whole "
+              "context is one shared 4096-token prefix (all work is chunk-first)",
 }
 
 
@@ -120,11 +125,11 @@ def _finish(name, rng, h, d, c, seg_lens, seq_paths, layers, token_fn=None,
 
 def make_config(name: str, layers: int = 1, seed: Optional[int] = None,
                 with_kv: bool = True) -> Workload:
-    """Build one of the five named configurations (see CONFIG_DESCRIPTIONS).
+    """Build one of the named configurations (see CONFIG_DESCRIPTIONS).
 
     ``with_kv=False`` skips the K/V draws (they come last, so tokens and Q
     are unchanged) for tests that only need the token structure."""
-    idx = CONFIG_NAMES.index(name)
+    idx = (CONFIG_NAMES + DIAGNOSTIC_NAMES).index(name)
     rng = np.random.Generator(np.random.PCG64(1000 + idx if seed is None else seed))
     if name == "tiny":
         b, h, d, c = 4, 2, 64, 16
@@ -154,6 +159,10 @@ def make_config(name: str, layers: int = 1, seed: Optional[int] = None,
         b = 64
         seg_lens = [2048] * b
         paths = [[u] for u in range(b)]
+    elif name == "phase1":
+        b = 64
+        seg_lens = [4096]
+        paths = [[0] for _ in range(b)]
     else:  # pragma: no cover
         raise ValueError(name)
     return _finish(name, rng, h, d, c, seg_lens, paths, layers, with_kv=with_kv)
