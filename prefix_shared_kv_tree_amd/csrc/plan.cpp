@@ -48,6 +48,112 @@ int32_t steps_to_chunks(int64_t steps, int32_t C) {
 
 struct Range { int32_t i = 0, j = 0; };
 
+// The lanes of one speed class, ordered by (load, lane).  The balancer only
+// ever takes the first lane and puts it back with a larger load, so the
+// class minimum never decreases: lanes sit in a ring of buckets, one per
+// load value, each a bitset over the class's lanes.  When the loads span
+// too many values for that, a 4-ary heap of (load << lane_bits | lane) keys
+// does the same job.
+class LaneQueue {
+public:
+    void init(int32_t lo, int32_t n, const std::vector<int64_t>& load, int64_t max_cost) {
+        lo_ = lo;
+        n_ = n;
+        if (n <= 0) return;
+        int64_t mn = load[lo], mx = load[lo];
+        for (int32_t l = lo; l < lo + n; ++l) {
+            mn = std::min(mn, load[l]);
+            mx = std::max(mx, load[l]);
+        }
+        words_ = (static_cast<size_t>(n) + 63) / 64;
+        size_t ring = 1;
+        while (ring <= static_cast<size_t>(mx - mn + max_cost)) ring <<= 1;
+        bucket_mode_ = ring * words_ <= (size_t{1} << 22);
+        if (bucket_mode_) {
+            mask_ = ring - 1;
+            bits_.assign(ring * words_, 0);
+            cnt_.assign(ring, 0);
+            cur_ = mn;
+            wc_ = 0;
+            for (int32_t l = lo; l < lo + n; ++l) add(l, load[l]);
+        } else {
+            lane_bits_ = 1;
+            while ((int64_t{1} << lane_bits_) < lo + n) ++lane_bits_;
+            heap_.clear();
+            heap_.reserve(n);
+            for (int32_t l = lo; l < lo + n; ++l) heap_push((static_cast<uint64_t>(load[l]) << lane_bits_) | l);
+        }
+    }
+    bool empty() const { return n_ <= 0; }
+    int64_t min_load() {
+        if (!bucket_mode_) return static_cast<int64_t>(heap_[0] >> lane_bits_);
+        while (cnt_[cur_ & mask_] == 0) {
+            ++cur_;
+            wc_ = 0;
+        }
+        return cur_;
+    }
+    // Take the first lane, give it load min_load() + cost, return it.
+    int32_t take(int64_t cost) {
+        const int64_t l0 = min_load();
+        if (!bucket_mode_) {
+            const int32_t lane = static_cast<int32_t>(heap_[0] & ((uint64_t{1} << lane_bits_) - 1));
+            heap_replace_top((static_cast<uint64_t>(l0 + cost) << lane_bits_) | lane);
+            return lane;
+        }
+        uint64_t* w = &bits_[(l0 & mask_) * words_];
+        while (w[wc_] == 0) ++wc_;
+        const int bit = __builtin_ctzll(w[wc_]);
+        w[wc_] &= w[wc_] - 1;
+        cnt_[l0 & mask_]--;
+        const int32_t lane = lo_ + static_cast<int32_t>(wc_ * 64) + bit;
+        add(lane, l0 + cost);
+        return lane;
+    }
+
+private:
+    void add(int32_t lane, int64_t load) {
+        const size_t k = static_cast<size_t>(lane - lo_);
+        bits_[(load & mask_) * words_ + k / 64] |= uint64_t{1} << (k % 64);
+        cnt_[load & mask_]++;
+    }
+    void heap_push(uint64_t k) {
+        size_t i = heap_.size();
+        heap_.push_back(k);
+        while (i > 0) {
+            const size_t p = (i - 1) / 4;
+            if (heap_[p] <= k) break;
+            heap_[i] = heap_[p];
+            i = p;
+        }
+        heap_[i] = k;
+    }
+    void heap_replace_top(uint64_t k) {
+        const size_t n = heap_.size();
+        size_t i = 0;
+        for (;;) {
+            const size_t c = 4 * i + 1;
+            if (c >= n) break;
+            size_t m = c;
+            const size_t e = std::min(c + 4, n);
+            for (size_t j = c + 1; j < e; ++j) m = heap_[j] < heap_[m] ? j : m;
+            if (heap_[m] >= k) break;
+            heap_[i] = heap_[m];
+            i = m;
+        }
+        heap_[i] = k;
+    }
+
+    int32_t lo_ = 0, n_ = 0;
+    bool bucket_mode_ = true;
+    size_t words_ = 0, mask_ = 0, wc_ = 0;
+    int64_t cur_ = 0;
+    std::vector<uint64_t> bits_;
+    std::vector<int32_t> cnt_;
+    int lane_bits_ = 1;
+    std::vector<uint64_t> heap_;
+};
+
 struct Item {
     std::vector<int32_t> chunks;
     int32_t key_base = 0;
@@ -120,11 +226,35 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
 
     // ---- 1. depth-first order over the batch's paths --------------------------
     const int32_t root = t.root();
-    std::unordered_map<int32_t, std::vector<int32_t>> ends;      // leaf node -> rows
-    std::unordered_map<int32_t, Range> range;                    // node -> [i, j)
-    for (int32_t r = 0; r < b; ++r) {
-        for (int32_t x : seqs[r]->path) range.emplace(x, Range{});
-        ends[seqs[r]->path.back()].push_back(r);
+    PlanScratch& sc = plan.scratch;
+    const size_t n_nodes = static_cast<size_t>(t.N) + 1;
+    if (sc.mark.size() != n_nodes) {
+        sc.mark.assign(n_nodes, 0);
+        sc.node.resize(n_nodes);
+        sc.epoch = 0;
+    }
+    if (++sc.epoch == 0) {
+        std::fill(sc.mark.begin(), sc.mark.end(), 0u);
+        sc.epoch = 1;
+    }
+    const uint32_t epoch = sc.epoch;
+    auto on_path = [&](int32_t x) { return sc.mark[x] == epoch; };
+    PlanScratch::NodeInfo* info = sc.node.data();
+    auto touch = [&](int32_t x) {
+        if (!on_path(x)) {
+            sc.mark[x] = epoch;
+            info[x] = PlanScratch::NodeInfo{0, 0, -1, -1};
+        }
+    };
+    touch(root);
+    for (int32_t r = 0; r < b; ++r)
+        for (int32_t x : seqs[r]->path) touch(x);
+    // rows ending at each leaf, as lists threaded through next_row (ascending)
+    std::vector<int32_t> next_row(b, -1);
+    for (int32_t r = b - 1; r >= 0; --r) {
+        const int32_t leaf = seqs[r]->path.back();
+        next_row[r] = info[leaf].first_row;
+        info[leaf].first_row = r;
     }
     std::vector<int32_t> dfs_row;             // depth-first position -> query row
     std::vector<int32_t> preorder;            // visited nodes, parents first
@@ -132,22 +262,18 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     {
         struct Frame { int32_t node; size_t next; };
         std::vector<Frame> stack{{root, 0}};
-        range[root] = Range{0, 0};
         while (!stack.empty()) {
             Frame& f = stack.back();
             const Node& n = t.node(f.node);
             if (f.next < n.children.size()) {
                 const int32_t ch = n.children[f.next++];
-                auto it = range.find(ch);
-                if (it == range.end()) continue;                  // not on a batch path
-                it->second.i = static_cast<int32_t>(dfs_row.size());
+                if (!on_path(ch)) continue;                       // not on a batch path
+                info[ch].i = static_cast<int32_t>(dfs_row.size());
                 preorder.push_back(ch);
-                auto e = ends.find(ch);
-                if (e != ends.end())
-                    for (int32_t r : e->second) dfs_row.push_back(r);
+                for (int32_t r = info[ch].first_row; r >= 0; r = next_row[r]) dfs_row.push_back(r);
                 stack.push_back({ch, 0});
             } else {
-                range[f.node].j = static_cast<int32_t>(dfs_row.size());
+                info[f.node].j = static_cast<int32_t>(dfs_row.size());
                 stack.pop_back();
             }
         }
@@ -156,26 +282,21 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         err = "plan: internal error, depth-first order lost rows";
         return PKVT_ERR_INVALID_ARG;
     }
-    auto cov = [&](int32_t x) { const Range& r = range[x]; return r.j - r.i; };
+    auto cov = [&](int32_t x) { return info[x].j - info[x].i; };
 
     // ---- 2. phase-1 segments ----------------------------------------------------
     std::vector<std::vector<int32_t>> segs;
     std::vector<Range> seg_range;
-    {
-        std::unordered_map<int32_t, int32_t> seg_of;
-        for (int32_t x : preorder) {
-            if (cov(x) < opts.min_share) continue;
-            const int32_t p = t.node(x).parent;
-            auto it = seg_of.find(p);
-            if (p != root && it != seg_of.end() && range[p].i == range[x].i &&
-                range[p].j == range[x].j) {
-                segs[it->second].push_back(x);
-                seg_of[x] = it->second;
-            } else {
-                seg_of[x] = static_cast<int32_t>(segs.size());
-                segs.push_back({x});
-                seg_range.push_back(range[x]);
-            }
+    for (int32_t x : preorder) {
+        if (cov(x) < opts.min_share) continue;
+        const int32_t p = t.node(x).parent;
+        if (p != root && info[p].seg >= 0 && info[p].i == info[x].i && info[p].j == info[x].j) {
+            segs[info[p].seg].push_back(x);
+            info[x].seg = info[p].seg;
+        } else {
+            info[x].seg = static_cast<int32_t>(segs.size());
+            segs.push_back({x});
+            seg_range.push_back(Range{info[x].i, info[x].j});
         }
     }
     // private suffix of every sequence: path[k0[p] ..)
@@ -337,7 +458,8 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     for (const Item& it : items2) singles.push_back(add_wave(it, 0));
 
     std::vector<std::vector<int32_t>> wg_units(G);
-    std::vector<std::vector<std::pair<int32_t, int32_t>>> lists(lanes);   // (wave, head)
+    std::vector<int32_t> task_lane;                                      // lane of each task
+    std::vector<std::pair<int32_t, int32_t>> task_entry;                  // (wave, head)
     std::vector<int64_t> load(lanes, 0);
     {
         // Workgroups g and g + G/2 share a compute unit and the hardware
@@ -380,29 +502,56 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
             wg_units[g].push_back(ui);
             wgq[pk.first].push({end, g});
         }
-        // single-wave tasks x heads, longest first
-        std::vector<std::pair<int64_t, int32_t>> st;         // (cost, single*H + head)
-        for (size_t i = 0; i < singles.size(); ++i)
-            for (int32_t h = 0; h < t.H; ++h)
-                st.push_back({wave_cost[singles[i]], static_cast<int32_t>(i) * t.H + h});
-        std::stable_sort(st.begin(), st.end(),
-                         [](const auto& a, const auto& c) { return a.first > c.first; });
-        MinHeap lq[2];
-        for (int32_t l = 0; l < lanes; ++l) lq[young(l / kWavesPerWg)].push({load[l], l});
-        for (const auto& e : st) {
-            const auto pk = pick(lq, e.first);
-            const int32_t l = pk.second.second;
-            lists[l].push_back({singles[e.second / t.H], e.second % t.H});
-            load[l] = pk.second.first + e.first;
-            lq[pk.first].push({load[l], l});
+        // single-wave tasks x heads, longest first; equal costs keep the
+        // (task, head) order.  The lane heaps hold load << lane_bits | lane,
+        // which orders like the pair (load, lane).
+        std::vector<int32_t> sorder(singles.size());
+        for (size_t i = 0; i < sorder.size(); ++i) sorder[i] = static_cast<int32_t>(i);
+        std::stable_sort(sorder.begin(), sorder.end(), [&](int32_t a, int32_t c) {
+            return wave_cost[singles[a]] > wave_cost[singles[c]];
+        });
+        int64_t max_cost = 1;
+        for (int32_t w : singles) max_cost = std::max(max_cost, wave_cost[w]);
+        const int32_t n_old = G > 1 ? kWavesPerWg * (G / 2) : lanes;     // lanes of older workgroups
+        LaneQueue lq[2];
+        lq[0].init(0, n_old, load, max_cost);
+        lq[1].init(n_old, lanes - n_old, load, max_cost);
+        task_lane.reserve(singles.size() * t.H);
+        task_entry.reserve(singles.size() * t.H);
+        for (int32_t i : sorder) {
+            const int64_t cost = wave_cost[singles[i]];
+            for (int32_t h = 0; h < t.H; ++h) {
+                int cls = -1;
+                int64_t best = 0;
+                for (int c = 0; c < 2; ++c) {
+                    if (lq[c].empty()) continue;
+                    const int64_t fin = (lq[c].min_load() + cost) * 100 / (c ? kYoungSpeedPct : 100);
+                    if (cls < 0 || fin < best) {
+                        cls = c;
+                        best = fin;
+                    }
+                }
+                const int32_t l = lq[cls].take(cost);
+                load[l] += cost;
+                task_lane.push_back(l);
+                task_entry.push_back({singles[i], h});
+            }
         }
+    }
+    // per-lane lists in assignment order (CSR over lanes)
+    std::vector<int32_t> lane_start(lanes + 1, 0);
+    for (int32_t l : task_lane) lane_start[l + 1]++;
+    for (int32_t l = 0; l < lanes; ++l) lane_start[l + 1] += lane_start[l];
+    std::vector<std::pair<int32_t, int32_t>> lane_tasks(task_lane.size());   // (wave, head)
+    {
+        std::vector<int32_t> fill(lane_start.begin(), lane_start.end() - 1);
+        for (size_t k = 0; k < task_lane.size(); ++k) lane_tasks[fill[task_lane[k]]++] = task_entry[k];
     }
 
     // ---- 6. emit the blob -------------------------------------------------------------
     const int32_t n_waves = static_cast<int32_t>(waves.size());
     const int32_t n_units = static_cast<int32_t>(units.size());
-    int32_t n_tasks = 0;
-    for (auto& l : lists) n_tasks += static_cast<int32_t>(l.size());
+    const int32_t n_tasks = static_cast<int32_t>(lane_tasks.size());
     int32_t total_chunks = 0;
     for (auto* l : wave_chunks) total_chunks += static_cast<int32_t>(l->size());
     for (const Unit& u : units) total_chunks += static_cast<int32_t>(u.it->chunks.size());
@@ -432,15 +581,13 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     while (blob.size() % 4) blob.push_back(0);
 
     {
-        int32_t at = 0;
         for (int32_t l = 0; l < lanes; ++l) {
-            blob[blob[kOffLists] + 2 * l] = at;
-            blob[blob[kOffLists] + 2 * l + 1] = static_cast<int32_t>(lists[l].size());
-            for (const auto& e : lists[l]) {
-                blob[blob[kOffTasks] + 2 * at] = e.first;
-                blob[blob[kOffTasks] + 2 * at + 1] = e.second;
-                ++at;
-            }
+            blob[blob[kOffLists] + 2 * l] = lane_start[l];
+            blob[blob[kOffLists] + 2 * l + 1] = lane_start[l + 1] - lane_start[l];
+        }
+        for (int32_t k = 0; k < n_tasks; ++k) {
+            blob[blob[kOffTasks] + 2 * k] = lane_tasks[k].first;
+            blob[blob[kOffTasks] + 2 * k + 1] = lane_tasks[k].second;
         }
         int32_t coff = 0;
         for (int32_t w = 0; w < n_waves; ++w) {
@@ -493,8 +640,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
 
     // unique (stored) tokens of the batch: every distinct node once
     int64_t unique = 0;
-    for (auto& kv : range)
-        if (kv.first != root) unique += t.node(kv.first).fill;
+    for (int32_t x : preorder) unique += t.node(x).fill;
 
     plan.serial += 1;
     blob[kSerial] = static_cast<int32_t>(plan.serial & 0x7fffffff);

@@ -86,6 +86,16 @@ struct PlanOpts {
     }
 };
 
+// Per-node working state of the planner, kept between calls so that a
+// re-plan allocates nothing proportional to the pool.  An entry is valid when
+// its mark equals the current epoch.
+struct PlanScratch {
+    struct NodeInfo { int32_t i, j, seg, first_row; };
+    std::vector<uint32_t> mark;
+    std::vector<NodeInfo> node;
+    uint32_t epoch = 0;
+};
+
 struct Plan {
     bool valid = false;
     int64_t serial = 0;               // identifies the structure part of the blob
@@ -102,6 +112,7 @@ struct Plan {
     int32_t shared_chunks = 0;
     int64_t unique_tokens = 0, logical_tokens = 0;
     std::vector<int32_t> dfs_seq;     // depth-first position -> sequence id (tests)
+    PlanScratch scratch;
 
     int32_t off(HeaderField f) const { return blob[f]; }
 };
