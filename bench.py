@@ -333,6 +333,100 @@ def copy_probe(torch, mib):
     del src, dst
 
 
+def decode_loop(args, name, layers, static_us_layer):
+    """Decoding iterations with the tree changing under the kernels: per step
+    a token appended to every row (K/V written by pkvt_kv_scatter), the plan
+    refreshed -- rebuilt only when a leaf chunk filled or a sequence left or
+    arrived -- and uploaded lazily, then attention on every layer.  A row
+    gets a new sequence every --loop-churn steps.  Timed twice: pipelined
+    (the host queues steps ahead of the GPU, as a serving loop that does not
+    wait for sampled tokens between layers) and synchronised after every
+    step (host work fully exposed)."""
+    import torch
+    from oracle import attention as A
+    from prefix_shared_kv_tree_amd import workloads as W
+    from prefix_shared_kv_tree_amd.harness import DecodeLoop, DecodeSetup, loop_pool_chunks
+
+    w = W.make_config(name, layers=layers)
+    tails = [len(w.segments[p[-1]]) for p in w.seq_paths if len(p) > 1]
+    suffix = (min(tails), max(tails)) if tails else None
+    warm, t1, t2 = args.loop_warmup, args.loop_steps, args.loop_steps // 2
+    idx = (W.CONFIG_NAMES + W.DIAGNOSTIC_NAMES).index(name)
+    tr = W.decode_trace(w, warm + t1 + t2, seed=2000 + idx, churn_every=args.loop_churn,
+                        suffix=suffix)
+    ds = DecodeSetup(w, layers=layers, pool_chunks=loop_pool_chunks(tr))
+    loop = DecodeLoop(ds, tr)
+    for t in range(warm):
+        loop.step(t)
+    torch.cuda.synchronize()
+
+    def snapshot():
+        return dict(loop.host.us), dict(loop.host.count), loop.us_total
+
+    # pipelined
+    h0 = snapshot()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    attn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(t1)]
+    e0.record()
+    for k in range(t1):
+        loop.step(warm + k, events=attn_ev[k])
+    e1.record()
+    torch.cuda.synchronize()
+    pipe_us = e0.elapsed_time(e1) * 1e3 / t1
+    attn_us = [a.elapsed_time(b) * 1e3 for a, b in attn_ev]
+    h1 = snapshot()
+    # synchronised after every step
+    sync_us = []
+    for k in range(t2):
+        s0 = time.perf_counter()
+        loop.step(warm + t1 + k)
+        torch.cuda.synchronize()
+        sync_us.append((time.perf_counter() - s0) * 1e6)
+    t_last = warm + t1 + t2 - 1
+    h2 = snapshot()
+
+    def host_means(a, b, n_steps):
+        us = {k: (b[0][k] - a[0][k]) for k in b[0]}
+        cnt = {k: (b[1][k] - a[1][k]) for k in b[1]}
+        tree_plan = sum(us.values())
+        return {
+            "per_step": round((b[2] - a[2]) / n_steps, 1),
+            "tree_and_plan_per_step": round(tree_plan / n_steps, 1),
+            "append": round(us["append"] / max(cnt["append"], 1), 1),
+            "plan_full": round(us["plan_full"] / max(cnt["plan_full"], 1), 1),
+            "plan_refresh": round(us["plan_refresh"] / max(cnt["plan_refresh"], 1), 1),
+            "join": round(us["join"] / max(cnt["join"], 1), 1),
+            "full_replans": cnt["plan_full"], "refreshes": cnt["plan_refresh"], "joins": cnt["join"],
+        }
+
+    # parity on sampled rows (every replaced row among them) at the last step
+    got = loop.out.float().cpu().numpy()
+    rows = sorted(set([0, w.b // 2, w.b - 1] + [j.row for j in tr.joins]))[:12]
+    wt = tr.workload_at(t_last)
+    err = 0.0
+    for l in range(layers):
+        ref = A.attention_batch(wt, layer=l, seqs=rows)
+        err = max(err, float(max(np.abs(got[l][u] - ref[u]).max() for u in rows)))
+    ctx = [wt.seq_len(u) for u in range(w.b)]
+    res = {
+        "layers": layers, "steps_pipelined": t1, "steps_synced": t2, "warmup": warm,
+        "churn_every": args.loop_churn, "join_suffix_tokens": list(suffix) if suffix else None,
+        "context_tokens_at_end": {"min": int(min(ctx)), "max": int(max(ctx)),
+                                  "mean": round(float(np.mean(ctx)), 1)},
+        "us_per_step_pipelined": round(pipe_us, 1),
+        "us_per_step_synced": round(float(np.median(sync_us)), 1),
+        "attn_us_per_layer": round(float(np.mean(attn_us)) / layers, 2),
+        "static_attn_us_per_layer": None if static_us_layer is None else round(static_us_layer, 2),
+        "host_us_pipelined": host_means(h0, h1, t1),
+        "host_us_synced": host_means(h1, h2, t2),
+        "meta_regrow": loop.regrow,
+        "parity_max_abs_err_sampled": err,
+    }
+    ds.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +452,14 @@ def main():
     ap.add_argument("--bench-log")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--loop-steps", type=int, default=128,
+                    help="decode-loop steps timed pipelined (half as many again synchronised)")
+    ap.add_argument("--loop-warmup", type=int, default=8)
+    ap.add_argument("--loop-churn", type=int, default=16,
+                    help="a row gets a new sequence every this many decode-loop steps")
+    ap.add_argument("--no-loop", action="store_true")
+    ap.add_argument("--loop-only", action="store_true",
+                    help="run only the decode loop (for profiling it)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args)
@@ -383,6 +485,10 @@ def main():
     b_tok = probe.h * probe.d * 2 * 2
     unique_bytes_est = W.unique_tokens(probe) * b_tok
     layers = max(2, math.ceil(2 * 2 ** 30 / unique_bytes_est))
+    if args.loop_only:
+        print(json.dumps({"config": args.config,
+                          "decode_loop": decode_loop(args, args.config, layers, None)}), flush=True)
+        return
     t0 = time.perf_counter()
     w = W.make_config(args.config, layers=layers)
     gen_s = time.perf_counter() - t0
@@ -495,6 +601,9 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, unique_bytes, args.cpu_budget)
     ds.close()
+    del ds
+    if not args.no_loop:
+        res["decode_loop"] = decode_loop(args, args.config, layers, us_layer)
     if args.copy_probe_mib:
         copy_probe(torch, args.copy_probe_mib)
     print(json.dumps(res), flush=True)

@@ -123,3 +123,211 @@ class DecodeSetup:
             self.close()
         except Exception:
             pass
+
+
+class HostDecoder:
+    """Tree side of decoding a trace (``workloads.DecodeTrace``).
+
+    Per step: departures and arrivals of the step's joins (``pkvt_tree_remove``
+    then ``pkvt_tree_build``), one ``pkvt_tree_append`` for the whole batch,
+    and ``pkvt_plan`` for the rows' live sequences.  The plan is rebuilt only
+    when the tree's structure changed (a leaf chunk filled and a new one was
+    allocated, or a sequence arrived or left); otherwise only the length
+    table is refreshed (ChunkAttention page, Knowl 5, lazy context copy).
+    Needs no GPU.  Host time per call is accumulated in ``us`` (microseconds)
+    and ``count``."""
+
+    def __init__(self, tree: int, trace, seq_ids, **plan_kw):
+        self.tree = tree
+        self.tr = trace
+        self.rows = np.array(seq_ids, dtype=np.int32)        # row -> live sequence id
+        self.plan_kw = plan_kw
+        self.us = {"join": 0.0, "append": 0.0, "plan_full": 0.0, "plan_refresh": 0.0}
+        self.count = {"join": 0, "append": 0, "plan_full": 0, "plan_refresh": 0}
+        self.structural = True
+
+    def _time(self, key, t0):
+        import time
+        self.us[key] += (time.perf_counter_ns() - t0) / 1e3
+        self.count[key] += 1
+
+    def joins(self, t: int):
+        """Apply step t's departures/arrivals.  Returns [(join, prompt slots)]."""
+        import time
+        out = []
+        for j in self.tr.joins_at(t):
+            t0 = time.perf_counter_ns()
+            B.pkvt_tree_remove(self.tree, int(self.rows[j.row]))
+            ids, slots = B.pkvt_tree_build(self.tree, [self.tr.prompt_tokens(j)])
+            self.rows[j.row] = ids[0]
+            self._time("join", t0)
+            self.structural = True
+            out.append((j, slots))
+        return out
+
+    def append(self, t: int) -> np.ndarray:
+        """Append step t's tokens; returns the slot of every row's new token."""
+        import time
+        t0 = time.perf_counter_ns()
+        slots = B.pkvt_tree_append(self.tree, self.rows, self.tr.tokens[t])
+        self._time("append", t0)
+        # a token at offset 0 of its chunk opened a new leaf chunk
+        if np.any(slots % self.tr.base.c == 0):
+            self.structural = True
+        return slots
+
+    def plan(self):
+        """(meta_bytes, workspace_bytes) of the plan for the rows' sequences."""
+        import time
+        t0 = time.perf_counter_ns()
+        mb, wb = B.pkvt_plan(self.tree, self.rows, **self.plan_kw)
+        self._time("plan_full" if self.structural else "plan_refresh", t0)
+        self.structural = False
+        return mb, wb
+
+
+class DecodeLoop:
+    """Decoding iterations over a ``DecodeSetup``, driven by a decode trace.
+
+    Step t, as a model's attention layers would run it (ChunkAttention page,
+    Knowl 1 and Knowl 5): the host applies the step's joins and appends one
+    token per row; the new tokens' slots go to the device through a ring of
+    pinned buffers; for every layer ``pkvt_kv_scatter`` writes the new K/V
+    into that layer's pools; the plan is refreshed (rebuilt only after a
+    structural change) and ``pkvt_plan_upload`` copies what changed; then
+    ``pkvt_attn_decode`` runs for every layer with the step's queries,
+    writing ``out[layer]``.  Nothing waits for the GPU except the pinned
+    ring (a buffer is reused only after its copy has run).  The trace's
+    per-step inputs live in device memory from construction on."""
+
+    def __init__(self, ds: "DecodeSetup", trace, ring: int = 8, **plan_kw):
+        torch = ds.torch
+        self.torch = torch
+        self.ds = ds
+        self.tr = trace
+        w = trace.base
+        dev = ds.device
+        if ds.layers > w.layers:
+            raise ValueError("the trace has fewer layers than the setup")
+        self.host = HostDecoder(ds.tree, trace, ds.seq_ids, **plan_kw)
+        self.q = torch.from_numpy(trace.q).to(dev)
+        self.k = [torch.from_numpy(trace.k[l]).to(dev) for l in range(ds.layers)]
+        self.v = [torch.from_numpy(trace.v[l]).to(dev) for l in range(ds.layers)]
+        self.join_kv = {}
+        for j in trace.joins:
+            self.join_kv[id(j)] = (
+                [torch.from_numpy(np.ascontiguousarray(j.suffix.k[l])).to(dev) for l in range(ds.layers)],
+                [torch.from_numpy(np.ascontiguousarray(j.suffix.v[l])).to(dev) for l in range(ds.layers)])
+        self.out = torch.empty((ds.layers, w.b, w.h, w.d), dtype=torch.float16, device=dev)
+        cap = max([w.b] + [len(j.suffix) + sum(len(w.segments[s]) for s in j.shared)
+                           for j in trace.joins])
+        self.ring = [(torch.empty(cap, dtype=torch.int64).pin_memory(),
+                      torch.empty(cap, dtype=torch.int64, device=dev),
+                      torch.cuda.Event()) for _ in range(ring)]
+        self.ring_used = [False] * ring
+        self.ring_at = 0
+        self.regrow = 0
+        self.us_total = 0.0
+        self.steps_run = 0
+        mb, wb = self.host.plan()
+        self.meta = torch.empty(max(2 * mb, 1 << 16) // 4, dtype=torch.int32, device=dev)
+        self.ws = torch.empty(max(2 * wb, 1 << 16) // 4, dtype=torch.float32, device=dev)
+        self.meta_bytes = mb
+        self.ws_bytes = wb
+        B.pkvt_plan_upload(ds.tree, self.meta.data_ptr(), self.meta.numel() * 4,
+                           torch.cuda.current_stream().cuda_stream)
+
+    def _to_device(self, slots: np.ndarray):
+        """Copy int64 slots to the device through the pinned ring."""
+        k = self.ring_at
+        self.ring_at = (k + 1) % len(self.ring)
+        pin, dst, ev = self.ring[k]
+        if self.ring_used[k]:
+            ev.synchronize()
+        n = slots.shape[0]
+        pin[:n].numpy()[:] = slots
+        dst[:n].copy_(pin[:n], non_blocking=True)
+        ev.record()
+        self.ring_used[k] = True
+        return dst
+
+    def _scatter(self, layer, d_slots, k_src, v_src, n, stream):
+        ds = self.ds
+        B.pkvt_kv_scatter(ds.tree, ds.k_pools[layer].data_ptr(), ds.v_pools[layer].data_ptr(),
+                          d_slots.data_ptr(), k_src.data_ptr(), v_src.data_ptr(), n, stream)
+
+    def _join_kv(self, j, slots, stream):
+        """Write the K/V of a new sequence's prompt tokens that need storing:
+        its suffix from device memory, and (when the kept prefix ends inside
+        a chunk) the few prefix tokens that landed in a fresh chunk."""
+        torch, ds, w = self.torch, self.ds, self.tr.base
+        n_pre = sum(len(w.segments[s]) for s in j.shared)
+        pre = slots[:n_pre]
+        need = np.nonzero(pre >= 0)[0]
+        if need.size:
+            for l in range(ds.layers):
+                kk = np.concatenate([w.segments[s].k[l] for s in j.shared])[need]
+                vv = np.concatenate([w.segments[s].v[l] for s in j.shared])[need]
+                kd = torch.from_numpy(np.ascontiguousarray(kk)).to(ds.device)
+                vd = torch.from_numpy(np.ascontiguousarray(vv)).to(ds.device)
+                d = self._to_device(pre[need])
+                self._scatter(l, d, kd, vd, need.size, stream)
+        suf = slots[n_pre:]
+        if suf.size:
+            d = self._to_device(suf)
+            ks, vs = self.join_kv[id(j)]
+            for l in range(ds.layers):
+                self._scatter(l, d, ks[l], vs[l], suf.size, stream)
+
+    def step(self, t: int, events=None):
+        """Run decode step t.  ``events`` = (start, end) torch events recorded
+        around the step's attention calls.  Host time of the step goes to
+        ``us_total`` (microseconds); the part spent outside HostDecoder
+        (copies, uploads, launches) is ``us_total`` minus the host's timers."""
+        import time
+        t_enter = time.perf_counter_ns()
+        torch, ds = self.torch, self.ds
+        stream = torch.cuda.current_stream().cuda_stream
+        for j, slots in self.host.joins(t):
+            self._join_kv(j, slots, stream)
+        slots = self.host.append(t)
+        d = self._to_device(slots)
+        b = self.tr.base.b
+        for l in range(ds.layers):
+            self._scatter(l, d, self.k[l][t], self.v[l][t], b, stream)
+        mb, wb = self.host.plan()
+        if mb > self.meta.numel() * 4 or wb > self.ws.numel() * 4:
+            self.regrow += 1
+            if mb > self.meta.numel() * 4:
+                self.meta = torch.empty(2 * mb // 4, dtype=torch.int32, device=ds.device)
+            if wb > self.ws.numel() * 4:
+                self.ws = torch.empty(2 * wb // 4, dtype=torch.float32, device=ds.device)
+        self.meta_bytes, self.ws_bytes = mb, wb
+        B.pkvt_plan_upload(ds.tree, self.meta.data_ptr(), self.meta.numel() * 4, stream)
+        if events is not None:
+            events[0].record()
+        q = self.q[t]
+        for l in range(ds.layers):
+            B.pkvt_attn_decode(ds.tree, self.meta.data_ptr(), q.data_ptr(),
+                               ds.k_pools[l].data_ptr(), ds.v_pools[l].data_ptr(),
+                               self.out[l].data_ptr(), self.ws.data_ptr() if wb else 0, wb,
+                               ds.scale, stream)
+        if events is not None:
+            events[1].record()
+        self.us_total += (time.perf_counter_ns() - t_enter) / 1e3
+        self.steps_run += 1
+        return self.out
+
+
+def loop_pool_chunks(trace) -> int:
+    """A pool size that a decode trace cannot exhaust: every base sequence's
+    chunks as if nothing were shared, plus, for every row and every join,
+    the chunks its appends and prompt could open."""
+    w = trace.base
+    c = w.c
+    grow = trace.steps // c + 2
+    n = sum(-(-w.seq_len(u) // c) for u in range(w.b)) + w.b * grow
+    for j in trace.joins:
+        n_pre = sum(len(w.segments[s]) for s in j.shared)
+        n += -(-(n_pre + len(j.suffix)) // c) + grow
+    return n

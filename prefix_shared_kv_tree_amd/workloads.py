@@ -312,3 +312,101 @@ def unique_tokens(w: Workload) -> int:
 
 def logical_tokens(w: Workload) -> int:
     return int(sum(w.seq_len(u) for u in range(w.b)))
+
+
+# ---- decode traces -------------------------------------------------------------
+#
+# A decode trace drives a batch through T decoding iterations (ChunkAttention
+# page, Knowl 1: each iteration appends one token per sequence to its leaf
+# chunk; sequences leave and new ones arrive while decoding goes on).  Row r
+# of the batch is one slot of the serving batch: at step t it holds one live
+# sequence, whose query is q[t, r] and whose new token (id, and K/V of every
+# layer) is tokens[t, r], k[layer][t, r], v[layer][t, r].  A join at step t
+# replaces the sequence of its row before that step's append: the old
+# sequence departs, and a new one arrives whose prompt is the old one's
+# shared segments (every segment of its base path but the last) followed by
+# a fresh private suffix.  The step-t append then adds the new sequence's
+# first decoded token.
+
+@dataclasses.dataclass
+class Join:
+    step: int
+    row: int
+    shared: List[int]                  # base segment indices kept from the row's path
+    suffix: Segment                    # the new private part of the prompt
+
+
+@dataclasses.dataclass
+class DecodeTrace:
+    base: Workload
+    steps: int
+    tokens: np.ndarray                 # int32 [T, b]
+    q: np.ndarray                      # float16 [T, b, h, d]
+    k: List[np.ndarray]                # per layer: float16 [T, b, h, d]
+    v: List[np.ndarray]
+    joins: List[Join]                  # in step order
+
+    def joins_at(self, t: int) -> List[Join]:
+        return [j for j in self.joins if j.step == t]
+
+    def prompt_tokens(self, j: Join) -> np.ndarray:
+        return np.concatenate([self.base.segments[s].tokens for s in j.shared] + [j.suffix.tokens])
+
+    def workload_at(self, t: int) -> Workload:
+        """The batch that step t's attention sees: every row's live sequence
+        after step t's joins and appends, with the queries of step t."""
+        w = self.base
+        if not 0 <= t < self.steps:
+            raise ValueError(f"step {t} outside [0, {self.steps})")
+        segs = list(w.segments)
+        paths = [list(p) for p in w.seq_paths]
+        start = [0] * w.b
+        for j in self.joins:
+            if j.step > t:
+                break
+            segs.append(j.suffix)
+            paths[j.row] = list(j.shared) + [len(segs) - 1]
+            start[j.row] = j.step
+        for r in range(w.b):
+            s = start[r]
+            segs.append(Segment(tokens=self.tokens[s:t + 1, r],
+                                k=[self.k[l][s:t + 1, r] for l in range(w.layers)],
+                                v=[self.v[l][s:t + 1, r] for l in range(w.layers)]))
+            paths[r].append(len(segs) - 1)
+        return Workload(name=f"{w.name}@step{t}", h=w.h, d=w.d, c=w.c, segments=segs,
+                        seq_paths=paths, q=self.q[t], layers=w.layers)
+
+
+def decode_trace(w: Workload, steps: int, seed: int, churn_every: int = 0,
+                 suffix=None) -> DecodeTrace:
+    """Draw a decode trace of ``steps`` iterations over the batch of ``w``.
+
+    Every ``churn_every`` steps (0 = never) one row, drawn uniformly, gets a
+    new sequence whose private suffix length is uniform in ``suffix``
+    (inclusive; default [c/2, 4c]).  Draw order, from one PCG64 generator
+    seeded with ``seed``: tokens [T, b]; per join (in step order) its row,
+    suffix length and suffix tokens; Q [T, b, h, d]; then for each layer:
+    K [T, b, h, d], V [T, b, h, d], and every join's suffix K then V."""
+    if steps < 1:
+        raise ValueError("steps must be >= 1")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    b, h, d, c = w.b, w.h, w.d, w.c
+    lo, hi = suffix if suffix is not None else (max(1, c // 2), 4 * c)
+    tokens = rng.integers(0, VOCAB, size=(steps, b), dtype=np.int64).astype(np.int32)
+    joins: List[Join] = []
+    if churn_every > 0:
+        for t in range(churn_every, steps, churn_every):
+            row = int(rng.integers(0, b))
+            n = int(rng.integers(lo, hi + 1))
+            toks = rng.integers(0, VOCAB, size=n, dtype=np.int64).astype(np.int32)
+            joins.append(Join(step=t, row=row, shared=list(w.seq_paths[row][:-1]),
+                              suffix=Segment(tokens=toks, k=[], v=[])))
+    q = _normal_f16(rng, (steps, b, h, d))
+    ks, vs = [], []
+    for _ in range(w.layers):
+        ks.append(_normal_f16(rng, (steps, b, h, d)))
+        vs.append(_normal_f16(rng, (steps, b, h, d)))
+        for j in joins:
+            j.suffix.k.append(_normal_f16(rng, (len(j.suffix), h, d)))
+            j.suffix.v.append(_normal_f16(rng, (len(j.suffix), h, d)))
+    return DecodeTrace(base=w, steps=steps, tokens=tokens, q=q, k=ks, v=vs, joins=joins)
