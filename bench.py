@@ -319,6 +319,66 @@ def summarize_trace(args):
     print("\n".join(out + [""]))
 
 
+def summarize_loop_trace(args):
+    """Turn the rocprofv3 --kernel-trace --memory-copy-trace --stats output of
+    a `bench.py --loop-only` run (and that run's JSON line) into the
+    committed decode-loop summary: per-kernel stats and the GPU time of one
+    pipelined step split by kernel."""
+    import csv as _csv
+    from collections import defaultdict
+    from prefix_shared_kv_tree_amd import workloads as W
+    d = args.trace_dir
+    stats = list(_csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    trace = list(_csv.DictReader(open(os.path.join(d, "run_kernel_trace.csv"))))
+    loop = None
+    for line in open(args.bench_log):
+        if line.startswith('{"config"'):
+            loop = json.loads(line)["decode_loop"]
+
+    def short(n):
+        n = n.replace("pkvt::(anonymous namespace)::", "").replace("void ", "")
+        return n.split("(")[0]
+
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short(r["Kernel_Name"]))
+                for r in trace)
+    attn = [e for e in ev if e[2].startswith("attn_kernel")]
+    L, T, warm = loop["layers"], loop["steps_pipelined"], loop["warmup"]
+    t0, t1 = attn[warm * L][0], attn[(warm + T) * L - 1][1]
+    region = [e for e in ev if t0 <= e[0] <= t1]
+    tot, cnt = defaultdict(float), defaultdict(int)
+    for s_, e_, n in region:
+        tot[n] += (e_ - s_) / 1e3
+        cnt[n] += 1
+    span = (t1 - t0) / 1e3 / T
+    busy = sum(tot.values()) / T
+    out = [f"# Decode loop -- kernel trace, workload {args.config}", "",
+           f"Workload: {W.CONFIG_DESCRIPTIONS[args.config]}; {L} layers, decoded for "
+           f"{warm} + {T} (pipelined) + {loop['steps_synced']} (synchronised) steps, a row "
+           f"replaced every {loop['churn_every']} steps.", "",
+           "Commands (GPU box, repository root as $R):", "", "```"] + list(args.command) + [
+           "```", "",
+           "| kernel | calls | total ns | avg ns | % | min ns | max ns |",
+           "|---|---|---|---|---|---|---|"]
+    for r in stats:
+        name = short(r["Name"])
+        out.append(f"| `{name[:70]}` | {r['Calls']} | {r['TotalDurationNs']} | "
+                   f"{float(r['AverageNs']):.0f} | {r['Percentage']} | {r['MinNs']} | {r['MaxNs']} |")
+    out += ["", f"GPU time per pipelined step (from the first attention launch of step {warm} to "
+            f"the end of the last of step {warm + T - 1}): {span:.1f} us, of which kernels "
+            f"busy {busy:.1f} us:", "",
+            "| kernel | launches per step | us per step | avg us |", "|---|---|---|---|"]
+    for n in sorted(tot, key=lambda k: -tot[k]):
+        out.append(f"| `{n}` | {cnt[n] / T:.2f} | {tot[n] / T:.1f} | {tot[n] / cnt[n]:.1f} |")
+    out += ["", f"Same run, bench.py's own figures: us_per_step_pipelined = "
+            f"{loop['us_per_step_pipelined']}, attn_us_per_layer (events around the attention "
+            f"calls) = {loop['attn_us_per_layer']}, host us per step (pipelined) = "
+            f"{loop['host_us_pipelined']['per_step']}, of which tree and plan = "
+            f"{loop['host_us_pipelined']['tree_and_plan_per_step']}; full plan "
+            f"{loop['host_us_pipelined']['plan_full']} us, length refresh "
+            f"{loop['host_us_pipelined']['plan_refresh']} us."]
+    print("\n".join(out + [""]))
+
+
 def copy_probe(torch, mib):
     """A plain copy of known size (torch's elementwise kernel: `mib` MiB read,
     `mib` MiB written), launched three times.  Under a counter-collection run
@@ -450,6 +510,10 @@ def main():
     ap.add_argument("--summarize-trace", action="store_true",
                     help="(no GPU) print the kernel-trace summary of --config from a rocprofv3 stats CSV")
     ap.add_argument("--bench-log")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--summarize-loop-trace", action="store_true",
+                    help="(no GPU) print the decode-loop trace summary from a rocprofv3 output "
+                         "directory (--trace-dir) and the run's log (--bench-log)")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--loop-steps", type=int, default=128,
@@ -466,6 +530,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_loop_trace:
+        summarize_loop_trace(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the decode attention of one "

@@ -211,11 +211,13 @@ pkvt_status pkvt_plan_info_get(const pkvt_tree* tree, pkvt_plan_info* out);
 pkvt_status pkvt_plan_blob(const pkvt_tree* tree, int32_t* out, int32_t cap, int32_t* n);
 
 /* Copy the current plan to the caller's device buffer d_meta (>= meta_bytes)
- * with an asynchronous host-to-device copy on stream.  Lazy (Knowl 5): when
- * d_meta already holds this plan nothing is copied, and when only sequence
- * lengths changed (decode appends that did not open a new chunk) only the
- * length table is copied.  The library's host staging buffer is not reused
- * until the previous copy from it has completed.
+ * asynchronously on stream: the words go to a pinned, device-mapped host
+ * staging buffer and a small kernel on stream copies them into d_meta (no
+ * copy engine is involved).  Lazy (Knowl 5): when d_meta already holds this
+ * plan nothing is copied, and when only sequence lengths changed (decode
+ * appends that did not open a new chunk) only the length table is copied.
+ * The library keeps a ring of 4 staging buffers and reuses one only after
+ * the copy from it has run, so the host may run up to 4 uploads ahead.
  * Errors: STALE_PLAN (no plan / tree changed since pkvt_plan),
  * BUFFER_TOO_SMALL, HIP. */
 pkvt_status pkvt_plan_upload(pkvt_tree* tree, void* d_meta, size_t meta_bytes, void* stream);
@@ -264,6 +266,17 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* tree, const void* d_meta, const
 pkvt_status pkvt_kv_scatter(const pkvt_tree* tree, void* k_pool, void* v_pool,
                             const int64_t* slots, const void* k_new, const void* v_new,
                             int64_t n_tokens, void* stream);
+
+/* pkvt_kv_scatter for one decode step's new tokens with the slots still in
+ * HOST memory (as pkvt_tree_append returned them): the n_tokens <=
+ * PKVT_INLINE_SLOTS slots are copied into the kernel's launch arguments
+ * during the call, so the caller needs no device slot buffer and the stream
+ * no host-to-device copy.  slots may be reused as soon as the call returns.
+ * Errors: INVALID_ARG (also n_tokens > PKVT_INLINE_SLOTS), HIP. */
+#define PKVT_INLINE_SLOTS 256
+pkvt_status pkvt_kv_scatter_host_slots(const pkvt_tree* tree, void* k_pool, void* v_pool,
+                                       const int64_t* slots, const void* k_new,
+                                       const void* v_new, int64_t n_tokens, void* stream);
 
 const char* pkvt_last_error(void);
 

@@ -76,6 +76,7 @@ _SIGNATURES = {
     "pkvt_attn_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp],
     "pkvt_attn_decode_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp, _vp, _vp],
     "pkvt_kv_scatter": [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int64, _vp],
+    "pkvt_kv_scatter_host_slots": [_vp, _vp, _vp, _i64p, _vp, _vp, C.c_int64, _vp],
     "pkvt_last_error": [],
 }
 _RESTYPE = {"pkvt_tree_destroy": None, "pkvt_last_error": C.c_char_p}
@@ -263,6 +264,17 @@ def pkvt_kv_scatter(tree: int, k_pool: int, v_pool: int, slots: int, k_new: int,
                     n_tokens: int, stream: int = 0) -> None:
     _check("pkvt_kv_scatter", load().pkvt_kv_scatter(tree, k_pool, v_pool, slots, k_new, v_new,
                                                      int(n_tokens), stream or None))
+
+
+PKVT_INLINE_SLOTS = 256
+
+
+def pkvt_kv_scatter_host_slots(tree: int, k_pool: int, v_pool: int, slots, k_new: int,
+                               v_new: int, stream: int = 0) -> None:
+    """slots: host int64 array (at most PKVT_INLINE_SLOTS entries)."""
+    s = _i64(slots)
+    _check("pkvt_kv_scatter_host_slots", load().pkvt_kv_scatter_host_slots(
+        tree, k_pool, v_pool, _p64(s), k_new, v_new, int(s.size), stream or None))
 
 
 def pkvt_last_error() -> str:

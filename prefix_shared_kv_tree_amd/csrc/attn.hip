@@ -47,6 +47,7 @@
 // read with non-temporal loads.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "kernels.h"
@@ -584,16 +585,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }
 
 // Write tokens' K/V (natural [token][head][dim]) into their pool slots.
+// One thread moves 8 dims of one (token, head): a 16-byte K piece and the
+// same dims of V.
 template <int D, int C>
-__global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
+__device__ __forceinline__ void scatter_piece(const ScatterArgs& a, int64_t gid, int64_t slot_of_tok,
+                                              int64_t tok) {
     constexpr int P = D / 8;
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (gid >= a.n_tokens * a.H * P) return;
     const int piece = static_cast<int>(gid % P);
-    const int64_t th = gid / P;
-    const int head = static_cast<int>(th % a.H);
-    const int64_t tok = th / a.H;
-    const int64_t slot = a.slots[tok];
+    const int head = static_cast<int>((gid / P) % a.H);
+    const int64_t slot = slot_of_tok;
     if (slot < 0 || slot >= a.slot_limit) return;
     const int64_t chunk = slot / C;
     const int t = static_cast<int>(slot % C);
@@ -610,6 +610,30 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
 }
 
 template <int D, int C>
+__global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= a.n_tokens * a.H * (D / 8)) return;
+    const int64_t tok = gid / (static_cast<int64_t>(a.H) * (D / 8));
+    scatter_piece<D, C>(a, gid, a.slots[tok], tok);
+}
+
+// Same, with the slots in the launch arguments (n_tokens <= kInlineSlots).
+template <int D, int C>
+__global__ __launch_bounds__(256) void scatter_inline_kernel(ScatterArgs a, InlineSlots is) {
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= a.n_tokens * a.H * (D / 8)) return;
+    const int64_t tok = gid / (static_cast<int64_t>(a.H) * (D / 8));
+    scatter_piece<D, C>(a, gid, is.slot[tok], tok);
+}
+
+__global__ __launch_bounds__(256) void copy_words_kernel(const int32_t* __restrict__ src,
+                                                         int32_t* __restrict__ dst, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        dst[i] = src[i];
+}
+
+template <int D, int C>
 hipError_t attn_dc(const AttnArgs& a, hipStream_t s) {
     const unsigned grid = static_cast<unsigned>(a.n_wg);
     if (grid == 0) return hipSuccess;
@@ -622,6 +646,15 @@ hipError_t scatter_dc(const ScatterArgs& a, hipStream_t s) {
     const int64_t threads = a.n_tokens * a.H * (D / 8);
     if (threads == 0) return hipSuccess;
     scatter_kernel<D, C><<<dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int D, int C>
+hipError_t scatter_inline_dc(const ScatterArgs& a, const InlineSlots& is, hipStream_t s) {
+    const int64_t threads = a.n_tokens * a.H * (D / 8);
+    if (threads == 0) return hipSuccess;
+    scatter_inline_kernel<D, C><<<dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s>>>(
+        a, is);
     return hipGetLastError();
 }
 
@@ -646,6 +679,19 @@ hipError_t launch_attn(const AttnArgs& a, int D, int C, hipStream_t s) {
 
 hipError_t launch_scatter(const ScatterArgs& a, int D, int C, hipStream_t s) {
     PKVT_DISPATCH(scatter_dc, D, C, a, s)
+}
+
+hipError_t launch_scatter_inline(const ScatterArgs& a, const InlineSlots& is, int D, int C,
+                                 hipStream_t s) {
+    if (a.n_tokens > kInlineSlots) return hipErrorInvalidValue;
+    PKVT_DISPATCH(scatter_inline_dc, D, C, a, is, s)
+}
+
+hipError_t launch_copy_words(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+    copy_words_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(src, dst, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, int D, hipStream_t s) {

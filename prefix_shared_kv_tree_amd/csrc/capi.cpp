@@ -4,6 +4,7 @@
 // metadata upload, made on the first upload.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -14,6 +15,17 @@
 #include "plan.h"
 #include "tree.h"
 
+// Pinned host buffer that the metadata upload kernel reads through its
+// device mapping, with the event that marks the end of that read.
+struct Staging {
+    int32_t* host = nullptr;
+    const int32_t* dev = nullptr;
+    size_t words = 0;
+    hipEvent_t done = nullptr;
+    bool in_flight = false;
+};
+constexpr int kStagingRing = 4;
+
 struct pkvt_tree {
     pkvt::Tree tree;
     pkvt::Plan plan;
@@ -21,17 +33,16 @@ struct pkvt_tree {
     const void* uploaded_ptr = nullptr;
     int64_t uploaded_serial = -1;
     int64_t uploaded_len_version = -1;
-    // pinned staging for the host-to-device copy
-    int32_t* staging = nullptr;
-    size_t staging_words = 0;
-    hipEvent_t staging_done = nullptr;
-    bool copy_in_flight = false;
+    Staging staging[kStagingRing];
+    int next_staging = 0;
 
     pkvt_tree(int32_t h, int32_t d, int32_t c, int32_t n) : tree(h, d, c, n) {}
     ~pkvt_tree() {
-        if (copy_in_flight) (void)hipEventSynchronize(staging_done);
-        if (staging) (void)hipHostFree(staging);
-        if (staging_done) (void)hipEventDestroy(staging_done);
+        for (Staging& st : staging) {
+            if (st.in_flight) (void)hipEventSynchronize(st.done);
+            if (st.host) (void)hipHostFree(st.host);
+            if (st.done) (void)hipEventDestroy(st.done);
+        }
     }
 };
 
@@ -255,29 +266,42 @@ pkvt_status pkvt_plan_upload(pkvt_tree* t, void* d_meta, size_t meta_bytes, void
         first = static_cast<size_t>(p.blob[pkvt::kOffSeqlen]);           // lengths only
         count = static_cast<size_t>(p.b);
     }
+    if (count % 4) count += 4 - count % 4;            // sections are padded to 16 bytes
+    count = std::min(count, words - first);
     hipError_t e;
-    if (t->copy_in_flight) {
-        if ((e = hipEventSynchronize(t->staging_done)) != hipSuccess) return hip_fail(e, "plan_upload");
-        t->copy_in_flight = false;
+    Staging& st = t->staging[t->next_staging];
+    if (st.in_flight) {
+        if ((e = hipEventSynchronize(st.done)) != hipSuccess) return hip_fail(e, "plan_upload");
+        st.in_flight = false;
     }
-    if (!t->staging_done && (e = hipEventCreateWithFlags(&t->staging_done, hipEventDisableTiming)) != hipSuccess)
+    if (!st.done && (e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming)) != hipSuccess)
         return hip_fail(e, "plan_upload: event");
-    if (t->staging_words < words) {
-        if (t->staging) (void)hipHostFree(t->staging);
-        t->staging = nullptr;
-        t->staging_words = 0;
-        if ((e = hipHostMalloc(reinterpret_cast<void**>(&t->staging), words * sizeof(int32_t),
-                               hipHostMallocDefault)) != hipSuccess)
+    if (st.words < words) {
+        if (st.host) (void)hipHostFree(st.host);
+        st.host = nullptr;
+        st.dev = nullptr;
+        st.words = 0;
+        const size_t want = words + words / 2;        // room for the plan to grow
+        if ((e = hipHostMalloc(reinterpret_cast<void**>(&st.host), want * sizeof(int32_t),
+                               hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess)
             return hip_fail(e, "plan_upload: pinned staging");
-        t->staging_words = words;
+        void* dev = nullptr;
+        if ((e = hipHostGetDevicePointer(&dev, st.host, 0)) != hipSuccess) {
+            (void)hipHostFree(st.host);
+            st.host = nullptr;
+            return hip_fail(e, "plan_upload: staging mapping");
+        }
+        st.dev = static_cast<const int32_t*>(dev);
+        st.words = want;
     }
-    std::memcpy(t->staging + first, p.blob.data() + first, count * sizeof(int32_t));
+    std::memcpy(st.host + first, p.blob.data() + first, count * sizeof(int32_t));
     auto s = static_cast<hipStream_t>(stream);
-    if ((e = hipMemcpyAsync(static_cast<int32_t*>(d_meta) + first, t->staging + first,
-                            count * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess)
-        return hip_fail(e, "plan_upload: copy");
-    if ((e = hipEventRecord(t->staging_done, s)) != hipSuccess) return hip_fail(e, "plan_upload: record");
-    t->copy_in_flight = true;
+    if ((e = pkvt::launch_copy_words(st.dev + first, static_cast<int32_t*>(d_meta) + first,
+                                     static_cast<int64_t>(count), s)) != hipSuccess)
+        return hip_fail(e, "plan_upload: copy kernel");
+    if ((e = hipEventRecord(st.done, s)) != hipSuccess) return hip_fail(e, "plan_upload: record");
+    st.in_flight = true;
+    t->next_staging = (t->next_staging + 1) % kStagingRing;
     t->uploaded_ptr = d_meta;
     t->uploaded_serial = p.serial;
     t->uploaded_len_version = p.len_version;
@@ -376,6 +400,36 @@ pkvt_status pkvt_kv_scatter(const pkvt_tree* t, void* k_pool, void* v_pool, cons
     a.H = t->tree.H;
     hipError_t e = pkvt::launch_scatter(a, t->tree.D, t->tree.C, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_scatter");
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_kv_scatter_host_slots(const pkvt_tree* t, void* k_pool, void* v_pool,
+                                       const int64_t* slots, const void* k_new, const void* v_new,
+                                       int64_t n_tokens, void* stream) {
+    if (!t || n_tokens < 0 || n_tokens > PKVT_INLINE_SLOTS)
+        return fail(PKVT_ERR_INVALID_ARG, "kv_scatter_host_slots: need 0 <= n_tokens <= " +
+                                              std::to_string(PKVT_INLINE_SLOTS));
+    if (!shape_ok(t->tree.D, t->tree.C))
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE,
+                    "kv_scatter_host_slots: unsupported head_dim / chunk_size");
+    if (n_tokens == 0) return PKVT_OK;
+    if (!k_pool || !v_pool || !slots || !k_new || !v_new)
+        return fail(PKVT_ERR_INVALID_ARG, "kv_scatter_host_slots: NULL argument");
+    static_assert(PKVT_INLINE_SLOTS == pkvt::kInlineSlots, "inline slot capacity");
+    pkvt::ScatterArgs a{};
+    a.kpool = k_pool;
+    a.vpool = v_pool;
+    a.slots = nullptr;
+    a.knew = k_new;
+    a.vnew = v_new;
+    a.n_tokens = n_tokens;
+    a.slot_limit = static_cast<int64_t>(t->tree.N) * t->tree.C;
+    a.H = t->tree.H;
+    pkvt::InlineSlots is;
+    std::memcpy(is.slot, slots, static_cast<size_t>(n_tokens) * sizeof(int64_t));
+    hipError_t e = pkvt::launch_scatter_inline(a, is, t->tree.D, t->tree.C,
+                                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kv_scatter_host_slots");
     return PKVT_OK;
 }
 

@@ -51,7 +51,17 @@ struct ScatterArgs {
     int32_t H;
 };
 
+constexpr int kInlineSlots = 256;
+struct InlineSlots {
+    int64_t slot[kInlineSlots];
+};
+
 hipError_t launch_attn(const AttnArgs& a, int D, int C, hipStream_t s);
+// slots come from is.slot instead of a.slots (a.n_tokens <= kInlineSlots)
+hipError_t launch_scatter_inline(const ScatterArgs& a, const InlineSlots& is, int D, int C,
+                                 hipStream_t s);
+// dst[i] = src[i] for i < n; src may be a device-mapped host pointer
+hipError_t launch_copy_words(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int D, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, int D, int C, hipStream_t s);
 

@@ -291,10 +291,18 @@ class DecodeLoop:
         for j, slots in self.host.joins(t):
             self._join_kv(j, slots, stream)
         slots = self.host.append(t)
-        d = self._to_device(slots)
         b = self.tr.base.b
-        for l in range(ds.layers):
-            self._scatter(l, d, self.k[l][t], self.v[l][t], b, stream)
+        if b <= B.PKVT_INLINE_SLOTS:
+            # the slots travel in the scatter launches' arguments
+            for l in range(ds.layers):
+                B.pkvt_kv_scatter_host_slots(ds.tree, ds.k_pools[l].data_ptr(),
+                                             ds.v_pools[l].data_ptr(), slots,
+                                             self.k[l][t].data_ptr(), self.v[l][t].data_ptr(),
+                                             stream)
+        else:
+            d = self._to_device(slots)
+            for l in range(ds.layers):
+                self._scatter(l, d, self.k[l][t], self.v[l][t], b, stream)
         mb, wb = self.host.plan()
         if mb > self.meta.numel() * 4 or wb > self.ws.numel() * 4:
             self.regrow += 1

@@ -106,3 +106,42 @@ def test_decode_loop_long_prefix_sampled():
             worst = max(worst, _check(loop, tr, t, 1, rows=rows))
     print(f"[case]   rows {rows} worst err {worst:.3e} host counts {loop.host.count}", flush=True)
     ds.close()
+
+
+@pytest.mark.parametrize("d,c,n", [(128, 64, 64), (64, 16, 256), (128, 32, 1)])
+def test_scatter_host_slots_matches_device_slots(d, c, n):
+    """pkvt_kv_scatter_host_slots (slots in the launch arguments) writes the
+    same pool bytes as pkvt_kv_scatter (slots in device memory), skipping
+    -1 and out-of-pool entries alike."""
+    torch = _torch()
+    from prefix_shared_kv_tree_amd import binding as B
+    B.load()
+    h, pool = 3, 40
+    tree = B.pkvt_tree_create(h, d, c, pool)
+    try:
+        rng = np.random.default_rng(n)
+        slots = rng.choice(pool * c, size=n, replace=False).astype(np.int64)
+        slots[1::7] = -1
+        if n > 3:
+            slots[3] = pool * c + 5                      # outside the pool: skipped
+        kn = torch.from_numpy(rng.standard_normal((n, h, d), dtype=np.float32).astype(np.float16)).cuda()
+        vn = torch.from_numpy(rng.standard_normal((n, h, d), dtype=np.float32).astype(np.float16)).cuda()
+        elems = B.pkvt_pool_bytes(h, d, c, pool) // 2
+        pools = [torch.zeros(elems, dtype=torch.float16, device="cuda") for _ in range(4)]
+        stream = torch.cuda.current_stream().cuda_stream
+        sd = torch.from_numpy(slots).cuda()
+        B.pkvt_kv_scatter(tree, pools[0].data_ptr(), pools[1].data_ptr(), sd.data_ptr(),
+                          kn.data_ptr(), vn.data_ptr(), n, stream)
+        host = slots.copy()
+        B.pkvt_kv_scatter_host_slots(tree, pools[2].data_ptr(), pools[3].data_ptr(), host,
+                                     kn.data_ptr(), vn.data_ptr(), stream)
+        host[:] = -1                                     # reusable as soon as the call returns
+        torch.cuda.synchronize()
+        assert torch.equal(pools[0], pools[2]) and torch.equal(pools[1], pools[3])
+        assert int((pools[0] != 0).sum()) > 0
+        with pytest.raises(B.PkvtError):
+            B.pkvt_kv_scatter_host_slots(tree, pools[2].data_ptr(), pools[3].data_ptr(),
+                                         np.zeros(B.PKVT_INLINE_SLOTS + 1, np.int64),
+                                         kn.data_ptr(), vn.data_ptr(), stream)
+    finally:
+        B.pkvt_tree_destroy(tree)
