@@ -487,6 +487,80 @@ def decode_loop(args, name, layers, static_us_layer):
     return res
 
 
+# ChunkAttention page, Knowl 8 (b = 32, c = 64, fp16, A100): decode throughput in
+# 10^3 tokens/s while completions of n_c tokens grow after n_s shared prompt
+# tokens -- (ChunkAttn, PagedAttn).  Context only: other hardware.
+PAGE_DIVERGENCE = {
+    (1024, 256): (241.93, 76.35), (1024, 512): (186.44, 69.15), (1024, 1024): (127.85, 58.12),
+    (2048, 512): (145.41, 39.85), (2048, 1024): (107.37, 36.18), (2048, 2048): (70.33, 30.17),
+    (4096, 512): (101.69, 21.04), (4096, 4096): (37.05, 15.12),
+}
+# Knowl 9 (n_s = 2048, n_c = 64): ChunkAttn 10^3 tokens/s at the two ends of b in [16, 96].
+PAGE_BATCH = {16: 155.0, 96: 224.0}
+
+
+def sweep_time(torch, B, W, b, n_s, private, seed, variant, steps, warmup, ev):
+    """µs per layer of one decode batch: b sequences sharing n_s prompt
+    tokens, each with `private` tokens of its own (h = 32, d = 128, c = 64),
+    K/V and Q drawn on the device; steps rotate over enough layer pools to
+    defeat the Infinity Cache."""
+    from prefix_shared_kv_tree_amd.harness import DecodeSetup
+    w = W.one_prefix(seed, b, n_s, private, h=32, d=128, c=64, with_kv=False)
+    b_tok = w.h * w.d * 2 * 2
+    unique = (n_s + b * private) * b_tok
+    layers = max(2, math.ceil(2 * 2 ** 30 / unique))
+    ds = DecodeSetup(w, layers=layers, device_random_seed=seed,
+                     min_share=(1 << 20) if variant == "plain" else 0)
+    stream = torch.cuda.current_stream().cuda_stream
+    total_ms, _, _, _ = time_region(ds, B, ev, stream, steps, warmup, per_kernel=False)
+    info = dict(ds.info)
+    ds.close()
+    del ds
+    return total_ms / steps * 1e3, info, unique
+
+
+def run_sweep(args):
+    """Knowl 8 (divergence) and Knowl 9 (batch) shapes.  A point's
+    throughput is b / (mean step latency while the completions grow from 0
+    to n_c tokens); the mean is taken with the midpoint rule over 4 equal
+    panels of n_c (private lengths n_c/8, 3n_c/8, 5n_c/8, 7n_c/8), exact for a
+    latency affine in the context length."""
+    import torch
+    from prefix_shared_kv_tree_amd import binding as B
+    from prefix_shared_kv_tree_amd import workloads as W
+    B.load()
+    ev = HipEvents()
+    if args.sweep == "divergence":
+        grid = [(32, n_s, n_c) for n_s, n_c in sorted(PAGE_DIVERGENCE)]
+        grid += [(32, n_s, 0) for n_s in (1024, 2048, 4096)]
+    else:
+        grid = [(b, 2048, 64) for b in (16, 32, 48, 64, 80, 96)]
+    points = []
+    for i, (b, n_s, n_c) in enumerate(grid):
+        privs = [max(1, (2 * k + 1) * n_c // 8) for k in range(4)] if n_c else [1]
+        row = {"b": b, "n_s": n_s, "n_c": n_c, "private_tokens": privs}
+        for variant in ("tpp", "plain"):
+            us = []
+            for k, p in enumerate(privs):
+                t, info, _ = sweep_time(torch, B, W, b, n_s, p, 3000 + 10 * i + k, variant,
+                                        args.sweep_steps, 10, ev)
+                us.append(t)
+            mean_us = float(np.mean(us))
+            row[f"{variant}_us_per_layer"] = [round(x, 2) for x in us]
+            row[f"{variant}_ktok_per_s"] = round(b / (mean_us * 1e-6) / 1e3, 2)
+        row["speedup"] = round(row["tpp_ktok_per_s"] / row["plain_ktok_per_s"], 3)
+        page = PAGE_DIVERGENCE.get((n_s, n_c)) if args.sweep == "divergence" else None
+        if page:
+            row["page_a100_ktok_per_s"] = {"chunkattn": page[0], "pagedattn": page[1]}
+        if args.sweep == "batch" and b in PAGE_BATCH:
+            row["page_a100_ktok_per_s"] = {"chunkattn": PAGE_BATCH[b]}
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        points.append(row)
+    print(json.dumps({"sweep": args.sweep, "h": 32, "d": 128, "c": 64, "dtype": "f16",
+                      "data": "synthetic, device N(0,1)", "steps_per_point": args.sweep_steps,
+                      "points": points}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -522,6 +596,10 @@ def main():
     ap.add_argument("--loop-churn", type=int, default=16,
                     help="a row gets a new sequence every this many decode-loop steps")
     ap.add_argument("--no-loop", action="store_true")
+    ap.add_argument("--sweep", choices=["divergence", "batch"],
+                    help="time the decode-throughput sweeps of the pages' divergence (Knowl 8) "
+                         "or batch-size (Knowl 9) experiments instead of the benchmark")
+    ap.add_argument("--sweep-steps", type=int, default=60)
     ap.add_argument("--loop-only", action="store_true",
                     help="run only the decode loop (for profiling it)")
     args = ap.parse_args()
@@ -547,6 +625,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     B.load()
+    if args.sweep:
+        run_sweep(args)
+        return
 
     probe = W.make_config(args.config, with_kv=False)
     b_tok = probe.h * probe.d * 2 * 2

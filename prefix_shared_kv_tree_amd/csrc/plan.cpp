@@ -48,6 +48,22 @@ int32_t steps_to_chunks(int64_t steps, int32_t C) {
 
 struct Range { int32_t i = 0, j = 0; };
 
+// Row blocks of a phase-1 item with n_rows rows: blocks of kRowsPerUnit and
+// the remainder, except that a remainder too small for a workgroup unit is
+// avoided by cutting the rows into equal blocks when those are all large
+// enough (80 rows: 40 + 40 rather than 64 + a 16-row single-wave task).
+std::vector<int32_t> row_blocks(int32_t n_rows, int32_t unit_rows) {
+    std::vector<int32_t> out;
+    const int32_t k = (n_rows + kRowsPerUnit - 1) / kRowsPerUnit;
+    const int32_t rem = n_rows % kRowsPerUnit;
+    if (k > 1 && rem != 0 && rem < unit_rows && n_rows / k >= unit_rows) {
+        for (int32_t i = 0; i < k; ++i) out.push_back(n_rows / k + (i < n_rows % k ? 1 : 0));
+        return out;
+    }
+    for (int32_t r0 = 0; r0 < n_rows; r0 += kRowsPerUnit) out.push_back(std::min(kRowsPerUnit, n_rows - r0));
+    return out;
+}
+
 // The lanes of one speed class, ordered by (load, lane).  The balancer only
 // ever takes the first lane and puts it back with a larger load, so the
 // class minimum never decreases: lanes sit in a ring of buckets, one per
@@ -321,8 +337,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         for (size_t s = 0; s < segs.size(); ++s) {
             const int64_t st = steps_of(static_cast<int64_t>(segs[s].size()) * t.C);
             const int32_t rows = seg_range[s].j - seg_range[s].i;
-            for (int32_t r0 = 0; r0 < rows; r0 += kRowsPerUnit) {
-                const int32_t rb = std::min(kRowsPerUnit, rows - r0);
+            for (const int32_t rb : row_blocks(rows, opts.unit_rows)) {
                 if (rb >= opts.unit_rows)
                     quarters += kWavesPerWg * kUnitStepCost * st;
                 else
@@ -436,7 +451,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         wave_cost.push_back(task_cost(item_keys(it)));
         return static_cast<int32_t>(waves.size()) - 1;
     };
-    // Phase-1 rows are cut into blocks of kRowsPerUnit.  A block of at least
+    // Phase-1 rows are cut into blocks of up to kRowsPerUnit.  A block of at least
     // unit_rows rows (default: more than one row group) becomes one workgroup
     // unit per head, in which the 4 waves split every step's loads and share
     // the data through LDS.  Smaller blocks are cut into single-wave tasks of
@@ -446,13 +461,14 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     std::vector<int32_t> singles;            // single-wave tasks (x heads)
     for (const Item& it : items1) {
         const int32_t keys = static_cast<int32_t>(item_keys(it));
-        for (int32_t r0 = 0; r0 < it.n_rows; r0 += kRowsPerUnit) {
-            const int32_t rb = std::min(kRowsPerUnit, it.n_rows - r0);
+        int32_t r0 = 0;
+        for (const int32_t rb : row_blocks(it.n_rows, opts.unit_rows)) {
             if (rb < opts.unit_rows) {
                 for (int32_t r = r0; r < r0 + rb; r += kRowsPerWave) singles.push_back(add_wave(it, r));
-                continue;
+            } else {
+                for (int32_t h = 0; h < t.H; ++h) units.push_back({&it, r0, rb, h, keys, unit_cost(keys)});
             }
-            for (int32_t h = 0; h < t.H; ++h) units.push_back({&it, r0, rb, h, keys, unit_cost(keys)});
+            r0 += rb;
         }
     }
     for (const Item& it : items2) singles.push_back(add_wave(it, 0));

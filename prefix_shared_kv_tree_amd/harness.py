@@ -50,7 +50,11 @@ class DecodeSetup:
 
     def __init__(self, w, layers: Optional[int] = None, pool_slack: int = 0, device: str = "cuda",
                  phase1_chunks: int = 0, phase2_chunks: int = 0, min_share: int = 0,
-                 pool_chunks: Optional[int] = None, unit_rows: int = 0):
+                 pool_chunks: Optional[int] = None, unit_rows: int = 0,
+                 device_random_seed: Optional[int] = None):
+        """``device_random_seed``: instead of the workload's K/V (which may
+        then be absent), fill the pools and Q with N(0,1) fp16 drawn on the
+        device (for timing sweeps that need no oracle)."""
         import torch
         self.torch = torch
         self.w = w
@@ -68,9 +72,19 @@ class DecodeSetup:
         self.k_pools: List = []
         self.v_pools: List = []
         stream = torch.cuda.current_stream().cuda_stream
+        gen = None
+        if device_random_seed is not None:
+            gen = torch.Generator(device=device)
+            gen.manual_seed(device_random_seed)
         for layer in range(self.layers):
             kp = torch.empty(pool_elems, dtype=torch.float16, device=device)
             vp = torch.empty(pool_elems, dtype=torch.float16, device=device)
+            if gen is not None:
+                kp.normal_(generator=gen)
+                vp.normal_(generator=gen)
+                self.k_pools.append(kp)
+                self.v_pools.append(vp)
+                continue
             k_new, v_new, s_new = gather_new_tokens(w, self.slots, layer)
             if s_new.size:
                 kd = torch.from_numpy(np.ascontiguousarray(k_new)).to(device)
@@ -82,7 +96,10 @@ class DecodeSetup:
                 del kd, vd, sd
             self.k_pools.append(kp)
             self.v_pools.append(vp)
-        self.q = torch.from_numpy(np.ascontiguousarray(w.q)).to(device)
+        if gen is not None:
+            self.q = torch.empty(w.q.shape, dtype=torch.float16, device=device).normal_(generator=gen)
+        else:
+            self.q = torch.from_numpy(np.ascontiguousarray(w.q)).to(device)
         self.out = torch.empty_like(self.q)
         self.scale = 1.0 / math.sqrt(w.d)
         self.replan(phase1_chunks, phase2_chunks, min_share, unit_rows=unit_rows)

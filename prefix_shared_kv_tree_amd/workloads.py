@@ -240,14 +240,18 @@ def random_tree(seed: int, h: int = 2, d: int = 16, c: int = 4, max_b: int = 6,
 
 
 def one_prefix(seed: int, b: int, prefix: int, suffix, h: int = 2, d: int = 64, c: int = 16,
-               layers: int = 1) -> Workload:
+               layers: int = 1, with_kv: bool = True) -> Workload:
     """b sequences that share one prefix of ``prefix`` tokens, each followed
     by a private suffix (``suffix`` tokens, or a list of b lengths)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     suf = [int(suffix)] * b if np.isscalar(suffix) else [int(x) for x in suffix]
-    seg_lens = [prefix] + suf
-    paths = [[0, 1 + u] if suf[u] > 0 else [0] for u in range(b)]
-    return _finish(f"one_prefix{b}x{prefix}", rng, h, d, c, seg_lens, paths, layers)
+    seg_lens = ([prefix] if prefix > 0 else []) + suf
+    if prefix > 0:
+        paths = [[0, 1 + u] if suf[u] > 0 else [0] for u in range(b)]
+    else:
+        paths = [[u] for u in range(b)]
+    return _finish(f"one_prefix{b}x{prefix}", rng, h, d, c, seg_lens, paths, layers,
+                   with_kv=with_kv)
 
 
 def layered_tree(seed: int, b: int, n_roots: int, h: int = 2, d: int = 64, c: int = 16,

@@ -397,3 +397,27 @@ def test_plan_refresh_after_length_only_append():
     B.pkvt_tree_append(box.t, [ids[0]] * 3, [9, 10, 11])   # fills [5,8,9,10], opens [11]
     B.pkvt_plan(box.t, ids)
     assert B.pkvt_plan_info_get(box.t)["structure_version"] != v0
+
+
+@pytest.mark.parametrize("rows,unit_rows,want_units,want_single_rows", [
+    (80, 0, [40, 40], []),           # 64 + 16 would leave a 16-row single-wave task
+    (65, 0, [33, 32], []),
+    (96, 0, [64, 32], []),           # the 32-row remainder is a unit already
+    (130, 0, [44, 43, 43], []),      # not 64 + 64 + a 2-row single-wave task
+    (150, 0, [64, 64, 22], []),      # the 22-row remainder is a unit already
+    (70, 40, [64], [6]),             # equal blocks of 35 would be below unit_rows
+    (64, 0, [64], []),
+    (16, 0, [], [16]),
+])
+def test_phase1_row_blocks(rows, unit_rows, want_units, want_single_rows):
+    """How the rows of one shared prefix are cut into workgroup units (17..64
+    rows) and single-wave tasks (<= 16 rows)."""
+    w = W.one_prefix(9, rows, 8, 0, h=1, d=64, c=4, with_kv=False)
+    box = TreeBox(h=1, c=4, n=4096)
+    ids, _ = B.pkvt_tree_build(box.t, w.all_seq_tokens())
+    plan = _plan_and_check(box, ids, phase1_chunks=2, unit_rows=unit_rows)
+    got_units = sorted((int(u[5]) for u in plan["units"]), reverse=True)
+    shared = [i for i, ch in enumerate(plan["wave_chunks"]) if len(ch) and
+              all(B.pkvt_tree_chunk_refcount(box.t, int(x)) > 1 for x in ch)]
+    assert sorted(want_units, reverse=True) == got_units    # one item: 8 tokens = 2 chunks
+    assert sorted(int(plan["waves"][i][5]) for i in shared) == sorted(want_single_rows)

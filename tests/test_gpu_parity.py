@@ -239,3 +239,23 @@ def test_decode_append_and_lazy_upload():
         err = _err(got, A.attention_batch(w))
         assert err <= TOL, (step, err)
     ds.close()
+
+
+@pytest.mark.parametrize("b,n_s,private", [(96, 2048, 56), (16, 2048, 8), (32, 1024, 1),
+                                           (32, 4096, 960), (80, 2048, 40)])
+@pytest.mark.parametrize("variant", ["tpp", "plain"])
+def test_sweep_shapes_sampled(b, n_s, private, variant):
+    """Full-size points of the divergence and batch sweeps (h = 32, d = 128,
+    c = 64; b sequences sharing n_s prompt tokens plus `private` tokens
+    each): sampled rows against the oracle."""
+    _torch()
+    print(f"\n[case] sweep shape b={b} n_s={n_s} private={private} {variant}", flush=True)
+    w = W.one_prefix(4000 + b + n_s + private, b, n_s, private, h=32, d=128, c=64)
+    ds = _setup(w, min_share=(1 << 20) if variant == "plain" else 0)
+    got = _run(ds)
+    rows = sorted({0, b // 3, b // 2 + 1, b - 1})
+    ref = A.attention_batch(w, seqs=rows)
+    err = _err(got[rows], ref[rows])
+    print(f"[case]   rows {rows} err={err:.3e} info={ds.info}", flush=True)
+    assert err <= TOL
+    ds.close()
