@@ -499,15 +499,15 @@ PAGE_DIVERGENCE = {
 PAGE_BATCH = {16: 155.0, 96: 224.0}
 
 
-def sweep_time(torch, B, W, b, n_s, private, seed, variant, steps, warmup, ev):
+def sweep_time(torch, B, W, b, n_s, private, seed, variant, steps, warmup, ev, h=32, d=128, c=64):
     """µs per layer of one decode batch: b sequences sharing n_s prompt
-    tokens, each with `private` tokens of its own (h = 32, d = 128, c = 64),
-    K/V and Q drawn on the device; steps rotate over enough layer pools to
-    defeat the Infinity Cache."""
+    tokens, each with `private` tokens of its own (a count, or one per
+    sequence), K/V and Q drawn on the device; steps rotate over enough layer
+    pools to defeat the Infinity Cache."""
     from prefix_shared_kv_tree_amd.harness import DecodeSetup
-    w = W.one_prefix(seed, b, n_s, private, h=32, d=128, c=64, with_kv=False)
+    w = W.one_prefix(seed, b, n_s, private, h=h, d=d, c=c, with_kv=False)
     b_tok = w.h * w.d * 2 * 2
-    unique = (n_s + b * private) * b_tok
+    unique = (n_s + int(np.sum(np.broadcast_to(private, (b,))))) * b_tok
     layers = max(2, math.ceil(2 * 2 ** 30 / unique))
     ds = DecodeSetup(w, layers=layers, device_random_seed=seed,
                      min_share=(1 << 20) if variant == "plain" else 0)
@@ -530,6 +530,30 @@ def run_sweep(args):
     from prefix_shared_kv_tree_amd import workloads as W
     B.load()
     ev = HipEvents()
+    if args.sweep == "shapes":
+        # the long-shared-prompt batch (b = 64, 4096 shared tokens, private
+        # suffixes uniform in [256, 1024]) at every supported head_dim and
+        # chunk size, with h * d = 4096 so that a token's K/V bytes stay fixed
+        rng = np.random.Generator(np.random.PCG64(1002))
+        priv = [int(x) for x in rng.integers(256, 1025, size=64)]
+        points = []
+        for d in (64, 128, 256):
+            for c in (16, 32, 64, 128):
+                row = {"d": d, "c": c, "h": 4096 // d}
+                for variant in ("tpp", "plain"):
+                    t, info, unique = sweep_time(torch, B, W, 64, 4096, priv, 3100 + d + c, variant,
+                                                 args.sweep_steps, 10, ev, h=4096 // d, d=d, c=c)
+                    row[f"{variant}_us_per_layer"] = round(t, 2)
+                    if variant == "tpp":
+                        row["effective_gbps"] = round(unique / (t * 1e-6) / 1e9, 1)
+                        row["frac_hbm_peak"] = round(unique / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                row["speedup"] = round(row["plain_us_per_layer"] / row["tpp_us_per_layer"], 3)
+                print(json.dumps(row), file=sys.stderr, flush=True)
+                points.append(row)
+        print(json.dumps({"sweep": "shapes", "b": 64, "n_s": 4096, "private": "uniform [256, 1024]",
+                          "dtype": "f16", "data": "synthetic, device N(0,1)",
+                          "steps_per_point": args.sweep_steps, "points": points}), flush=True)
+        return
     if args.sweep == "divergence":
         grid = [(32, n_s, n_c) for n_s, n_c in sorted(PAGE_DIVERGENCE)]
         grid += [(32, n_s, 0) for n_s in (1024, 2048, 4096)]
@@ -596,7 +620,7 @@ def main():
     ap.add_argument("--loop-churn", type=int, default=16,
                     help="a row gets a new sequence every this many decode-loop steps")
     ap.add_argument("--no-loop", action="store_true")
-    ap.add_argument("--sweep", choices=["divergence", "batch"],
+    ap.add_argument("--sweep", choices=["divergence", "batch", "shapes"],
                     help="time the decode-throughput sweeps of the pages' divergence (Knowl 8) "
                          "or batch-size (Knowl 9) experiments instead of the benchmark")
     ap.add_argument("--sweep-steps", type=int, default=60)

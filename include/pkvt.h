@@ -30,7 +30,7 @@
  *   - Mutating calls that fail leave the tree exactly as it was.
  *
  * Shapes: n_heads h (query heads == KV heads), all tensors fp16 (IEEE
- * binary16).  The kernels support head_dim d in {64, 128} and chunk_size c
+ * binary16).  The kernels support head_dim d in {64, 128, 256} and chunk_size c
  * in {16, 32, 64, 128}; the host tree and planner accept any c in [1, 4096]
  * and d >= 1, and the device entry points (pkvt_pool_bytes, pkvt_kv_scatter,
  * pkvt_plan_upload, pkvt_attn_decode) return UNSUPPORTED_SHAPE otherwise.

@@ -60,8 +60,18 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;          // waves per workgroup
-constexpr int kStep = 64;          // keys per step of the streaming loop
 constexpr int kVPad = 128;         // LDS padding after each 4-key group of a V image
+
+// Keys per step of the streaming loop: 4 tiles of 16 keys up to head_dim
+// 128; one tile at head_dim 256, where a step of K and V in registers next
+// to the 64 accumulator registers of O^T would not fit otherwise (16 KiB of
+// K and V per wave per step).  With one tile the P V product takes the
+// 16-key form of the matrix instruction.
+template <int D>
+struct Step {
+    static constexpr int kTiles = D <= 128 ? 4 : 1;
+    static constexpr int kKeys = 16 * kTiles;
+};
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -81,8 +91,9 @@ __device__ __forceinline__ cint* meta(const int32_t* p) { return (cint*)(p); }
 // makes it wait for everything); a tile past the end re-reads the last valid
 // tile -- same addresses, so no extra HBM traffic -- and its scores are
 // forced to -inf and its V entries zeroed by softmax_pv.
+template <int D>
 __device__ __forceinline__ int tile_start(int step, int tt, int n_valid) {
-    const int key = step * kStep + 16 * tt;
+    const int key = step * Step<D>::kKeys + 16 * tt;
     const int last = (n_valid - 1) & ~15;
     return key < last ? key : last;
 }
@@ -98,16 +109,16 @@ __device__ __forceinline__ int lane_ids(cint* chunks, int n_chunks, int lane) {
     return lane < n_chunks ? chunks[lane] : 0;
 }
 
-template <int C>
+template <int D, int C>
 __device__ __forceinline__ int tile_id(int ids, int step, int tt, int n_valid) {
-    return __builtin_amdgcn_readlane(ids, min((step * kStep + 16 * tt) / C, (n_valid - 1) / C));
+    return __builtin_amdgcn_readlane(ids, min((step * Step<D>::kKeys + 16 * tt) / C, (n_valid - 1) / C));
 }
 
-// S^T = K Q^T for the 64 keys of a step: tile tt = keys 16tt .. 16tt+15.
-template <int KS>
-__device__ __forceinline__ void qk(f4 (&s)[4], const h8 (&kr)[4][KS], const h8 (&qb)[KS]) {
+// S^T = K Q^T for the keys of a step: tile tt = keys 16tt .. 16tt+15.
+template <int NT, int KS>
+__device__ __forceinline__ void qk(f4 (&s)[NT], const h8 (&kr)[NT][KS], const h8 (&qb)[KS]) {
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < NT; ++tt) {
         s[tt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -117,17 +128,18 @@ __device__ __forceinline__ void qk(f4 (&s)[4], const h8 (&kr)[4][KS], const h8 (
 
 // Online softmax of one step (partial_attn) folded into the running state
 // (attn_reduce): lane (col, grp) holds the scores of query row col for keys
-// 16tt + 4grp + i.  Returns P^T as two fp16 B operands (keys of tiles
-// 2hs, 2hs+1) and rescales o to the new running max.
-template <int DT>
-__device__ __forceinline__ void softmax_step(f4 (&s)[4], h8 (&pb)[2], f4 (&o)[DT], float& m_run,
+// 16tt + 4grp + i.  Returns P^T in fp16, pq[tt] = keys 16tt + 4grp .. +3 of
+// row col (the B-operand layout of the P V product), and rescales o to the
+// new running max.
+template <int NT, int DT>
+__device__ __forceinline__ void softmax_step(f4 (&s)[NT], h4 (&pq)[NT], f4 (&o)[DT], float& m_run,
                                              float& l_run, int step, int n_valid, int grp,
                                              float scale_log2e) {
-    const int key0 = step * kStep;
-    const bool tail = key0 + kStep > n_valid;
+    const int key0 = step * 16 * NT;
+    const bool tail = key0 + 16 * NT > n_valid;
     float mx = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float x = s[tt][i] * scale_log2e;
@@ -143,9 +155,9 @@ __device__ __forceinline__ void softmax_step(f4 (&s)[4], h8 (&pb)[2], f4 (&o)[DT
     m_run = m_new;
     float lsum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 4 * NT; ++e) {
         const _Float16 p = static_cast<_Float16>(fast_exp2(s[e >> 2][e & 3] - m_new));
-        pb[e >> 3][e & 7] = p;
+        pq[e >> 2][e & 3] = p;
         lsum += static_cast<float>(p);
     }
     l_run = l_run * alpha + lsum;
@@ -162,34 +174,42 @@ __device__ __forceinline__ h4 mask_v(h4 v, int key, int n_valid) {
     return __builtin_bit_cast(h4, __builtin_bit_cast(unsigned long long, v) & mk);
 }
 
-// O^T += V^T P^T for one 16-dim tile: v[hs][*] holds V of dim 16dt + col for
-// the keys of tiles 2hs and 2hs+1 that the lane's P covers.
-__device__ __forceinline__ f4 pv_tile(f4 o, const h4 (&v)[2][2], const h8 (&pb)[2]) {
+// O^T += V^T P^T for one 16-dim tile: v[tt] holds V of dim 16dt + col for
+// the keys of tile tt that the lane's P covers (16tt + 4grp .. +3).  Pairs of
+// tiles go through the 32-key instruction (the key order inside a pair is
+// permuted alike in both operands); a single tile through the 16-key one.
+template <int NT>
+__device__ __forceinline__ f4 pv_tile(f4 o, const h4 (&v)[NT], const h4 (&pq)[NT]) {
+    if constexpr (NT == 1) {
+        o = __builtin_amdgcn_mfma_f32_16x16x16f16(v[0], pq[0], o, 0, 0, 0);
+    } else {
 #pragma unroll
-    for (int hs = 0; hs < 2; ++hs) {
-        const h8 va = __builtin_shufflevector(v[hs][0], v[hs][1], 0, 1, 2, 3, 4, 5, 6, 7);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[hs], o, 0, 0, 0);
+        for (int hs = 0; hs < NT / 2; ++hs) {
+            const h8 va = __builtin_shufflevector(v[2 * hs], v[2 * hs + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const h8 pb = __builtin_shufflevector(pq[2 * hs], pq[2 * hs + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o, 0, 0, 0);
+        }
     }
     return o;
 }
 
 // softmax_step, then the PV product with a whole step of V in registers.
-template <int DT>
-__device__ __forceinline__ void softmax_pv(f4 (&s)[4], h4 (&vr)[DT][2][2], f4 (&o)[DT],
+template <int NT, int DT>
+__device__ __forceinline__ void softmax_pv(f4 (&s)[NT], h4 (&vr)[DT][NT], f4 (&o)[DT],
                                            float& m_run, float& l_run, int step, int n_valid,
                                            int grp, float scale_log2e) {
-    h8 pb[2];
-    softmax_step<DT>(s, pb, o, m_run, l_run, step, n_valid, grp, scale_log2e);
-    const int key0 = step * kStep;
-    if (key0 + kStep > n_valid) {
+    h4 pq[NT];
+    softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, n_valid, grp, scale_log2e);
+    const int key0 = step * 16 * NT;
+    if (key0 + 16 * NT > n_valid) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-                vr[dt][tt >> 1][tt & 1] = mask_v(vr[dt][tt >> 1][tt & 1], key0 + 16 * tt + 4 * grp, n_valid);
+                vr[dt][tt] = mask_v(vr[dt][tt], key0 + 16 * tt + 4 * grp, n_valid);
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = pv_tile(o[dt], vr[dt], pb);
+    for (int dt = 0; dt < DT; ++dt) o[dt] = pv_tile<NT>(o[dt], vr[dt], pq);
 }
 
 // End of a task for query row col (lane group grp holds dims 16dt + 4grp ..):
@@ -229,10 +249,11 @@ __device__ __forceinline__ void finish(const AttnArgs& a, const f4 (&o)[DT], flo
 // then V as [tile][4-key group][d][4] with kVPad bytes after every group.
 template <int D>
 struct Img {
-    static constexpr int kBytesK = kStep * D * 2;
+    static constexpr int kBytesK = Step<D>::kKeys * D * 2;
     static constexpr int kGroupV = D * 8 + kVPad;
-    static constexpr int kBytes = kBytesK + (kStep / 4) * kGroupV;
-    static constexpr int kPieces = 16 * D;        // 16-byte pieces of K and V together
+    static constexpr int kBytes = kBytesK + (Step<D>::kKeys / 4) * kGroupV;
+    static constexpr int kPiecesK = kBytesK / 16;         // 16-byte pieces of K (2D per tile)
+    static constexpr int kPieces = 2 * kPiecesK;          // ... of K and V together
 };
 
 // One workgroup unit: query rows [row_lo, row_lo + n_rows) of one head.
@@ -242,10 +263,13 @@ struct Img {
 // passes the same number of barriers.
 template <int D, int C>
 __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, int lane, char* img) {
-    constexpr int KS = D / 32, DT = D / 16;
+    constexpr int KS = D / 32, DT = D / 16, NT = Step<D>::kTiles;
     constexpr int kPer = Img<D>::kPieces / kWaves;   // pieces per wave per step
     constexpr int NL = kPer / 64;                    // 16-byte loads per lane per step
-    static_assert(kPer % 64 == 0 && (2 * D) % 64 == 0, "piece split");
+    constexpr int KP = Img<D>::kPiecesK;
+    constexpr int TPW = kPer >= 2 * D ? kPer / (2 * D) : 1;   // tiles a wave loads per step
+    static_assert(kPer % 64 == 0 && (2 * D) % 64 == 0 && (kPer % (2 * D) == 0 || NT == 1) &&
+                  NL % TPW == 0, "piece split");
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int H = a.H;
@@ -257,29 +281,31 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
     const int out = u[6];
     const int role = wave;
     const bool computes = 16 * role < n_rows;
-    const int n_steps = (n_keys + kStep - 1) / kStep;
+    const int n_steps = (n_keys + Step<D>::kKeys - 1) / Step<D>::kKeys;
     const size_t slice = static_cast<size_t>(C) * D * 2;      // bytes per (chunk, head)
     const char* kbase = static_cast<const char*>(a.kpool) + static_cast<size_t>(head) * slice;
     const char* vbase = static_cast<const char*>(a.vpool) + static_cast<size_t>(head) * slice;
     const size_t cstride = static_cast<size_t>(H) * slice;    // bytes per chunk
 
     h8 stg[NL];
-    // piece j of the image: K pieces [0, 8D) as (tile, d/8 piece, key), then
-    // V pieces [8D, 16D) as (tile, byte offset / 16 in the tile's V block)
-    // A wave's pieces cover two tiles, ta and ta + 1 (of K for waves 0-1, of
-    // V for waves 2-3); loads i < NL/2 fall in tile ta.
-    const int ta = 2 * (role & 1);
+    // piece j of the image: K pieces [0, KP) as (tile, d/8 piece, key), then
+    // V pieces [KP, 2 KP) as (tile, byte offset / 16 in the tile's V block)
+    // A wave's pieces cover TPW tiles from ta on (of K for waves 0-1, of V
+    // for waves 2-3); load i falls in tile ta + i / (NL / TPW).  With one
+    // tile per step every wave loads a part of tile 0.
+    const int ta = NT == 1 ? 0 : TPW * (role & 1);
     auto stage = [&](int step) {
-        const int id_a = tile_id<C>(ids, step, ta, n_keys);
-        const int id_b = tile_id<C>(ids, step, ta + 1, n_keys);
+        int id[TPW];
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) id[k] = tile_id<D, C>(ids, step, ta + k, n_keys);
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int j0 = role * kPer + i * 64;                   // wave-uniform
-            const bool is_k = j0 < 8 * D;
-            const int jj = is_k ? j0 : j0 - 8 * D;
-            const int ts = tile_start(step, jj / (2 * D), n_keys);
+            const bool is_k = j0 < KP;
+            const int jj = is_k ? j0 : j0 - KP;
+            const int ts = tile_start<D>(step, jj / (2 * D), n_keys);
             const int rem = jj % (2 * D) + lane;
-            const size_t cbytes = static_cast<size_t>(i < NL / 2 ? id_a : id_b) * cstride;
+            const size_t cbytes = static_cast<size_t>(id[i / (NL / TPW)]) * cstride;
             const char* kp = kbase + cbytes + (static_cast<size_t>(rem >> 4) * C + ts % C + (rem & 15)) * 16;
             const char* vp = vbase + cbytes + static_cast<size_t>((ts % C) / 4) * (D * 8) + rem * 16;
             stg[i] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(is_k ? kp : vp));
@@ -289,12 +315,12 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int j = role * kPer + i * 64 + lane;
-            const int jv = j - 8 * D;
+            const int jv = j - KP;
             const int tt = jv / (2 * D);
             const int rem = jv % (2 * D);
             const int voff = Img<D>::kBytesK + (tt * 4 + rem / (D / 2)) * Img<D>::kGroupV +
                              (rem % (D / 2)) * 16;
-            *reinterpret_cast<h8*>(img + (j < 8 * D ? j * 16 : voff)) = stg[i];
+            *reinterpret_cast<h8*>(img + (j < KP ? j * 16 : voff)) = stg[i];
         }
     };
 
@@ -323,9 +349,9 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
         if (computes) {
             // fragments are read from LDS tile by tile, next to the MFMAs
             // that use them, to keep register pressure low
-            f4 s[4];
+            f4 s[NT];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
+            for (int tt = 0; tt < NT; ++tt) {
                 s[tt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -334,18 +360,18 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
                     s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qb[ks], s[tt], 0, 0, 0);
                 }
             }
-            h8 pb[2];
-            softmax_step<DT>(s, pb, o, m_run, l_run, step, n_keys, grp, a.scale_log2e);
+            h4 pq[NT];
+            softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, n_keys, grp, a.scale_log2e);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                h4 v[2][2];
+                h4 v[NT];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-                    v[tt >> 1][tt & 1] = mask_v(
+                for (int tt = 0; tt < NT; ++tt)
+                    v[tt] = mask_v(
                         *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
                                                      (tt * 4 + grp) * Img<D>::kGroupV + (16 * dt + col) * 8),
-                        step * kStep + 16 * tt + 4 * grp, n_keys);
-                o[dt] = pv_tile(o[dt], v, pb);
+                        step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+                o[dt] = pv_tile<NT>(o[dt], v, pq);
             }
         }
     }
@@ -356,14 +382,14 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 struct Task {
     int ids;                 // the task's chunk ids, one per lane (lane_ids)
     int n_valid;             // keys to attend over
-    int n_steps;             // ceil(n_valid / 64)
+    int n_steps;             // ceil(n_valid / keys per step)
     int row_lo;              // depth-first position of query row 0
     int n_rows;
     int out;                 // partial slot of row 0, or -1: write O
     int head;
 };
 
-template <int C>
+template <int D, int C>
 __device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
     cint* tk = meta(a.tasks) + 2 * idx;
     const int wave_id = tk[0];
@@ -380,7 +406,7 @@ __device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
     int n_valid = n_chunks * C;
     if (len_row >= 0) n_valid = min(n_valid, meta(a.seqlen)[len_row] - key_base);
     t.n_valid = n_valid;
-    t.n_steps = (n_valid + kStep - 1) / kStep;
+    t.n_steps = (n_valid + Step<D>::kKeys - 1) / Step<D>::kKeys;
     return t;
 }
 
@@ -390,6 +416,7 @@ void attn_kernel(AttnArgs a) {
     static_assert(D % 32 == 0 && C % 16 == 0, "tile shape");
     constexpr int KS = D / 32;     // 32-dim k-steps of Q K^T
     constexpr int DT = D / 16;     // 16-dim output tiles of P V
+    constexpr int NT = Step<D>::kTiles;
     __shared__ __attribute__((aligned(16))) char lds[Img<D>::kBytes];
     const int H = a.H;
     const int wave = wave_uniform(threadIdx.x >> 6);
@@ -415,9 +442,9 @@ void attn_kernel(AttnArgs a) {
     const _Float16* __restrict__ kpool = static_cast<const _Float16*>(a.kpool);
     const _Float16* __restrict__ vpool = static_cast<const _Float16*>(a.vpool);
 
-    h8 qb[KS];        // Q^T (B operand): row col, dims 32*ks + 8*grp .. +7
-    h8 kr[4][KS];     // K of one step: tile t = keys 16t .. 16t+15
-    h4 vr[DT][2][2];  // V of one step: [dim tile][key half][4-key piece]
+    h8 qb[KS];            // Q^T (B operand): row col, dims 32*ks + 8*grp .. +7
+    h8 kr[NT][KS];        // K of one step: tile t = keys 16t .. 16t+15
+    h4 vr[DT][NT];        // V of one step: [dim tile][key tile], 4 keys per lane
 
     auto query_row = [&](const Task& t) { return col < t.n_rows ? a.rows[t.row_lo + col] : -1; };
     auto load_q = [&](const Task& t, int qrow) {
@@ -436,9 +463,9 @@ void attn_kernel(AttnArgs a) {
     };
     auto load_k = [&](const Task& t, int step) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int key = tile_start(step, tt, t.n_valid);
-            const char* base = slice_of(kpool, tile_id<C>(t.ids, step, tt, t.n_valid), t.head) + (key % C) * 16;
+        for (int tt = 0; tt < NT; ++tt) {
+            const int key = tile_start<D>(step, tt, t.n_valid);
+            const char* base = slice_of(kpool, tile_id<D, C>(t.ids, step, tt, t.n_valid), t.head) + (key % C) * 16;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 kr[tt][ks] = __builtin_nontemporal_load(
@@ -447,18 +474,17 @@ void attn_kernel(AttnArgs a) {
     };
     auto load_v = [&](const Task& t, int step) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int key = tile_start(step, tt, t.n_valid);
-            const char* base = slice_of(vpool, tile_id<C>(t.ids, step, tt, t.n_valid), t.head) +
+        for (int tt = 0; tt < NT; ++tt) {
+            const int key = tile_start<D>(step, tt, t.n_valid);
+            const char* base = slice_of(vpool, tile_id<D, C>(t.ids, step, tt, t.n_valid), t.head) +
                                ((key % C) / 4) * (D * 8);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-                vr[dt][tt >> 1][tt & 1] =
-                    __builtin_nontemporal_load(reinterpret_cast<const h4*>(base + dt * 128 + v_lane));
+                vr[dt][tt] = __builtin_nontemporal_load(reinterpret_cast<const h4*>(base + dt * 128 + v_lane));
         }
     };
 
-    Task cur = fetch_task<C>(a, first);
+    Task cur = fetch_task<D, C>(a, first);
     int cur_qrow = query_row(cur);
     load_q(cur, cur_qrow);
     load_k(cur, 0);
@@ -468,13 +494,13 @@ void attn_kernel(AttnArgs a) {
     Task nxt = cur;
     int nxt_qrow = -1;
     if (has_next) {
-        nxt = fetch_task<C>(a, first + 1);
+        nxt = fetch_task<D, C>(a, first + 1);
         nxt_qrow = query_row(nxt);
     }
 
     f4 o[DT];
     float m_run, l_run;
-    f4 s[4];
+    f4 s[NT];
     for (;;) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -483,18 +509,18 @@ void attn_kernel(AttnArgs a) {
         // all steps but the last: the next step's K and V follow right behind
         const int n_steps = cur.n_steps;
         for (int step = 0; step + 1 < n_steps; ++step) {
-            qk<KS>(s, kr, qb);
+            qk<NT, KS>(s, kr, qb);
             load_k(cur, step + 1);
-            softmax_pv<DT>(s, vr, o, m_run, l_run, step, cur.n_valid, grp, a.scale_log2e);
+            softmax_pv<NT, DT>(s, vr, o, m_run, l_run, step, cur.n_valid, grp, a.scale_log2e);
             load_v(cur, step + 1);
         }
         // last step: the next task's queries and K/V follow instead
-        qk<KS>(s, kr, qb);
+        qk<NT, KS>(s, kr, qb);
         if (has_next) {
             load_q(nxt, nxt_qrow);
             load_k(nxt, 0);
         }
-        softmax_pv<DT>(s, vr, o, m_run, l_run, n_steps - 1, cur.n_valid, grp, a.scale_log2e);
+        softmax_pv<NT, DT>(s, vr, o, m_run, l_run, n_steps - 1, cur.n_valid, grp, a.scale_log2e);
         finish<D, DT>(a, o, m_run, l_run, cur_qrow, cur.out, cur.head, col, grp);
         if (!has_next) break;
         load_v(nxt, 0);
@@ -503,7 +529,7 @@ void attn_kernel(AttnArgs a) {
         ++ti;
         has_next = ti + 1 < count;
         if (has_next) {
-            nxt = fetch_task<C>(a, first + ti + 1);
+            nxt = fetch_task<D, C>(a, first + ti + 1);
             nxt_qrow = query_row(nxt);
         }
     }
@@ -670,6 +696,10 @@ hipError_t scatter_inline_dc(const ScatterArgs& a, const InlineSlots& is, hipStr
         case 128032: return FN<128, 32>(__VA_ARGS__);                  \
         case 128064: return FN<128, 64>(__VA_ARGS__);                  \
         case 128128: return FN<128, 128>(__VA_ARGS__);                 \
+        case 256016: return FN<256, 16>(__VA_ARGS__);                  \
+        case 256032: return FN<256, 32>(__VA_ARGS__);                  \
+        case 256064: return FN<256, 64>(__VA_ARGS__);                  \
+        case 256128: return FN<256, 128>(__VA_ARGS__);                 \
         default: return hipErrorInvalidValue;                          \
     }
 
@@ -702,6 +732,8 @@ hipError_t launch_merge(const MergeArgs& a, int D, hipStream_t s) {
         merge_kernel<64><<<grid, dim3(256), 0, s>>>(a);
     else if (D == 128)
         merge_kernel<128><<<grid, dim3(256), 0, s>>>(a);
+    else if (D == 256)
+        merge_kernel<256><<<grid, dim3(256), 0, s>>>(a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -60,7 +60,7 @@ pkvt_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool shape_ok(int32_t d, int32_t c) {
-    return (d == 64 || d == 128) && (c == 16 || c == 32 || c == 64 || c == 128);
+    return (d == 64 || d == 128 || d == 256) && (c == 16 || c == 32 || c == 64 || c == 128);
 }
 
 // Two resident workgroups of 4 waves per compute unit: the attention kernel
@@ -97,7 +97,7 @@ pkvt_status pkvt_pool_bytes(int32_t n_heads, int32_t head_dim, int32_t chunk_siz
     if (!bytes || n_heads < 1 || pool_chunks < 1)
         return fail(PKVT_ERR_INVALID_ARG, "pool_bytes: bad arguments");
     if (!shape_ok(head_dim, chunk_size))
-        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "pool_bytes: head_dim must be 64 or 128 and "
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "pool_bytes: head_dim must be 64, 128 or 256 and "
                                                 "chunk_size one of 16, 32, 64, 128");
     *bytes = static_cast<size_t>(pool_chunks) * n_heads * chunk_size * head_dim * 2;
     return PKVT_OK;
@@ -254,7 +254,7 @@ pkvt_status pkvt_plan_upload(pkvt_tree* t, void* d_meta, size_t meta_bytes, void
     if (!t || !d_meta) return fail(PKVT_ERR_INVALID_ARG, "plan_upload: NULL argument");
     if (!plan_current(t)) return fail(PKVT_ERR_STALE_PLAN, "plan_upload: no plan for the current tree");
     if (!shape_ok(t->tree.D, t->tree.C))
-        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "plan_upload: the kernels need head_dim 64 or 128 "
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "plan_upload: the kernels need head_dim 64, 128 or 256 "
                                                 "and chunk_size 16, 32, 64 or 128");
     const pkvt::Plan& p = t->plan;
     const size_t words = p.blob.size();

@@ -237,7 +237,7 @@ def test_empty_prompt_rejected_and_nothing_inserted():
     assert B.pkvt_tree_stats(box.t)["used_chunks"] == 0
 
 
-@pytest.mark.parametrize("d,c", [(32, 16), (96, 64), (128, 8), (128, 48), (256, 64)])
+@pytest.mark.parametrize("d,c", [(32, 16), (96, 64), (128, 8), (128, 48), (512, 64), (256, 256)])
 def test_unsupported_shapes(d, c):
     """Host tree works for any shape; device entry points refuse before
     touching the GPU."""

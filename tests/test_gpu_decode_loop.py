@@ -65,7 +65,7 @@ def test_decode_loop_every_step_small():
     ds.close()
 
 
-@pytest.mark.parametrize("seed,d,c", [(31, 128, 32), (32, 64, 16), (33, 128, 64)])
+@pytest.mark.parametrize("seed,d,c", [(31, 128, 32), (32, 64, 16), (33, 128, 64), (34, 256, 32)])
 def test_decode_loop_unaligned_prefix(seed, d, c):
     """A shared prefix that ends inside a chunk (its tail is private to each
     sequence, and a new arrival writes it again), ragged suffixes, joins every
@@ -108,7 +108,7 @@ def test_decode_loop_long_prefix_sampled():
     ds.close()
 
 
-@pytest.mark.parametrize("d,c,n", [(128, 64, 64), (64, 16, 256), (128, 32, 1)])
+@pytest.mark.parametrize("d,c,n", [(128, 64, 64), (64, 16, 256), (128, 32, 1), (256, 128, 100)])
 def test_scatter_host_slots_matches_device_slots(d, c, n):
     """pkvt_kv_scatter_host_slots (slots in the launch arguments) writes the
     same pool bytes as pkvt_kv_scatter (slots in device memory), skipping

@@ -65,7 +65,7 @@ def test_config_parity(name, variant):
 def test_random_trees(seed):
     _torch()
     rng = np.random.default_rng(seed)
-    d = int(rng.choice([64, 128]))
+    d = int(rng.choice([64, 128, 256]))
     c = int(rng.choice([16, 32, 64, 128]))
     h = int(rng.integers(1, 4))
     print(f"\n[case] random tree seed={seed} h={h} d={d} c={c}", flush=True)
@@ -85,7 +85,7 @@ def test_wide_trees(seed):
     run as workgroup units (LDS-shared loads) and longer blocks are cut."""
     _torch()
     rng = np.random.default_rng(200 + seed)
-    d = int(rng.choice([64, 128]))
+    d = int(rng.choice([64, 128, 256]))
     c = int(rng.choice([16, 32, 64, 128]))
     h = int(rng.integers(1, 4))
     b = int(rng.integers(20, 141))
@@ -102,7 +102,8 @@ def test_wide_trees(seed):
 
 
 @pytest.mark.parametrize("rows", [17, 32, 33, 48, 64, 65, 81, 130])
-@pytest.mark.parametrize("d,c,n_chunks", [(64, 16, 5), (128, 32, 3), (128, 64, 2)])
+@pytest.mark.parametrize("d,c,n_chunks", [(64, 16, 5), (128, 32, 3), (128, 64, 2), (256, 16, 3),
+                                          (256, 128, 1)])
 def test_unit_row_counts(rows, d, c, n_chunks):
     """One shared prefix read by `rows` sequences: unit row blocks of every
     size class, and prefixes whose length is not a multiple of 64 keys (the
@@ -258,4 +259,39 @@ def test_sweep_shapes_sampled(b, n_s, private, variant):
     err = _err(got[rows], ref[rows])
     print(f"[case]   rows {rows} err={err:.3e} info={ds.info}", flush=True)
     assert err <= TOL
+    ds.close()
+
+
+@pytest.mark.parametrize("d,c", [(256, 64), (256, 16), (256, 128), (64, 64)])
+def test_head_dim_variants_long_prefix(d, c):
+    """The long-shared-prompt batch (64 sequences, 4096 shared tokens,
+    ragged private suffixes) at other head dims, with h d = 4096: sampled
+    rows against the oracle, two-phase and plain."""
+    _torch()
+    h = 4096 // d
+    rng = np.random.default_rng(d + c)
+    suffix = [int(x) for x in rng.integers(256, 1025, size=64)]
+    print(f"\n[case] head_dim variant d={d} c={c} h={h}", flush=True)
+    w = W.one_prefix(5000 + d + c, 64, 4096, suffix, h=h, d=d, c=c)
+    rows = [0, 21, 42, 63]
+    ref = A.attention_batch(w, seqs=rows)
+    for ms in (0, 1 << 20):
+        ds = _setup(w, min_share=ms)
+        got = _run(ds)
+        err = _err(got[rows], ref[rows])
+        print(f"[case]   min_share={ms} err={err:.3e} info={ds.info}", flush=True)
+        assert err <= TOL
+        ds.close()
+
+
+def test_single_key_bit_exact_head_dim_256():
+    _torch()
+    w = W.random_tree(3, h=2, d=256, c=16, max_b=6, max_len=1)
+    for p in w.seq_paths:
+        assert sum(len(w.segments[s]) for s in p) == 1
+    ds = _setup(w)
+    got = ds.decode().cpu().numpy()
+    for u in range(w.b):
+        K, V = A.materialize(w, u)
+        assert np.array_equal(got[u], V[0].astype(np.float16))
     ds.close()
