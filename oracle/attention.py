@@ -167,3 +167,46 @@ def tpp_attention(w, chunk_labels: List[np.ndarray], c: int, layer: int = 0,
                 o, m, n = attn_reduce(oC, mC, nC, o, m, n)
             out[u, hh] = o / n
     return out
+
+
+# --------------------------------------------------------------------------
+# Prefill: many new query rows per sequence, causal.
+# --------------------------------------------------------------------------
+
+def prefill_rows(w, seqs: Sequence[int], q_from: Sequence[int]) -> List[Tuple[int, int]]:
+    """The (sequence, position) of every prefill query row, in row order:
+    for each u of ``seqs`` in order, positions q_from[i] .. L_u - 1."""
+    rows = []
+    for u, a in zip(seqs, q_from):
+        rows += [(int(u), p) for p in range(int(a), w.seq_len(int(u)))]
+    return rows
+
+
+def prefill_attention(w, seqs: Sequence[int], q_from: Sequence[int], q: np.ndarray,
+                      layer: int = 0, scale: float = None, rows: Sequence[int] = None) -> np.ndarray:
+    """Causal attention of prefill query rows, fp64.
+
+    A new token at position p of sequence u attends to u's tokens 0..p: the
+    keys already stored before it (a matched shared prefix, or earlier
+    pieces of a chunked prompt) and the new tokens up to itself (causal
+    visibility; ChunkAttention page, Knowl 1 arrival; the chunked-prefill
+    page, sections 1-2: append-only KV and the causal mask make feeding a
+    prompt in pieces exact).  ``q`` [R, h, d] holds the rows of
+    ``prefill_rows(w, seqs, q_from)``; returns O [R, h, d] (only ``rows``
+    filled when given, NaN elsewhere)."""
+    R, h, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    meta = prefill_rows(w, seqs, q_from)
+    assert len(meta) == R
+    out = np.full((R, h, d), np.nan, dtype=np.float64)
+    want = set(range(R)) if rows is None else set(int(r) for r in rows)
+    cache_u, KV = None, None
+    for r, (u, p) in enumerate(meta):
+        if r not in want:
+            continue
+        if u != cache_u:
+            KV, cache_u = materialize(w, u, layer), u
+        K, V = KV
+        out[r] = attention_one(q[r], K[:p + 1], V[:p + 1], scale)
+    return out

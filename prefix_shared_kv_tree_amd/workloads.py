@@ -414,3 +414,45 @@ def decode_trace(w: Workload, steps: int, seed: int, churn_every: int = 0,
             j.suffix.k.append(_normal_f16(rng, (len(j.suffix), h, d)))
             j.suffix.v.append(_normal_f16(rng, (len(j.suffix), h, d)))
     return DecodeTrace(base=w, steps=steps, tokens=tokens, q=q, k=ks, v=vs, joins=joins)
+
+
+# ---- prefill batches ------------------------------------------------------------
+#
+# A prefill batch: sequences arrive whose prompts begin with a prefix that the
+# tree already stores (held by a resident sequence that is not part of the
+# batch), so only their new tokens need attention (ChunkAttention page,
+# Knowl 1 arrival: matched prefix chunks are shared, the newly computed suffix
+# tokens get chunks of their own).  Every new token at position p attends to
+# the sequence's tokens 0..p.
+
+@dataclasses.dataclass
+class PrefillBatch:
+    w: Workload                       # segment 0: the resident prefix; sequences 1..: the batch
+    resident: List[int]               # token sequence already in the tree before the batch
+    seqs: List[int]                   # batch sequences (indices into w.seq_paths)
+    q_from: List[int]                 # first new position of each batch sequence
+    q: np.ndarray                     # float16 [R, h, d], rows in (sequence, position) order
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.q.shape[0])
+
+
+def prefill_batch(seed: int, b: int, prefix: int, new, h: int = 2, d: int = 64, c: int = 16,
+                  layers: int = 1, with_kv: bool = True) -> PrefillBatch:
+    """b sequences = one shared prefix of ``prefix`` tokens + ``new`` tokens
+    each (a count or b counts).  The prefix is stored beforehand; its full
+    chunks are matched, so every sequence's new rows start at the prefix
+    length rounded down to a whole chunk (a partial last prefix chunk is
+    written again by each sequence, as whole-chunk matching dictates).
+    Draw order (PCG64(seed)): the workload as ``one_prefix`` draws it
+    (tokens, a decode Q that is not used, K/V), then the prefill Q [R, h, d]."""
+    newl = [int(new)] * b if np.isscalar(new) else [int(x) for x in new]
+    w = one_prefix(seed, b, prefix, newl, h=h, d=d, c=c, layers=layers, with_kv=with_kv)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    a = (prefix // c) * c
+    q_from = [a] * b
+    R = sum(w.seq_len(u) - a for u in range(b))
+    q = _normal_f16(rng, (R, h, d))
+    resident = [int(x) for x in w.segments[0].tokens] if prefix > 0 else []
+    return PrefillBatch(w=w, resident=resident, seqs=list(range(b)), q_from=q_from, q=q)
