@@ -585,6 +585,68 @@ def run_sweep(args):
                       "points": points}), flush=True)
 
 
+def prefill_flops(pb):
+    """Useful FLOPs of a prefill: 4 d per (row, head, visible key); the row
+    at position p sees p + 1 keys."""
+    n = 0
+    for u, a in zip(pb.seqs, pb.q_from):
+        L = pb.w.seq_len(u)
+        n += (L * (L + 1) - a * (a + 1)) // 2
+    return 4 * pb.w.d * pb.w.h * n
+
+
+def run_prefill(args):
+    """Prefix-aware prefill of arriving sequences over a stored shared
+    prefix: µs per layer and useful TFLOP/s (against the dense f16 matrix
+    peak), and the same rows with every sequence holding its own copy of the
+    prefix (nothing shared: each sequence's rows read the prefix for
+    themselves).  K/V and Q are drawn on the device."""
+    import torch
+    from prefix_shared_kv_tree_amd import binding as B
+    from prefix_shared_kv_tree_amd import workloads as W
+    from prefix_shared_kv_tree_amd.harness import PrefillSetup
+    B.load()
+    rng = np.random.Generator(np.random.PCG64(1002))
+    cases = [("b32_prefix1024_new512", 32, 1024, 512),
+             ("b64_prefix4096_new256-1024", 64, 4096, [int(x) for x in rng.integers(256, 1025, 64)]),
+             ("b64_prefix2048_new64", 64, 2048, 64)]
+    out = []
+    for name, b, prefix, new in cases:
+        row = {"workload": name, "b": b, "prefix": prefix, "h": 32, "d": 128, "c": 64}
+        for variant in ("shared", "unshared"):
+            pb = W.prefill_batch(4242, b, prefix, new, h=32, d=128, c=64, with_kv=False)
+            if variant == "unshared":
+                pb = W.prefill_unshared(pb)
+            ps = PrefillSetup(pb, layers=2, device_random_seed=4242)
+            stream = torch.cuda.current_stream().cuda_stream
+            for i in range(3):
+                ps.run(i % 2, stream=stream)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            steps = args.prefill_steps
+            e0.record()
+            for i in range(steps):
+                ps.run(i % 2, stream=stream)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            fl = prefill_flops(pb)
+            row[f"{variant}_us_per_layer"] = round(us, 1)
+            row[f"{variant}_tflops"] = round(fl / (us * 1e-6) / 1e12, 1)
+            if variant == "shared":
+                row["rows"] = pb.n_rows
+                row["useful_gflop"] = round(fl / 1e9, 2)
+                row["frac_mfma_f16_peak"] = round(fl / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+                row["plan"] = {k: ps.info[k] for k in ("wg_units", "slots", "phase1_items")}
+            ps.close()
+            del ps
+        row["speedup_vs_unshared"] = round(row["unshared_us_per_layer"] / row["shared_us_per_layer"], 3)
+        print(json.dumps(row), file=sys.stderr, flush=True)
+        out.append(row)
+    print(json.dumps({"prefill": out, "dtype": "f16", "data": "synthetic, device N(0,1)",
+                      "steps": args.prefill_steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -624,6 +686,9 @@ def main():
                     help="time the decode-throughput sweeps of the pages' divergence (Knowl 8) "
                          "or batch-size (Knowl 9) experiments instead of the benchmark")
     ap.add_argument("--sweep-steps", type=int, default=60)
+    ap.add_argument("--prefill", action="store_true",
+                    help="time prefix-aware prefill attention instead of the decode benchmark")
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--loop-only", action="store_true",
                     help="run only the decode loop (for profiling it)")
     args = ap.parse_args()
@@ -651,6 +716,9 @@ def main():
     B.load()
     if args.sweep:
         run_sweep(args)
+        return
+    if args.prefill:
+        run_prefill(args)
         return
 
     probe = W.make_config(args.config, with_kv=False)

@@ -256,6 +256,52 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* tree, const void* d_meta, const
                                 void* workspace, size_t workspace_bytes, float scale,
                                 void* stream, void* attn_start_event, void* attn_end_event);
 
+/* ------------------------------------------------------------------------
+ * Prefix-aware prefill (Knowl 1 arrival: matched prefix chunks are shared,
+ * the newly computed suffix tokens are stored in new chunks).  After a
+ * pkvt_tree_build (or appends, for a prompt fed in pieces) and
+ * pkvt_kv_scatter of the new tokens' K/V, the new tokens' queries attend
+ * causally: the row at position p of sequence s sees s's tokens 0 .. p, the
+ * stored prefix included.  Chunks that several batch sequences read are
+ * read once per block of up to 64 rows for all of them together (the
+ * chunk-first phase of Knowl 2 applied to many query rows).
+ * ---------------------------------------------------------------------- */
+
+/* Plan the prefill of n sequences: query rows are positions q_from[i] ..
+ * len_i - 1 of sequence seq_ids[i], sequences in the given order, positions
+ * ascending (R rows in all).  opts may be NULL; phase1_chunks caps the
+ * chunks per work item (0 = 64), workgroups as for pkvt_plan, the other
+ * fields are ignored.  Reports the metadata bytes (pkvt_prefill_upload) and
+ * the workspace bytes (fp32 partials) pkvt_prefill_attn needs.
+ * Errors: UNKNOWN_SEQ, INVALID_ARG (n < 1, a duplicate id, q_from outside
+ * [0, len)), HOST_MEMORY. */
+pkvt_status pkvt_prefill_plan(pkvt_tree* tree, int32_t n, const int32_t* seq_ids,
+                              const int64_t* q_from, const pkvt_plan_opts* opts,
+                              size_t* meta_bytes, size_t* workspace_bytes);
+/* Summary of the prefill plan (b = R rows, slots = partials, wg_units =
+ * work units; the decode-only fields are 0). */
+pkvt_status pkvt_prefill_info_get(const pkvt_tree* tree, pkvt_plan_info* out);
+/* Introspection for tests: the prefill plan's metadata words, as
+ * pkvt_plan_blob. */
+pkvt_status pkvt_prefill_blob(const pkvt_tree* tree, int32_t* out, int32_t cap, int32_t* n);
+/* Copy the prefill plan to d_meta, as pkvt_plan_upload does for the decode
+ * plan (skipped when d_meta already holds it).  A d_meta buffer holds one
+ * plan at a time: uploading either plan into it makes the other stale.
+ * Errors: STALE_PLAN, BUFFER_TOO_SMALL, UNSUPPORTED_SHAPE, HIP. */
+pkvt_status pkvt_prefill_upload(pkvt_tree* tree, void* d_meta, size_t meta_bytes, void* stream);
+/* Prefill attention on stream:
+ *   q   : device fp16 [R][h][d], rows as pkvt_prefill_plan numbers them
+ *   out : device fp16 [R][h][d]
+ *   k_pool, v_pool : the layer's pools, holding every token of the batch
+ *         sequences (the new ones written by pkvt_kv_scatter beforehand)
+ *   workspace : device, >= workspace_bytes of pkvt_prefill_plan
+ * One attention launch (work units only) and one merge launch.
+ * Errors: INVALID_ARG, STALE_PLAN (no prefill plan for the current tree, or
+ * not uploaded to d_meta), BUFFER_TOO_SMALL, UNSUPPORTED_SHAPE, HIP. */
+pkvt_status pkvt_prefill_attn(const pkvt_tree* tree, const void* d_meta, const void* q,
+                              const void* k_pool, const void* v_pool, void* out,
+                              void* workspace, size_t workspace_bytes, float scale, void* stream);
+
 /* Write n_tokens tokens' K/V into the pools (the caller's side of arrival
  * and decode append):
  *   slots : device int64 [n_tokens] from pkvt_tree_build / pkvt_tree_append;

@@ -75,6 +75,12 @@ _SIGNATURES = {
     "pkvt_plan_upload": [_vp, _vp, _sz, _vp],
     "pkvt_attn_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp],
     "pkvt_attn_decode_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp, _vp, _vp],
+    "pkvt_prefill_plan": [_vp, C.c_int32, _i32p, _i64p, C.POINTER(PlanOpts), C.POINTER(_sz),
+                          C.POINTER(_sz)],
+    "pkvt_prefill_info_get": [_vp, C.POINTER(PlanInfo)],
+    "pkvt_prefill_blob": [_vp, _i32p, C.c_int32, _i32p],
+    "pkvt_prefill_upload": [_vp, _vp, _sz, _vp],
+    "pkvt_prefill_attn": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp],
     "pkvt_kv_scatter": [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int64, _vp],
     "pkvt_kv_scatter_host_slots": [_vp, _vp, _vp, _i64p, _vp, _vp, C.c_int64, _vp],
     "pkvt_last_error": [],
@@ -241,6 +247,51 @@ def pkvt_plan_blob(tree: int) -> np.ndarray:
 
 def pkvt_plan_upload(tree: int, d_meta: int, meta_bytes: int, stream: int = 0) -> None:
     _check("pkvt_plan_upload", load().pkvt_plan_upload(tree, d_meta, meta_bytes, stream or None))
+
+
+# ---- prefill ---------------------------------------------------------------------
+
+def pkvt_prefill_plan(tree: int, seq_ids, q_from, phase1_chunks: int = 0,
+                      workgroups: int = 0) -> Tuple[int, int]:
+    """Plan a prefill; returns (meta_bytes, workspace_bytes)."""
+    ids = _i32(seq_ids)
+    qf = _i64(q_from)
+    if ids.shape != qf.shape:
+        raise ValueError("seq_ids and q_from must have the same length")
+    opts = PlanOpts(phase1_chunks, 0, 0, workgroups, 0)
+    mb, wb = _sz(), _sz()
+    _check("pkvt_prefill_plan", load().pkvt_prefill_plan(
+        tree, ids.size, _p32(ids) if ids.size else None, _p64(qf) if qf.size else None,
+        C.byref(opts), C.byref(mb), C.byref(wb)))
+    return mb.value, wb.value
+
+
+def pkvt_prefill_info_get(tree: int) -> dict:
+    s = PlanInfo()
+    _check("pkvt_prefill_info_get", load().pkvt_prefill_info_get(tree, C.byref(s)))
+    return {k: getattr(s, k) for k, _ in PlanInfo._fields_ if k != "reserved"}
+
+
+def pkvt_prefill_blob(tree: int) -> np.ndarray:
+    n = C.c_int32()
+    rc = load().pkvt_prefill_blob(tree, None, 0, C.byref(n))
+    if rc not in (PKVT_OK, -6):
+        _check("pkvt_prefill_blob", rc)
+    buf = np.zeros(max(n.value, 1), dtype=np.int32)
+    _check("pkvt_prefill_blob", load().pkvt_prefill_blob(tree, _p32(buf), buf.size, C.byref(n)))
+    return buf[:n.value]
+
+
+def pkvt_prefill_upload(tree: int, d_meta: int, meta_bytes: int, stream: int = 0) -> None:
+    _check("pkvt_prefill_upload", load().pkvt_prefill_upload(tree, d_meta, meta_bytes,
+                                                             stream or None))
+
+
+def pkvt_prefill_attn(tree: int, d_meta: int, q: int, k_pool: int, v_pool: int, out: int,
+                      workspace: int, workspace_bytes: int, scale: float, stream: int = 0) -> None:
+    _check("pkvt_prefill_attn", load().pkvt_prefill_attn(tree, d_meta, q, k_pool, v_pool, out,
+                                                         workspace or None, workspace_bytes,
+                                                         float(scale), stream or None))
 
 
 # ---- device work ----------------------------------------------------------------

@@ -260,8 +260,10 @@ struct Img {
 // Wave w loads pieces [w, w + 1) * kPieces / 4 of every step's image and
 // computes rows 16w .. 16w + 15 (if it has any) from the LDS copy.  The trip
 // count comes from the unit descriptor that all 4 waves read, so every wave
-// passes the same number of barriers.
-template <int D, int C>
+// passes the same number of barriers.  kCausal (prefill): the row at
+// sequence position p sees only the keys at positions <= p, the unit's keys
+// starting at position key_base.
+template <int D, int C, bool kCausal>
 __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, int lane, char* img) {
     constexpr int KS = D / 32, DT = D / 16, NT = Step<D>::kTiles;
     constexpr int kPer = Img<D>::kPieces / kWaves;   // pieces per wave per step
@@ -279,6 +281,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
     const int row_lo = u[4];
     const int n_rows = u[5];
     const int out = u[6];
+    const int key_base = kCausal ? u[7] : 0;
     const int role = wave;
     const bool computes = 16 * role < n_rows;
     const int n_steps = (n_keys + Step<D>::kKeys - 1) / Step<D>::kKeys;
@@ -326,9 +329,11 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 
     h8 qb[KS];
     int qrow = -1;
+    int lim = n_keys;                  // keys this lane's row sees
     if (computes) {
         const int r = 16 * role + col;
         qrow = r < n_rows ? a.rows[row_lo + r] : -1;
+        if (kCausal && r < n_rows) lim = min(n_keys, a.qpos[row_lo + r] + 1 - key_base);
         const _Float16* qp = static_cast<const _Float16*>(a.q) +
                              (static_cast<size_t>(qrow < 0 ? 0 : qrow) * H + head) * D + 8 * grp;
 #pragma unroll
@@ -361,7 +366,8 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
                 }
             }
             h4 pq[NT];
-            softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, n_keys, grp, a.scale_log2e);
+            softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, kCausal ? lim : n_keys, grp,
+                                 a.scale_log2e);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 h4 v[NT];
@@ -429,7 +435,7 @@ void attn_kernel(AttnArgs a) {
         const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
         const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
         for (int k = 0; k < ucount; ++k)
-            run_unit<D, C>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
+            run_unit<D, C, false>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
     }
 
     // ---- this wave's single-wave tasks ------------------------------------------
@@ -533,6 +539,19 @@ void attn_kernel(AttnArgs a) {
             nxt_qrow = query_row(nxt);
         }
     }
+}
+
+// Prefill: the workgroup's units with the causal mask per row; nothing else.
+template <int D, int C>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void prefill_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[Img<D>::kBytes];
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
+    const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
+    for (int k = 0; k < ucount; ++k)
+        run_unit<D, C, true>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
 }
 
 // Fold every partial of one (sequence, head) with attn_reduce and divide.
@@ -668,6 +687,14 @@ hipError_t attn_dc(const AttnArgs& a, hipStream_t s) {
 }
 
 template <int D, int C>
+hipError_t prefill_dc(const AttnArgs& a, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(a.n_wg);
+    if (grid == 0) return hipSuccess;
+    prefill_kernel<D, C><<<dim3(grid), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int D, int C>
 hipError_t scatter_dc(const ScatterArgs& a, hipStream_t s) {
     const int64_t threads = a.n_tokens * a.H * (D / 8);
     if (threads == 0) return hipSuccess;
@@ -705,6 +732,10 @@ hipError_t scatter_inline_dc(const ScatterArgs& a, const InlineSlots& is, hipStr
 
 hipError_t launch_attn(const AttnArgs& a, int D, int C, hipStream_t s) {
     PKVT_DISPATCH(attn_dc, D, C, a, s)
+}
+
+hipError_t launch_prefill(const AttnArgs& a, int D, int C, hipStream_t s) {
+    PKVT_DISPATCH(prefill_dc, D, C, a, s)
 }
 
 hipError_t launch_scatter(const ScatterArgs& a, int D, int C, hipStream_t s) {

@@ -26,13 +26,18 @@ struct Staging {
 };
 constexpr int kStagingRing = 4;
 
+// What the last upload of a plan put where.
+struct Uploaded {
+    const void* ptr = nullptr;
+    int64_t serial = -1;
+    int64_t len_version = -1;
+};
+
 struct pkvt_tree {
     pkvt::Tree tree;
-    pkvt::Plan plan;
-    // what the last upload put where
-    const void* uploaded_ptr = nullptr;
-    int64_t uploaded_serial = -1;
-    int64_t uploaded_len_version = -1;
+    pkvt::Plan plan;          // decode
+    pkvt::Plan prefill;       // prefill
+    Uploaded up_plan, up_prefill;
     Staging staging[kStagingRing];
     int next_staging = 0;
 
@@ -55,8 +60,8 @@ pkvt_status fail(pkvt_status code, const std::string& msg) {
     return code;
 }
 
-pkvt_status hip_fail(hipError_t e, const char* what) {
-    return fail(PKVT_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+pkvt_status hip_fail(hipError_t e, const std::string& what) {
+    return fail(PKVT_ERR_HIP, what + ": " + hipGetErrorString(e));
 }
 
 bool shape_ok(int32_t d, int32_t c) {
@@ -81,9 +86,90 @@ int32_t default_workgroups() {
     return cached;
 }
 
-bool plan_current(const pkvt_tree* t) {
-    return t->plan.valid && t->plan.struct_version == t->tree.structure_version() &&
-           t->plan.len_version == t->tree.length_version();
+bool current(const pkvt_tree* t, const pkvt::Plan& p) {
+    return p.valid && p.struct_version == t->tree.structure_version() &&
+           p.len_version == t->tree.length_version();
+}
+bool plan_current(const pkvt_tree* t) { return current(t, t->plan); }
+
+// Copy plan p into d_meta (lazily: nothing when d_meta already holds it;
+// with len_refresh, only the length table when only lengths changed) through
+// the next staging buffer of the ring and the word-copy kernel.  other: the
+// upload record of the tree's other plan, forgotten if d_meta held it.
+pkvt_status upload(pkvt_tree* t, const pkvt::Plan& p, Uploaded& up, Uploaded& other,
+                   void* d_meta, size_t meta_bytes, void* stream, bool len_refresh,
+                   const std::string& who) {
+    const size_t words = p.blob.size();
+    if (meta_bytes < words * sizeof(int32_t))
+        return fail(PKVT_ERR_BUFFER_TOO_SMALL, who + ": meta buffer smaller than the plan");
+    size_t first = 0, count = words;
+    if (up.ptr == d_meta && up.serial == p.serial) {
+        if (up.len_version == p.len_version) return PKVT_OK;             // already there
+        if (len_refresh) {
+            first = static_cast<size_t>(p.blob[pkvt::kOffSeqlen]);       // lengths only
+            count = static_cast<size_t>(p.b);
+        }
+    }
+    if (count % 4) count += 4 - count % 4;            // sections are padded to 16 bytes
+    count = std::min(count, words - first);
+    hipError_t e;
+    Staging& st = t->staging[t->next_staging];
+    if (st.in_flight) {
+        if ((e = hipEventSynchronize(st.done)) != hipSuccess) return hip_fail(e, who);
+        st.in_flight = false;
+    }
+    if (!st.done && (e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, who + ": event");
+    if (st.words < words) {
+        if (st.host) (void)hipHostFree(st.host);
+        st.host = nullptr;
+        st.dev = nullptr;
+        st.words = 0;
+        const size_t want = words + words / 2;        // room for the plan to grow
+        if ((e = hipHostMalloc(reinterpret_cast<void**>(&st.host), want * sizeof(int32_t),
+                               hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess)
+            return hip_fail(e, who + ": pinned staging");
+        void* dev = nullptr;
+        if ((e = hipHostGetDevicePointer(&dev, st.host, 0)) != hipSuccess) {
+            (void)hipHostFree(st.host);
+            st.host = nullptr;
+            return hip_fail(e, who + ": staging mapping");
+        }
+        st.dev = static_cast<const int32_t*>(dev);
+        st.words = want;
+    }
+    std::memcpy(st.host + first, p.blob.data() + first, count * sizeof(int32_t));
+    auto s = static_cast<hipStream_t>(stream);
+    if ((e = pkvt::launch_copy_words(st.dev + first, static_cast<int32_t*>(d_meta) + first,
+                                     static_cast<int64_t>(count), s)) != hipSuccess)
+        return hip_fail(e, who + ": copy kernel");
+    if ((e = hipEventRecord(st.done, s)) != hipSuccess) return hip_fail(e, who + ": record");
+    st.in_flight = true;
+    t->next_staging = (t->next_staging + 1) % kStagingRing;
+    up.ptr = d_meta;
+    up.serial = p.serial;
+    up.len_version = p.len_version;
+    if (other.ptr == d_meta) other = Uploaded{};
+    return PKVT_OK;
+}
+
+void fill_info(const pkvt::Plan& p, pkvt_plan_info* out) {
+    std::memset(out, 0, sizeof(*out));
+    out->b = p.b;
+    out->phase1_items = p.phase1_items;
+    out->phase2_items = p.phase2_items;
+    out->waves = p.n_waves;
+    out->workgroups = p.n_wg;
+    out->slots = p.n_slots;
+    out->merge_rows = p.n_merge;
+    out->shared_chunks = p.shared_chunks;
+    out->unique_tokens = p.unique_tokens;
+    out->logical_tokens = p.logical_tokens;
+    out->structure_version = static_cast<int32_t>(p.serial & 0x7fffffff);
+    out->tasks = p.n_tasks;
+    out->phase1_split = p.split1_chunks;
+    out->phase2_split = p.split2_chunks;
+    out->wg_units = p.n_units;
 }
 
 }  // namespace
@@ -221,23 +307,7 @@ pkvt_status pkvt_plan(pkvt_tree* t, int32_t b, const int32_t* q_order, const pkv
 pkvt_status pkvt_plan_info_get(const pkvt_tree* t, pkvt_plan_info* out) {
     if (!t || !out) return fail(PKVT_ERR_INVALID_ARG, "plan_info: NULL argument");
     if (!t->plan.valid) return fail(PKVT_ERR_STALE_PLAN, "plan_info: no plan");
-    std::memset(out, 0, sizeof(*out));
-    const pkvt::Plan& p = t->plan;
-    out->b = p.b;
-    out->phase1_items = p.phase1_items;
-    out->phase2_items = p.phase2_items;
-    out->waves = p.n_waves;
-    out->workgroups = p.n_wg;
-    out->slots = p.n_slots;
-    out->merge_rows = p.n_merge;
-    out->shared_chunks = p.shared_chunks;
-    out->unique_tokens = p.unique_tokens;
-    out->logical_tokens = p.logical_tokens;
-    out->structure_version = static_cast<int32_t>(p.serial & 0x7fffffff);
-    out->tasks = p.n_tasks;
-    out->phase1_split = p.split1_chunks;
-    out->phase2_split = p.split2_chunks;
-    out->wg_units = p.n_units;
+    fill_info(t->plan, out);
     return PKVT_OK;
 }
 
@@ -256,56 +326,8 @@ pkvt_status pkvt_plan_upload(pkvt_tree* t, void* d_meta, size_t meta_bytes, void
     if (!shape_ok(t->tree.D, t->tree.C))
         return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "plan_upload: the kernels need head_dim 64, 128 or 256 "
                                                 "and chunk_size 16, 32, 64 or 128");
-    const pkvt::Plan& p = t->plan;
-    const size_t words = p.blob.size();
-    if (meta_bytes < words * sizeof(int32_t))
-        return fail(PKVT_ERR_BUFFER_TOO_SMALL, "plan_upload: meta buffer smaller than the plan");
-    size_t first = 0, count = words;
-    if (t->uploaded_ptr == d_meta && t->uploaded_serial == p.serial) {
-        if (t->uploaded_len_version == p.len_version) return PKVT_OK;    // already there
-        first = static_cast<size_t>(p.blob[pkvt::kOffSeqlen]);           // lengths only
-        count = static_cast<size_t>(p.b);
-    }
-    if (count % 4) count += 4 - count % 4;            // sections are padded to 16 bytes
-    count = std::min(count, words - first);
-    hipError_t e;
-    Staging& st = t->staging[t->next_staging];
-    if (st.in_flight) {
-        if ((e = hipEventSynchronize(st.done)) != hipSuccess) return hip_fail(e, "plan_upload");
-        st.in_flight = false;
-    }
-    if (!st.done && (e = hipEventCreateWithFlags(&st.done, hipEventDisableTiming)) != hipSuccess)
-        return hip_fail(e, "plan_upload: event");
-    if (st.words < words) {
-        if (st.host) (void)hipHostFree(st.host);
-        st.host = nullptr;
-        st.dev = nullptr;
-        st.words = 0;
-        const size_t want = words + words / 2;        // room for the plan to grow
-        if ((e = hipHostMalloc(reinterpret_cast<void**>(&st.host), want * sizeof(int32_t),
-                               hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess)
-            return hip_fail(e, "plan_upload: pinned staging");
-        void* dev = nullptr;
-        if ((e = hipHostGetDevicePointer(&dev, st.host, 0)) != hipSuccess) {
-            (void)hipHostFree(st.host);
-            st.host = nullptr;
-            return hip_fail(e, "plan_upload: staging mapping");
-        }
-        st.dev = static_cast<const int32_t*>(dev);
-        st.words = want;
-    }
-    std::memcpy(st.host + first, p.blob.data() + first, count * sizeof(int32_t));
-    auto s = static_cast<hipStream_t>(stream);
-    if ((e = pkvt::launch_copy_words(st.dev + first, static_cast<int32_t*>(d_meta) + first,
-                                     static_cast<int64_t>(count), s)) != hipSuccess)
-        return hip_fail(e, "plan_upload: copy kernel");
-    if ((e = hipEventRecord(st.done, s)) != hipSuccess) return hip_fail(e, "plan_upload: record");
-    st.in_flight = true;
-    t->next_staging = (t->next_staging + 1) % kStagingRing;
-    t->uploaded_ptr = d_meta;
-    t->uploaded_serial = p.serial;
-    t->uploaded_len_version = p.len_version;
-    return PKVT_OK;
+    return upload(t, t->plan, t->up_plan, t->up_prefill, d_meta, meta_bytes, stream, true,
+                  "plan_upload");
 }
 
 pkvt_status pkvt_attn_decode(const pkvt_tree* t, const void* d_meta, const void* q,
@@ -326,8 +348,8 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* t, const void* d_meta, const vo
     if (!shape_ok(t->tree.D, t->tree.C))
         return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "attn_decode: unsupported head_dim / chunk_size");
     const pkvt::Plan& p = t->plan;
-    if (t->uploaded_ptr != d_meta || t->uploaded_serial != p.serial ||
-        t->uploaded_len_version != p.len_version)
+    if (t->up_plan.ptr != d_meta || t->up_plan.serial != p.serial ||
+        t->up_plan.len_version != p.len_version)
         return fail(PKVT_ERR_STALE_PLAN, "attn_decode: the current plan is not uploaded to d_meta");
     const int32_t H = t->tree.H, D = t->tree.D, C = t->tree.C;
     const size_t need = static_cast<size_t>(p.n_slots) * H * (D + 2) * sizeof(float);
@@ -400,6 +422,109 @@ pkvt_status pkvt_kv_scatter(const pkvt_tree* t, void* k_pool, void* v_pool, cons
     a.H = t->tree.H;
     hipError_t e = pkvt::launch_scatter(a, t->tree.D, t->tree.C, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_scatter");
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_prefill_plan(pkvt_tree* t, int32_t n, const int32_t* seq_ids, const int64_t* q_from,
+                              const pkvt_plan_opts* opts, size_t* meta_bytes, size_t* workspace_bytes) {
+    if (!t) return fail(PKVT_ERR_INVALID_ARG, "prefill_plan: tree is NULL");
+    pkvt::PlanOpts o;
+    if (opts) {
+        o.phase1_chunks = opts->phase1_chunks;
+        o.workgroups = opts->workgroups;
+    }
+    if (o.workgroups < 0) return fail(PKVT_ERR_INVALID_ARG, "prefill_plan: workgroups must be >= 0");
+    if (o.workgroups == 0) o.workgroups = default_workgroups();
+    std::string err;
+    int rc = 0;
+    PKVT_GUARD(rc = pkvt::make_prefill_plan(t->tree, n, seq_ids, q_from, o, t->prefill, err));
+    if (rc) return fail(rc, err);
+    if (meta_bytes) *meta_bytes = t->prefill.blob.size() * sizeof(int32_t);
+    if (workspace_bytes)
+        *workspace_bytes = static_cast<size_t>(t->prefill.n_slots) * t->tree.H * (t->tree.D + 2) *
+                           sizeof(float);
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_prefill_info_get(const pkvt_tree* t, pkvt_plan_info* out) {
+    if (!t || !out) return fail(PKVT_ERR_INVALID_ARG, "prefill_info: NULL argument");
+    if (!t->prefill.valid) return fail(PKVT_ERR_STALE_PLAN, "prefill_info: no prefill plan");
+    fill_info(t->prefill, out);
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_prefill_blob(const pkvt_tree* t, int32_t* out, int32_t cap, int32_t* n) {
+    if (!t || !n || (cap > 0 && !out)) return fail(PKVT_ERR_INVALID_ARG, "prefill_blob: NULL argument");
+    if (!t->prefill.valid) return fail(PKVT_ERR_STALE_PLAN, "prefill_blob: no prefill plan");
+    *n = static_cast<int32_t>(t->prefill.blob.size());
+    if (cap < *n) return fail(PKVT_ERR_BUFFER_TOO_SMALL, "prefill_blob: cap smaller than the plan");
+    std::memcpy(out, t->prefill.blob.data(), t->prefill.blob.size() * sizeof(int32_t));
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_prefill_upload(pkvt_tree* t, void* d_meta, size_t meta_bytes, void* stream) {
+    if (!t || !d_meta) return fail(PKVT_ERR_INVALID_ARG, "prefill_upload: NULL argument");
+    if (!current(t, t->prefill))
+        return fail(PKVT_ERR_STALE_PLAN, "prefill_upload: no prefill plan for the current tree");
+    if (!shape_ok(t->tree.D, t->tree.C))
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "prefill_upload: unsupported head_dim / chunk_size");
+    return upload(t, t->prefill, t->up_prefill, t->up_plan, d_meta, meta_bytes, stream, false,
+                  "prefill_upload");
+}
+
+pkvt_status pkvt_prefill_attn(const pkvt_tree* t, const void* d_meta, const void* q,
+                              const void* k_pool, const void* v_pool, void* out, void* workspace,
+                              size_t workspace_bytes, float scale, void* stream) {
+    if (!t || !d_meta || !q || !k_pool || !v_pool || !out)
+        return fail(PKVT_ERR_INVALID_ARG, "prefill_attn: NULL argument");
+    if (!std::isfinite(scale)) return fail(PKVT_ERR_INVALID_ARG, "prefill_attn: scale is not finite");
+    const pkvt::Plan& p = t->prefill;
+    if (!current(t, p)) return fail(PKVT_ERR_STALE_PLAN, "prefill_attn: prefill plan is older than the tree");
+    if (!shape_ok(t->tree.D, t->tree.C))
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "prefill_attn: unsupported head_dim / chunk_size");
+    if (t->up_prefill.ptr != d_meta || t->up_prefill.serial != p.serial)
+        return fail(PKVT_ERR_STALE_PLAN, "prefill_attn: the prefill plan is not uploaded to d_meta");
+    const int32_t H = t->tree.H, D = t->tree.D, C = t->tree.C;
+    const size_t need = static_cast<size_t>(p.n_slots) * H * (D + 2) * sizeof(float);
+    if (!workspace || workspace_bytes < need)
+        return fail(PKVT_ERR_BUFFER_TOO_SMALL, "prefill_attn: workspace smaller than the plan needs");
+    const int32_t* m = static_cast<const int32_t*>(d_meta);
+    float* part_o = static_cast<float*>(workspace);
+    float* part_ml = part_o + static_cast<size_t>(p.n_slots) * H * D;
+    auto s = static_cast<hipStream_t>(stream);
+    pkvt::AttnArgs a{};
+    a.lists = m + p.blob[pkvt::kOffLists];
+    a.tasks = m + p.blob[pkvt::kOffTasks];
+    a.waves = m + p.blob[pkvt::kOffWaves];
+    a.wg_units = m + p.blob[pkvt::kOffWgUnits];
+    a.units = m + p.blob[pkvt::kOffUnits];
+    a.chunks = m + p.blob[pkvt::kOffChunks];
+    a.rows = m + p.blob[pkvt::kOffRows];
+    a.seqlen = m + p.blob[pkvt::kOffSeqlen];
+    a.qpos = m + p.blob[pkvt::kOffQpos];
+    a.q = q;
+    a.kpool = k_pool;
+    a.vpool = v_pool;
+    a.out = out;
+    a.part_o = part_o;
+    a.part_ml = part_ml;
+    a.H = H;
+    a.n_wg = p.n_units > 0 ? p.n_wg : 0;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    hipError_t e = pkvt::launch_prefill(a, D, C, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill_attn: attention kernel");
+    pkvt::MergeArgs mg{};
+    mg.merge_rows = m + p.blob[pkvt::kOffMerge];
+    mg.mptr = m + p.blob[pkvt::kOffMptr];
+    mg.mslots = m + p.blob[pkvt::kOffMslots];
+    mg.rows = a.rows;
+    mg.part_o = part_o;
+    mg.part_ml = part_ml;
+    mg.out = out;
+    mg.H = H;
+    mg.n_merge = p.n_merge;
+    e = pkvt::launch_merge(mg, D, s);
+    if (e != hipSuccess) return hip_fail(e, "prefill_attn: merge kernel");
     return PKVT_OK;
 }
 

@@ -26,6 +26,7 @@ struct AttnArgs {
     int32_t H;
     int32_t n_wg;             // persistent workgroups (grid size)
     float scale_log2e;        // score scale * log2(e)
+    const int32_t* qpos;      // prefill: [R] sequence position of every depth-first row
 };
 
 struct MergeArgs {
@@ -57,6 +58,8 @@ struct InlineSlots {
 };
 
 hipError_t launch_attn(const AttnArgs& a, int D, int C, hipStream_t s);
+// units only, each row masked to the keys at positions <= a.qpos[row]
+hipError_t launch_prefill(const AttnArgs& a, int D, int C, hipStream_t s);
 // slots come from is.slot instead of a.slots (a.n_tokens <= kInlineSlots)
 hipError_t launch_scatter_inline(const ScatterArgs& a, const InlineSlots& is, int D, int C,
                                  hipStream_t s);

@@ -179,6 +179,102 @@ struct Item {
     int32_t out = -1;
 };
 
+// Workgroup units, longest first (equal costs in index order), each to the
+// workgroup that would finish it first, where the younger workgroup of a
+// compute unit (g >= G/2) runs at kYoungSpeedPct % speed.  Ties go to the
+// older class, then to the lower workgroup index.
+void assign_units(const std::vector<int64_t>& cost, int32_t G,
+                  std::vector<std::vector<int32_t>>& wg_units, std::vector<int64_t>& wg_load) {
+    wg_units.assign(G, {});
+    wg_load.assign(G, 0);
+    std::vector<int32_t> order(cost.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = static_cast<int32_t>(i);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t c) { return cost[a] > cost[c]; });
+    int64_t max_cost = 1;
+    for (int64_t c : cost) max_cost = std::max(max_cost, c);
+    const int32_t n_old = G > 1 ? G / 2 : G;
+    LaneQueue q[2];
+    q[0].init(0, n_old, wg_load, max_cost);
+    q[1].init(n_old, G - n_old, wg_load, max_cost);
+    for (int32_t ui : order) {
+        int cls = -1;
+        int64_t best = 0;
+        for (int c = 0; c < 2; ++c) {
+            if (q[c].empty()) continue;
+            const int64_t fin = (q[c].min_load() + cost[ui]) * 100 / (c ? kYoungSpeedPct : 100);
+            if (cls < 0 || fin < best) {
+                cls = c;
+                best = fin;
+            }
+        }
+        const int32_t g = q[cls].take(cost[ui]);
+        wg_load[g] += cost[ui];
+        wg_units[g].push_back(ui);
+    }
+}
+
+// Depth-first order over the paths of the batch sequences, children in
+// creation order (Knowl 1's contiguity invariant: the sequences under any
+// node are one range of depth-first positions).  Fills sc.node[x] = {i, j}
+// for every node on a batch path (and the root), with seg = -1; returns the
+// depth-first position -> batch index order and the visited nodes, parents
+// first.  False if a row was lost (cannot happen for a consistent tree).
+bool batch_dfs(const Tree& t, const std::vector<const Seq*>& seqs, PlanScratch& sc,
+               std::vector<int32_t>& dfs_row, std::vector<int32_t>& preorder) {
+    const int32_t b = static_cast<int32_t>(seqs.size());
+    const int32_t root = t.root();
+    const size_t n_nodes = static_cast<size_t>(t.N) + 1;
+    if (sc.mark.size() != n_nodes) {
+        sc.mark.assign(n_nodes, 0);
+        sc.node.resize(n_nodes);
+        sc.epoch = 0;
+    }
+    if (++sc.epoch == 0) {
+        std::fill(sc.mark.begin(), sc.mark.end(), 0u);
+        sc.epoch = 1;
+    }
+    const uint32_t epoch = sc.epoch;
+    auto on_path = [&](int32_t x) { return sc.mark[x] == epoch; };
+    PlanScratch::NodeInfo* info = sc.node.data();
+    auto touch = [&](int32_t x) {
+        if (!on_path(x)) {
+            sc.mark[x] = epoch;
+            info[x] = PlanScratch::NodeInfo{0, 0, -1, -1};
+        }
+    };
+    touch(root);
+    for (int32_t r = 0; r < b; ++r)
+        for (int32_t x : seqs[r]->path) touch(x);
+    // rows ending at each leaf, as lists threaded through next_row (ascending)
+    std::vector<int32_t> next_row(b, -1);
+    for (int32_t r = b - 1; r >= 0; --r) {
+        const int32_t leaf = seqs[r]->path.back();
+        next_row[r] = info[leaf].first_row;
+        info[leaf].first_row = r;
+    }
+    dfs_row.clear();
+    preorder.clear();
+    dfs_row.reserve(b);
+    struct Frame { int32_t node; size_t next; };
+    std::vector<Frame> stack{{root, 0}};
+    while (!stack.empty()) {
+        Frame& f = stack.back();
+        const Node& n = t.node(f.node);
+        if (f.next < n.children.size()) {
+            const int32_t ch = n.children[f.next++];
+            if (!on_path(ch)) continue;                       // not on a batch path
+            info[ch].i = static_cast<int32_t>(dfs_row.size());
+            preorder.push_back(ch);
+            for (int32_t r = info[ch].first_row; r >= 0; r = next_row[r]) dfs_row.push_back(r);
+            stack.push_back({ch, 0});
+        } else {
+            info[f.node].j = static_cast<int32_t>(dfs_row.size());
+            stack.pop_back();
+        }
+    }
+    return static_cast<int32_t>(dfs_row.size()) == b;
+}
+
 }  // namespace
 
 static void write_seqlen(const Tree& t, Plan& plan) {
@@ -242,62 +338,13 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
 
     // ---- 1. depth-first order over the batch's paths --------------------------
     const int32_t root = t.root();
-    PlanScratch& sc = plan.scratch;
-    const size_t n_nodes = static_cast<size_t>(t.N) + 1;
-    if (sc.mark.size() != n_nodes) {
-        sc.mark.assign(n_nodes, 0);
-        sc.node.resize(n_nodes);
-        sc.epoch = 0;
-    }
-    if (++sc.epoch == 0) {
-        std::fill(sc.mark.begin(), sc.mark.end(), 0u);
-        sc.epoch = 1;
-    }
-    const uint32_t epoch = sc.epoch;
-    auto on_path = [&](int32_t x) { return sc.mark[x] == epoch; };
-    PlanScratch::NodeInfo* info = sc.node.data();
-    auto touch = [&](int32_t x) {
-        if (!on_path(x)) {
-            sc.mark[x] = epoch;
-            info[x] = PlanScratch::NodeInfo{0, 0, -1, -1};
-        }
-    };
-    touch(root);
-    for (int32_t r = 0; r < b; ++r)
-        for (int32_t x : seqs[r]->path) touch(x);
-    // rows ending at each leaf, as lists threaded through next_row (ascending)
-    std::vector<int32_t> next_row(b, -1);
-    for (int32_t r = b - 1; r >= 0; --r) {
-        const int32_t leaf = seqs[r]->path.back();
-        next_row[r] = info[leaf].first_row;
-        info[leaf].first_row = r;
-    }
     std::vector<int32_t> dfs_row;             // depth-first position -> query row
     std::vector<int32_t> preorder;            // visited nodes, parents first
-    dfs_row.reserve(b);
-    {
-        struct Frame { int32_t node; size_t next; };
-        std::vector<Frame> stack{{root, 0}};
-        while (!stack.empty()) {
-            Frame& f = stack.back();
-            const Node& n = t.node(f.node);
-            if (f.next < n.children.size()) {
-                const int32_t ch = n.children[f.next++];
-                if (!on_path(ch)) continue;                       // not on a batch path
-                info[ch].i = static_cast<int32_t>(dfs_row.size());
-                preorder.push_back(ch);
-                for (int32_t r = info[ch].first_row; r >= 0; r = next_row[r]) dfs_row.push_back(r);
-                stack.push_back({ch, 0});
-            } else {
-                info[f.node].j = static_cast<int32_t>(dfs_row.size());
-                stack.pop_back();
-            }
-        }
-    }
-    if (static_cast<int32_t>(dfs_row.size()) != b) {
+    if (!batch_dfs(t, seqs, plan.scratch, dfs_row, preorder)) {
         err = "plan: internal error, depth-first order lost rows";
         return PKVT_ERR_INVALID_ARG;
     }
+    PlanScratch::NodeInfo* info = plan.scratch.node.data();
     auto cov = [&](int32_t x) { return info[x].j - info[x].i; };
 
     // ---- 2. phase-1 segments ----------------------------------------------------
@@ -483,40 +530,13 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         // waves progress at about kYoungSpeedPct % of the older one's speed.
         // Work goes, longest first, to whichever wave (or workgroup, for
         // units) would finish it first at its speed.
-        using QE = std::pair<int64_t, int32_t>;
-        using MinHeap = std::priority_queue<QE, std::vector<QE>, std::greater<QE>>;
-        auto young = [&](int32_t g) { return G > 1 && g >= G / 2; };
-        // pick from two heaps (older, younger) the entry whose load + cost
-        // ends first at its class's speed
-        auto pick = [&](MinHeap* hq, int64_t cost) {
-            int cls = -1;
-            int64_t best = 0;
-            for (int c = 0; c < 2; ++c) {
-                if (hq[c].empty()) continue;
-                const int64_t fin = (hq[c].top().first + cost) * 100 / (c ? kYoungSpeedPct : 100);
-                if (cls < 0 || fin < best) {
-                    cls = c;
-                    best = fin;
-                }
-            }
-            const QE e = hq[cls].top();
-            hq[cls].pop();
-            return std::make_pair(cls, e);
-        };
-        // workgroup units, longest first
-        std::vector<int32_t> order(units.size());
-        for (size_t i = 0; i < order.size(); ++i) order[i] = static_cast<int32_t>(i);
-        std::stable_sort(order.begin(), order.end(),
-                         [&](int32_t a, int32_t c) { return units[a].cost > units[c].cost; });
-        MinHeap wgq[2];
-        for (int32_t g = 0; g < G; ++g) wgq[young(g)].push({0, g});
-        for (int32_t ui : order) {
-            const auto pk = pick(wgq, units[ui].cost);
-            const int32_t g = pk.second.second;
-            const int64_t end = pk.second.first + units[ui].cost;
-            for (int32_t k = 0; k < kWavesPerWg; ++k) load[g * kWavesPerWg + k] = end;
-            wg_units[g].push_back(ui);
-            wgq[pk.first].push({end, g});
+        {
+            std::vector<int64_t> cost(units.size());
+            for (size_t i = 0; i < units.size(); ++i) cost[i] = units[i].cost;
+            std::vector<int64_t> wg_load;
+            assign_units(cost, G, wg_units, wg_load);
+            for (int32_t g = 0; g < G; ++g)
+                for (int32_t k = 0; k < kWavesPerWg; ++k) load[g * kWavesPerWg + k] = wg_load[g];
         }
         // single-wave tasks x heads, longest first; equal costs keep the
         // (task, head) order.  The lane heaps hold load << lane_bits | lane,
@@ -682,6 +702,281 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     plan.dfs_seq.resize(b);
     for (int32_t p = 0; p < b; ++p) plan.dfs_seq[p] = q_order[dfs_row[p]];
     write_seqlen(t, plan);
+    return PKVT_OK;
+}
+
+int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const int64_t* q_from,
+                      const PlanOpts& in_opts, Plan& plan, std::string& err) {
+    if (n < 1 || !seq_ids || !q_from) {
+        err = "prefill_plan: need n >= 1, seq_ids and q_from";
+        return PKVT_ERR_INVALID_ARG;
+    }
+    if (in_opts.phase1_chunks < 0 || in_opts.workgroups < 0) {
+        err = "prefill_plan: chunk limit and workgroups must be >= 0";
+        return PKVT_ERR_INVALID_ARG;
+    }
+    const int32_t G = in_opts.workgroups > 0 ? in_opts.workgroups : kDefaultWorkgroups;
+    const int32_t lanes = G * kWavesPerWg;
+    const int32_t S = in_opts.phase1_chunks > 0 ? std::min(in_opts.phase1_chunks, kMaxItemChunks)
+                                                : kMaxItemChunks;
+    const int32_t C = t.C;
+
+    // ---- validate; rows per sequence ------------------------------------------
+    std::vector<const Seq*> seqs(n);
+    std::vector<int64_t> nrows(n);
+    int64_t R = 0;
+    {
+        std::unordered_map<int32_t, int32_t> seen;
+        for (int32_t s = 0; s < n; ++s) {
+            const Seq* sq = t.find_seq(seq_ids[s]);
+            if (!sq) {
+                err = "prefill_plan: unknown sequence id " + std::to_string(seq_ids[s]);
+                return PKVT_ERR_UNKNOWN_SEQ;
+            }
+            if (!seen.emplace(seq_ids[s], s).second) {
+                err = "prefill_plan: sequence id " + std::to_string(seq_ids[s]) + " listed twice";
+                return PKVT_ERR_INVALID_ARG;
+            }
+            if (q_from[s] < 0 || q_from[s] >= sq->len) {
+                err = "prefill_plan: q_from of sequence " + std::to_string(seq_ids[s]) +
+                      " must lie in [0, length)";
+                return PKVT_ERR_INVALID_ARG;
+            }
+            seqs[s] = sq;
+            nrows[s] = sq->len - q_from[s];
+            R += nrows[s];
+        }
+        if (R > (int64_t{1} << 30)) {
+            err = "prefill_plan: too many query rows";
+            return PKVT_ERR_INVALID_ARG;
+        }
+    }
+
+    // ---- depth-first order; row numbering -------------------------------------
+    const int32_t root = t.root();
+    std::vector<int32_t> dfs_seq, preorder;
+    if (!batch_dfs(t, seqs, plan.scratch, dfs_seq, preorder)) {
+        err = "prefill_plan: internal error, depth-first order lost rows";
+        return PKVT_ERR_INVALID_ARG;
+    }
+    PlanScratch::NodeInfo* info = plan.scratch.node.data();
+    std::vector<int64_t> caller_start(n + 1, 0), dfs_start(n + 1, 0);
+    for (int32_t s = 0; s < n; ++s) caller_start[s + 1] = caller_start[s] + nrows[s];
+    for (int32_t p = 0; p < n; ++p) dfs_start[p + 1] = dfs_start[p] + nrows[dfs_seq[p]];
+    std::vector<int32_t> row_of(R), qpos(R);
+    for (int32_t p = 0; p < n; ++p) {
+        const int32_t s = dfs_seq[p];
+        for (int64_t k = 0; k < nrows[s]; ++k) {
+            row_of[dfs_start[p] + k] = static_cast<int32_t>(caller_start[s] + k);
+            qpos[dfs_start[p] + k] = static_cast<int32_t>(q_from[s] + k);
+        }
+    }
+
+    // ---- segments: chains of nodes read by the same sequences -----------------
+    std::vector<int32_t> depth(static_cast<size_t>(t.N) + 1, 0);
+    std::vector<std::vector<int32_t>> segs;
+    std::vector<Range> seg_range;
+    std::vector<int32_t> seg_depth;
+    for (int32_t x : preorder) {
+        const int32_t par = t.node(x).parent;
+        depth[x] = par == root ? 0 : depth[par] + 1;
+        if (par != root && info[par].seg >= 0 && info[par].i == info[x].i && info[par].j == info[x].j) {
+            segs[info[par].seg].push_back(x);
+            info[x].seg = info[par].seg;
+        } else {
+            info[x].seg = static_cast<int32_t>(segs.size());
+            segs.push_back({x});
+            seg_range.push_back(Range{info[x].i, info[x].j});
+            seg_depth.push_back(depth[x]);
+        }
+    }
+
+    // ---- items x row blocks -> units ------------------------------------------
+    struct PUnit { int32_t item, keys, n_chunks, row_lo, n_rows, out, key_base; int64_t cost; };
+    std::vector<std::vector<int32_t>> item_chunks;
+    std::vector<PUnit> blocks;                      // one per (item, row block); x heads below
+    std::vector<std::vector<int32_t>> mslots(R);
+    int32_t n_slots = 0;
+    for (size_t sg = 0; sg < segs.size(); ++sg) {
+        const std::vector<int32_t>& ch = segs[sg];
+        const int32_t m = static_cast<int32_t>(ch.size());
+        const int32_t k_items = (m + S - 1) / S;
+        int32_t a = 0;
+        for (int32_t q = 0; q < k_items; ++q) {
+            const int32_t e = a + m / k_items + (q < m % k_items ? 1 : 0);
+            const int32_t item = static_cast<int32_t>(item_chunks.size());
+            item_chunks.emplace_back(ch.begin() + a, ch.begin() + e);
+            int64_t n_keys = 0;
+            for (int32_t i = a; i < e; ++i) n_keys += t.node(ch[i]).fill;
+            const int64_t kb = static_cast<int64_t>(seg_depth[sg] + a) * C;
+            // runs of consecutive rows that see at least the item's first key
+            std::vector<std::pair<int64_t, int64_t>> runs;
+            for (int32_t p = seg_range[sg].i; p < seg_range[sg].j; ++p) {
+                const int32_t s = dfs_seq[p];
+                const int64_t first = std::max<int64_t>(0, kb - q_from[s]);
+                if (first >= nrows[s]) continue;
+                const int64_t r0 = dfs_start[p] + first, r1 = dfs_start[p + 1];
+                if (!runs.empty() && runs.back().second == r0)
+                    runs.back().second = r1;
+                else
+                    runs.push_back({r0, r1});
+            }
+            for (const auto& run : runs) {
+                const int64_t len = run.second - run.first;
+                const int64_t kblk = (len + kRowsPerUnit - 1) / kRowsPerUnit;
+                int64_t b0 = run.first;
+                for (int64_t bi = 0; bi < kblk; ++bi) {
+                    const int64_t rows = len / kblk + (bi < len % kblk ? 1 : 0);
+                    int32_t max_pos = 0;
+                    for (int64_t r = b0; r < b0 + rows; ++r) max_pos = std::max(max_pos, qpos[r]);
+                    // keys past the block's last position are masked for every row
+                    const int64_t keys = std::min<int64_t>(n_keys, max_pos - kb + 1);
+                    PUnit u;
+                    u.item = item;
+                    u.keys = static_cast<int32_t>(keys);
+                    u.n_chunks = static_cast<int32_t>((keys + C - 1) / C);
+                    u.row_lo = static_cast<int32_t>(b0);
+                    u.n_rows = static_cast<int32_t>(rows);
+                    u.out = n_slots;
+                    u.key_base = static_cast<int32_t>(kb);
+                    u.cost = unit_cost(keys);
+                    for (int64_t r = b0; r < b0 + rows; ++r) mslots[r].push_back(n_slots + static_cast<int32_t>(r - b0));
+                    n_slots += static_cast<int32_t>(rows);
+                    blocks.push_back(u);
+                    b0 += rows;
+                }
+            }
+            a = e;
+        }
+    }
+    for (int64_t r = 0; r < R; ++r) {
+        if (mslots[r].empty()) {
+            err = "prefill_plan: internal error, a row reads no key";
+            return PKVT_ERR_INVALID_ARG;
+        }
+    }
+    const int32_t H = t.H;
+    const int64_t n_units64 = static_cast<int64_t>(blocks.size()) * H;
+    if (n_units64 > (int64_t{1} << 28)) {
+        err = "prefill_plan: too many work units";
+        return PKVT_ERR_INVALID_ARG;
+    }
+    std::vector<int64_t> cost(n_units64);
+    for (size_t bi = 0; bi < blocks.size(); ++bi)
+        for (int32_t h = 0; h < H; ++h) cost[bi * H + h] = blocks[bi].cost;
+    std::vector<std::vector<int32_t>> wg_units;
+    std::vector<int64_t> wg_load;
+    assign_units(cost, G, wg_units, wg_load);
+
+    // ---- emit the blob ------------------------------------------------------------
+    const int32_t Ri = static_cast<int32_t>(R);
+    const int32_t n_units = static_cast<int32_t>(n_units64);
+    int64_t total_chunks = 0;
+    for (const auto& c : item_chunks) total_chunks += static_cast<int64_t>(c.size());
+    int64_t n_mslots = 0;
+    for (const auto& m : mslots) n_mslots += static_cast<int64_t>(m.size());
+    std::vector<int32_t> blob(kHeaderWords, 0);
+    auto section = [&](HeaderField f, size_t words) {
+        while (blob.size() % 4) blob.push_back(0);
+        blob[f] = static_cast<int32_t>(blob.size());
+        blob.resize(blob.size() + words, 0);
+    };
+    section(kOffLists, static_cast<size_t>(lanes) * 2);
+    section(kOffTasks, 0);
+    section(kOffWaves, 0);
+    section(kOffWgUnits, static_cast<size_t>(G) * 2);
+    section(kOffUnits, static_cast<size_t>(n_units) * 8);
+    section(kOffChunks, static_cast<size_t>(total_chunks));
+    section(kOffRows, R);
+    section(kOffMerge, R);
+    section(kOffMptr, R + 1);
+    section(kOffMslots, static_cast<size_t>(n_mslots));
+    section(kOffSeqlen, R);
+    section(kOffQpos, R);
+    while (blob.size() % 4) blob.push_back(0);
+    if (blob.size() > (size_t{1} << 31) - 1) {
+        err = "prefill_plan: metadata too large";
+        return PKVT_ERR_INVALID_ARG;
+    }
+    std::vector<int32_t> chunk_off(item_chunks.size());
+    {
+        int32_t coff = 0;
+        for (size_t i = 0; i < item_chunks.size(); ++i) {
+            chunk_off[i] = coff;
+            for (int32_t id : item_chunks[i]) blob[blob[kOffChunks] + coff++] = id;
+        }
+        int32_t ua = 0;
+        for (int32_t g = 0; g < G; ++g) {
+            blob[blob[kOffWgUnits] + 2 * g] = ua;
+            blob[blob[kOffWgUnits] + 2 * g + 1] = static_cast<int32_t>(wg_units[g].size());
+            for (int32_t ui : wg_units[g]) {
+                const PUnit& u = blocks[ui / H];
+                UnitDesc d{};
+                d.n_keys = u.keys;
+                d.chunk_off = chunk_off[u.item];
+                d.n_chunks = u.n_chunks;
+                d.head = ui % H;
+                d.row_lo = u.row_lo;
+                d.n_rows = u.n_rows;
+                d.out = u.out;
+                d.key_base = u.key_base;
+                std::copy(reinterpret_cast<const int32_t*>(&d),
+                          reinterpret_cast<const int32_t*>(&d) + 8, &blob[blob[kOffUnits] + ua * 8]);
+                ++ua;
+            }
+        }
+    }
+    {
+        int32_t at = 0;
+        for (int32_t r = 0; r < Ri; ++r) {
+            blob[blob[kOffRows] + r] = row_of[r];
+            blob[blob[kOffMerge] + r] = r;
+            blob[blob[kOffQpos] + r] = qpos[r];
+            blob[blob[kOffMptr] + r] = at;
+            for (int32_t sl : mslots[r]) blob[blob[kOffMslots] + at++] = sl;
+        }
+        blob[blob[kOffMptr] + Ri] = at;
+    }
+    blob[kMagic] = kPlanMagic;
+    blob[kB] = Ri;
+    blob[kNWaves] = 0;
+    blob[kNWg] = G;
+    blob[kNTasks] = 0;
+    blob[kNUnits] = n_units;
+    blob[kNSlots] = n_slots;
+    blob[kNMerge] = Ri;
+    blob[kTotalWords] = static_cast<int32_t>(blob.size());
+
+    int64_t unique = 0, logical = 0;
+    for (int32_t x : preorder) unique += t.node(x).fill;
+    for (int32_t s = 0; s < n; ++s) logical += seqs[s]->len;
+    plan.serial += 1;
+    blob[kSerial] = static_cast<int32_t>(plan.serial & 0x7fffffff);
+    plan.blob = std::move(blob);
+    plan.valid = true;
+    plan.struct_version = t.structure_version();
+    plan.len_version = t.length_version();
+    plan.b = Ri;
+    plan.q_order.assign(seq_ids, seq_ids + n);
+    plan.opts = in_opts;
+    plan.phase1_items = static_cast<int32_t>(item_chunks.size());
+    plan.phase2_items = 0;
+    plan.n_waves = 0;
+    plan.n_wg = G;
+    plan.n_tasks = 0;
+    plan.n_units = n_units;
+    plan.n_slots = n_slots;
+    plan.n_merge = Ri;
+    plan.split1_chunks = S;
+    plan.split2_chunks = 0;
+    int32_t shared = 0;
+    for (int32_t x : preorder)
+        if (info[x].j - info[x].i >= 2) ++shared;
+    plan.shared_chunks = shared;
+    plan.unique_tokens = unique;
+    plan.logical_tokens = logical;
+    plan.dfs_seq.resize(n);
+    for (int32_t p = 0; p < n; ++p) plan.dfs_seq[p] = seq_ids[dfs_seq[p]];
     return PKVT_OK;
 }
 

@@ -55,14 +55,14 @@ struct UnitDesc {
     int32_t row_lo;      // depth-first position of row 0
     int32_t n_rows;
     int32_t out;         // partial slot of row 0
-    int32_t pad;
+    int32_t key_base;    // prefill: sequence position of the first key (causal mask); decode: 0
 };
 static_assert(sizeof(UnitDesc) == 32, "UnitDesc is 8 int32");
 
 enum HeaderField {
     kMagic = 0, kSerial, kB, kNWaves, kNWg, kNTasks, kNSlots, kNMerge,
     kOffLists, kOffTasks, kOffWaves, kOffChunks, kOffRows, kOffMerge, kOffMptr, kOffMslots,
-    kOffSeqlen, kTotalWords, kNUnits, kOffWgUnits, kOffUnits, kHeaderWords = 24
+    kOffSeqlen, kTotalWords, kNUnits, kOffWgUnits, kOffUnits, kOffQpos, kHeaderWords = 24
 };
 constexpr int32_t kPlanMagic = 0x504b5657;   // "PKVW": lane lists + workgroup units
 constexpr int32_t kRowsPerUnit = 64;         // query rows of one workgroup-unit block
@@ -120,5 +120,18 @@ struct Plan {
 // Build (or refresh) the plan.  Returns a PKVT_* status.
 int make_plan(const Tree& tree, int32_t b, const int32_t* q_order, const PlanOpts& opts,
               Plan& plan, std::string& err);
+
+// Prefill plan: the query rows are positions q_from[s] .. len - 1 of each of
+// the n sequences seq_ids[s] (in that order, positions ascending), and a row
+// at position p attends to its sequence's tokens 0 .. p.  Every chunk on a
+// batch path is read once per block of up to 64 rows that see it: the rows
+// of all batch sequences that share it (a stored prefix) are batched, and a
+// sequence's own new chunks are read by its rows with the causal mask
+// applied per row in the kernel.  The blob has the decode layout with no
+// single-wave tasks, plus qpos [R] (position of every depth-first row); b is
+// the row count R, every row is merged from its partials.  Options used:
+// phase1_chunks (item length cap, 0 = 64 chunks) and workgroups.
+int make_prefill_plan(const Tree& tree, int32_t n, const int32_t* seq_ids, const int64_t* q_from,
+                      const PlanOpts& opts, Plan& plan, std::string& err);
 
 }  // namespace pkvt

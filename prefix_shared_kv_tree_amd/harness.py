@@ -356,3 +356,113 @@ def loop_pool_chunks(trace) -> int:
         n_pre = sum(len(w.segments[s]) for s in j.shared)
         n += -(-(n_pre + len(j.suffix)) // c) + grow
     return n
+
+
+class PrefillSetup:
+    """A prefill batch (``workloads.PrefillBatch``) on the GPU: the resident
+    prefix is inserted and its K/V written first, then the batch sequences
+    arrive (``pkvt_tree_build``; their matched prefix chunks are shared), the
+    new tokens' K/V are written by ``pkvt_kv_scatter``, and the prefill plan
+    for rows q_from .. len - 1 of every sequence is built and uploaded."""
+
+    def __init__(self, pb, layers: Optional[int] = None, device: str = "cuda",
+                 phase1_chunks: int = 0, device_random_seed: Optional[int] = None,
+                 pool_slack: int = 0):
+        import torch
+        self.torch = torch
+        self.pb = pb
+        w = pb.w
+        self.w = w
+        self.layers = w.layers if layers is None else layers
+        self.device = device
+        c = w.c
+        pool_chunks = (sum(-(-len(w.segments[s]) // c) for s in pb.residents) +
+                       sum(-(-w.seq_len(u) // c) for u in pb.seqs) + pool_slack)
+        self.tree = B.pkvt_tree_create(w.h, w.d, c, pool_chunks)
+        stream = torch.cuda.current_stream().cuda_stream
+        res_slots = np.zeros(0, np.int64)
+        if pb.residents:
+            self.resident_ids, res_slots = B.pkvt_tree_build(
+                self.tree, [w.segments[s].tokens for s in pb.residents])
+        self.seq_ids, slots = B.pkvt_tree_build(self.tree, [w.seq_tokens(u) for u in pb.seqs])
+        pos = 0
+        for u, a in zip(pb.seqs, pb.q_from):
+            L = w.seq_len(u)
+            s = slots[pos:pos + L]
+            if not (np.all(s[:a] == -1) and np.all(s[a:] >= 0)):
+                raise RuntimeError(f"sequence {u}: stored prefix does not end at q_from = {a}")
+            pos += L
+        pool_elems = B.pkvt_pool_bytes(w.h, w.d, c, pool_chunks) // 2
+        gen = None
+        if device_random_seed is not None:
+            gen = torch.Generator(device=device)
+            gen.manual_seed(device_random_seed)
+        self.k_pools, self.v_pools = [], []
+        for layer in range(self.layers):
+            kp = torch.empty(pool_elems, dtype=torch.float16, device=device)
+            vp = torch.empty(pool_elems, dtype=torch.float16, device=device)
+            if gen is not None:
+                kp.normal_(generator=gen)
+                vp.normal_(generator=gen)
+            else:
+                writes = []
+                at = 0
+                for s in pb.residents:
+                    seg = w.segments[s]
+                    rs = res_slots[at:at + len(seg)]
+                    at += len(seg)
+                    need = np.nonzero(rs >= 0)[0]
+                    writes.append((seg.k[layer][need], seg.v[layer][need], rs[need]))
+                writes.append(gather_new_tokens(w, slots, layer))
+                for k_new, v_new, s_new in writes:
+                    if s_new.size == 0:
+                        continue
+                    kd = torch.from_numpy(np.ascontiguousarray(k_new)).to(device)
+                    vd = torch.from_numpy(np.ascontiguousarray(v_new)).to(device)
+                    sd = torch.from_numpy(np.ascontiguousarray(s_new, dtype=np.int64)).to(device)
+                    B.pkvt_kv_scatter(self.tree, kp.data_ptr(), vp.data_ptr(), sd.data_ptr(),
+                                      kd.data_ptr(), vd.data_ptr(), s_new.size, stream)
+                    torch.cuda.synchronize()
+            self.k_pools.append(kp)
+            self.v_pools.append(vp)
+        if gen is not None:
+            self.q = torch.empty(pb.q.shape, dtype=torch.float16, device=device).normal_(generator=gen)
+        else:
+            self.q = torch.from_numpy(np.ascontiguousarray(pb.q)).to(device)
+        self.out = torch.empty_like(self.q)
+        self.scale = 1.0 / math.sqrt(w.d)
+        self.replan(phase1_chunks)
+
+    def replan(self, phase1_chunks: int = 0, workgroups: int = 0):
+        torch = self.torch
+        mb, wb = B.pkvt_prefill_plan(self.tree, self.seq_ids, self.pb.q_from,
+                                     phase1_chunks=phase1_chunks, workgroups=workgroups)
+        self.meta = torch.empty(max(mb // 4, 1), dtype=torch.int32, device=self.device)
+        self.meta_bytes = mb
+        self.ws = torch.empty(max(wb // 4, 1), dtype=torch.float32, device=self.device)
+        self.ws_bytes = wb
+        B.pkvt_prefill_upload(self.tree, self.meta.data_ptr(), mb,
+                              torch.cuda.current_stream().cuda_stream)
+        self.info = B.pkvt_prefill_info_get(self.tree)
+        return self.info
+
+    def run(self, layer: int = 0, out=None, stream: Optional[int] = None):
+        torch = self.torch
+        out = self.out if out is None else out
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        B.pkvt_prefill_attn(self.tree, self.meta.data_ptr(), self.q.data_ptr(),
+                            self.k_pools[layer].data_ptr(), self.v_pools[layer].data_ptr(),
+                            out.data_ptr(), self.ws.data_ptr(), self.ws_bytes, self.scale, stream)
+        return out
+
+    def close(self):
+        if self.tree:
+            B.pkvt_tree_destroy(self.tree)
+            self.tree = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -427,8 +427,8 @@ def decode_trace(w: Workload, steps: int, seed: int, churn_every: int = 0,
 
 @dataclasses.dataclass
 class PrefillBatch:
-    w: Workload                       # segment 0: the resident prefix; sequences 1..: the batch
-    resident: List[int]               # token sequence already in the tree before the batch
+    w: Workload
+    residents: List[int]              # segments stored (each as a sequence of its own) before the batch
     seqs: List[int]                   # batch sequences (indices into w.seq_paths)
     q_from: List[int]                 # first new position of each batch sequence
     q: np.ndarray                     # float16 [R, h, d], rows in (sequence, position) order
@@ -454,5 +454,14 @@ def prefill_batch(seed: int, b: int, prefix: int, new, h: int = 2, d: int = 64, 
     q_from = [a] * b
     R = sum(w.seq_len(u) - a for u in range(b))
     q = _normal_f16(rng, (R, h, d))
-    resident = [int(x) for x in w.segments[0].tokens] if prefix > 0 else []
-    return PrefillBatch(w=w, resident=resident, seqs=list(range(b)), q_from=q_from, q=q)
+    return PrefillBatch(w=w, residents=[0] if prefix > 0 else [], seqs=list(range(b)),
+                        q_from=q_from, q=q)
+
+
+def prefill_unshared(pb: PrefillBatch) -> PrefillBatch:
+    """The same rows, K/V and Q with nothing shared: every sequence holds its
+    own copy of the stored prefix under distinct token ids (``unshare``), all
+    copies stored before the batch."""
+    w = unshare(pb.w)
+    residents = [w.seq_paths[u][0] for u in pb.seqs] if pb.residents else []
+    return PrefillBatch(w=w, residents=residents, seqs=pb.seqs, q_from=pb.q_from, q=pb.q)

@@ -8,7 +8,7 @@ import numpy as np
 
 (H_MAGIC, H_SERIAL, H_B, H_NWAVES, H_NWG, H_NTASKS, H_NSLOTS, H_NMERGE, H_OFF_LISTS,
  H_OFF_TASKS, H_OFF_WAVES, H_OFF_CHUNKS, H_OFF_ROWS, H_OFF_MERGE, H_OFF_MPTR, H_OFF_MSLOTS,
- H_OFF_SEQLEN, H_TOTAL, H_NUNITS, H_OFF_WGUNITS, H_OFF_UNITS) = range(21)
+ H_OFF_SEQLEN, H_TOTAL, H_NUNITS, H_OFF_WGUNITS, H_OFF_UNITS, H_OFF_QPOS) = range(22)
 MAGIC = 0x504B5657
 ROWS_PER_UNIT = 64
 
@@ -35,6 +35,7 @@ def parse(blob: np.ndarray) -> dict:
         mptr=mptr,
         mslots=blob[blob[H_OFF_MSLOTS]:blob[H_OFF_MSLOTS] + int(mptr[-1])],
         seqlen=blob[blob[H_OFF_SEQLEN]:blob[H_OFF_SEQLEN] + b],
+        qpos=blob[blob[H_OFF_QPOS]:blob[H_OFF_QPOS] + b] if blob[H_OFF_QPOS] else None,
         total=int(blob[H_TOTAL]),
     )
 
@@ -164,3 +165,49 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
     for wi, w in enumerate(plan["waves"]):
         if phase1[wi]:
             assert int(w[5]) <= max_rows
+
+
+def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: int, heads: int):
+    """Every prefill row (sequence s, position p) reads exactly the keys
+    0 .. p of s, each once, from the chunks on s's path, in units of at most
+    64 rows whose first key it can see; its partial slots are its merge list."""
+    R = plan["b"]
+    rows_meta = []
+    for s, a in zip(seq_ids, q_from):
+        rows_meta += [(int(s), p) for p in range(int(a), lens[int(s)])]
+    assert len(rows_meta) == R
+    caller = [int(x) for x in plan["rows"]]
+    assert sorted(caller) == list(range(R)), "rows is not a permutation"
+    qpos = [int(x) for x in plan["qpos"]]
+    for r in range(R):
+        assert qpos[r] == rows_meta[caller[r]][1]
+    assert len(plan["waves"]) == 0 and len(plan["tasks"]) == 0
+    seen = defaultdict(lambda: defaultdict(int))        # (row, head) -> position -> count
+    slot_rows = {}
+    for u, ch in zip(plan["units"], plan["unit_chunks"]):
+        n_keys, chunk_off, n_chunks, head, row_lo, n_rows, out, key_base = [int(v) for v in u]
+        assert 1 <= n_rows <= ROWS_PER_UNIT and 1 <= n_chunks <= 64 and 0 <= head < heads
+        assert (n_keys + c - 1) // c == n_chunks and key_base % c == 0
+        for i in range(n_rows):
+            r = row_lo + i
+            s, p = rows_meta[caller[r]]
+            assert p >= key_base, "a row that sees none of the unit's keys"
+            path = [int(x) for x in paths[s]]
+            k0 = key_base // c
+            assert [int(x) for x in ch] == path[k0:k0 + n_chunks], "unit chunks are not on the row's path"
+            for pos in range(key_base, min(key_base + n_keys, p + 1)):
+                seen[(r, head)][pos] += 1
+            if head == 0:
+                assert out + i not in slot_rows, "slot written twice"
+                slot_rows[out + i] = r
+    for r in range(R):
+        s, p = rows_meta[caller[r]]
+        for h in range(heads):
+            got = seen[(r, h)]
+            assert sorted(got) == list(range(p + 1)), f"row {r} head {h} keys"
+            assert all(v == 1 for v in got.values()), f"row {r} head {h} reads a key twice"
+    assert set(slot_rows) == set(range(plan["n_slots"]))
+    assert [int(m) for m in plan["merge"]] == list(range(R))
+    for r in range(R):
+        sl = sorted(int(x) for x in plan["mslots"][plan["mptr"][r]:plan["mptr"][r + 1]])
+        assert sl == sorted(k for k, v in slot_rows.items() if v == r)
