@@ -610,10 +610,12 @@ def run_prefill(args):
     cases = [("b32_prefix1024_new512", 32, 1024, 512),
              ("b64_prefix4096_new256-1024", 64, 4096, [int(x) for x in rng.integers(256, 1025, 64)]),
              ("b64_prefix2048_new64", 64, 2048, 64)]
+    if args.prefill_case is not None:
+        cases = [cases[args.prefill_case]]
     out = []
     for name, b, prefix, new in cases:
         row = {"workload": name, "b": b, "prefix": prefix, "h": 32, "d": 128, "c": 64}
-        for variant in ("shared", "unshared"):
+        for variant in ("shared",) if args.prefill_case is not None else ("shared", "unshared"):
             pb = W.prefill_batch(4242, b, prefix, new, h=32, d=128, c=64, with_kv=False)
             if variant == "unshared":
                 pb = W.prefill_unshared(pb)
@@ -640,7 +642,8 @@ def run_prefill(args):
                 row["plan"] = {k: ps.info[k] for k in ("wg_units", "slots", "phase1_items")}
             ps.close()
             del ps
-        row["speedup_vs_unshared"] = round(row["unshared_us_per_layer"] / row["shared_us_per_layer"], 3)
+        if "unshared_us_per_layer" in row:
+            row["speedup_vs_unshared"] = round(row["unshared_us_per_layer"] / row["shared_us_per_layer"], 3)
         print(json.dumps(row), file=sys.stderr, flush=True)
         out.append(row)
     print(json.dumps({"prefill": out, "dtype": "f16", "data": "synthetic, device N(0,1)",
@@ -689,6 +692,8 @@ def main():
     ap.add_argument("--prefill", action="store_true",
                     help="time prefix-aware prefill attention instead of the decode benchmark")
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-case", type=int, default=None,
+                    help="time only this prefill workload (index), shared variant only")
     ap.add_argument("--loop-only", action="store_true",
                     help="run only the decode loop (for profiling it)")
     args = ap.parse_args()

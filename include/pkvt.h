@@ -294,8 +294,10 @@ pkvt_status pkvt_prefill_upload(pkvt_tree* tree, void* d_meta, size_t meta_bytes
  *   out : device fp16 [R][h][d]
  *   k_pool, v_pool : the layer's pools, holding every token of the batch
  *         sequences (the new ones written by pkvt_kv_scatter beforehand)
- *   workspace : device, >= workspace_bytes of pkvt_prefill_plan
- * One attention launch (work units only) and one merge launch.
+ *   workspace : device, >= workspace_bytes of pkvt_prefill_plan (may be NULL
+ *         when that is 0: every row is then written by a single work unit)
+ * One attention launch (work units only) and, when some row has several
+ * partials, one merge launch.
  * Errors: INVALID_ARG, STALE_PLAN (no prefill plan for the current tree, or
  * not uploaded to d_meta), BUFFER_TOO_SMALL, UNSUPPORTED_SHAPE, HIP. */
 pkvt_status pkvt_prefill_attn(const pkvt_tree* tree, const void* d_meta, const void* q,

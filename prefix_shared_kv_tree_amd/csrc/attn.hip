@@ -381,7 +381,9 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
             }
         }
     }
-    if (computes) finish<D, DT>(a, o, m_run, l_run, qrow, out + 16 * role, head, col, grp);
+    // a prefill unit whose rows read nothing else writes O itself (out < 0)
+    const int wout = (kCausal && out < 0) ? -1 : out + 16 * role;
+    if (computes) finish<D, DT>(a, o, m_run, l_run, qrow, wout, head, col, grp);
 }
 
 // Wave-uniform description of one single-wave task.

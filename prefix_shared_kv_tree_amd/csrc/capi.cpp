@@ -486,11 +486,11 @@ pkvt_status pkvt_prefill_attn(const pkvt_tree* t, const void* d_meta, const void
         return fail(PKVT_ERR_STALE_PLAN, "prefill_attn: the prefill plan is not uploaded to d_meta");
     const int32_t H = t->tree.H, D = t->tree.D, C = t->tree.C;
     const size_t need = static_cast<size_t>(p.n_slots) * H * (D + 2) * sizeof(float);
-    if (!workspace || workspace_bytes < need)
+    if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(PKVT_ERR_BUFFER_TOO_SMALL, "prefill_attn: workspace smaller than the plan needs");
     const int32_t* m = static_cast<const int32_t*>(d_meta);
-    float* part_o = static_cast<float*>(workspace);
-    float* part_ml = part_o + static_cast<size_t>(p.n_slots) * H * D;
+    float* part_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+    float* part_ml = part_o ? part_o + static_cast<size_t>(p.n_slots) * H * D : nullptr;
     auto s = static_cast<hipStream_t>(stream);
     pkvt::AttnArgs a{};
     a.lists = m + p.blob[pkvt::kOffLists];
@@ -513,6 +513,7 @@ pkvt_status pkvt_prefill_attn(const pkvt_tree* t, const void* d_meta, const void
     a.scale_log2e = scale * 1.4426950408889634f;
     hipError_t e = pkvt::launch_prefill(a, D, C, s);
     if (e != hipSuccess) return hip_fail(e, "prefill_attn: attention kernel");
+    if (p.n_merge == 0) return PKVT_OK;
     pkvt::MergeArgs mg{};
     mg.merge_rows = m + p.blob[pkvt::kOffMerge];
     mg.mptr = m + p.blob[pkvt::kOffMptr];

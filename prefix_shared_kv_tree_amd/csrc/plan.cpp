@@ -772,85 +772,138 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
         }
     }
 
-    // ---- segments: chains of nodes read by the same sequences -----------------
-    std::vector<int32_t> depth(static_cast<size_t>(t.N) + 1, 0);
-    std::vector<std::vector<int32_t>> segs;
-    std::vector<Range> seg_range;
-    std::vector<int32_t> seg_depth;
-    for (int32_t x : preorder) {
-        const int32_t par = t.node(x).parent;
-        depth[x] = par == root ? 0 : depth[par] + 1;
-        if (par != root && info[par].seg >= 0 && info[par].i == info[x].i && info[par].j == info[x].j) {
-            segs[info[par].seg].push_back(x);
-            info[x].seg = info[par].seg;
-        } else {
-            info[x].seg = static_cast<int32_t>(segs.size());
-            segs.push_back({x});
-            seg_range.push_back(Range{info[x].i, info[x].j});
-            seg_depth.push_back(depth[x]);
+    // ---- row blocks: depth-first rows, up to 64 per block ------------------------
+    // Each sequence's rows are cut into near-equal pieces of at most 64 rows;
+    // consecutive pieces (of neighbouring sequences, which share the longest
+    // prefixes in depth-first order) are packed into one block while it
+    // holds at most 64 rows.  A block reads, once for all its rows, the
+    // chunks common to all its sequences (the chunk-first batching of Knowl
+    // 2, over query rows), and each of its sequences reads its own chunks
+    // beyond those for its rows.  A unit reads at most S chunks; the rows of
+    // a block with a single sequence and a single unit get O directly.
+    struct Piece { int32_t p; int64_t r0, r1; };
+    std::vector<Piece> pieces;
+    for (int32_t p = 0; p < n; ++p) {
+        const int64_t len = nrows[dfs_seq[p]];
+        const int64_t k = (len + kRowsPerUnit - 1) / kRowsPerUnit;
+        int64_t r0 = dfs_start[p];
+        for (int64_t i = 0; i < k; ++i) {
+            const int64_t rows = len / k + (i < len % k ? 1 : 0);
+            pieces.push_back({p, r0, r0 + rows});
+            r0 += rows;
         }
     }
+    struct Block { size_t first, last; };          // pieces [first, last]
+    std::vector<Block> blks;
+    for (size_t i = 0; i < pieces.size(); ++i) {
+        if (!blks.empty() &&
+            pieces[i].r1 - pieces[blks.back().first].r0 <= kRowsPerUnit)
+            blks.back().last = i;
+        else
+            blks.push_back({i, i});
+    }
+    // chunks: every batch sequence's path, once
+    std::vector<int32_t> path_off(n + 1, 0);
+    for (int32_t p = 0; p < n; ++p)
+        path_off[p + 1] = path_off[p] + static_cast<int32_t>(seqs[dfs_seq[p]]->path.size());
 
-    // ---- items x row blocks -> units ------------------------------------------
-    struct PUnit { int32_t item, keys, n_chunks, row_lo, n_rows, out, key_base; int64_t cost; };
-    std::vector<std::vector<int32_t>> item_chunks;
-    std::vector<PUnit> blocks;                      // one per (item, row block); x heads below
+    struct PUnit { int32_t keys, chunk_off, n_chunks, row_lo, n_rows, out, key_base; int64_t cost; };
+    std::vector<PUnit> blocks;                      // work units (x heads below)
+    std::vector<int32_t> n_units_of(R, 0);          // units per row
+    struct Pending { int64_t r0, r1; int32_t p, k0, k1; int64_t max_pos; };
+    std::vector<Pending> pend;
+    for (const Block& bk : blks) {
+        const int32_t pa = pieces[bk.first].p, pb_ = pieces[bk.last].p;
+        const std::vector<int32_t>& path_a = seqs[dfs_seq[pa]]->path;
+        const std::vector<int32_t>& path_b = seqs[dfs_seq[pb_]]->path;
+        const int64_t r0 = pieces[bk.first].r0, r1 = pieces[bk.last].r1;
+        if (pa == pb_) {
+            int32_t max_pos = 0;
+            for (int64_t r = r0; r < r1; ++r) max_pos = std::max(max_pos, qpos[r]);
+            pend.push_back({r0, r1, pa, 0, (max_pos + C) / C, max_pos});
+            continue;
+        }
+        int32_t lcp = 0;                            // chunks common to every sequence of the block
+        while (lcp < static_cast<int32_t>(std::min(path_a.size(), path_b.size())) &&
+               path_a[lcp] == path_b[lcp])
+            ++lcp;
+        if (lcp > 0) {
+            int32_t max_pos = 0;
+            for (int64_t r = r0; r < r1; ++r) max_pos = std::max(max_pos, qpos[r]);
+            const int32_t k1 = std::min(lcp, (max_pos + C) / C);
+            pend.push_back({r0, r1, pa, 0, k1, max_pos});
+        }
+        for (size_t i = bk.first; i <= bk.last; ++i) {
+            const Piece& pc = pieces[i];
+            int32_t max_pos = 0;
+            for (int64_t r = pc.r0; r < pc.r1; ++r) max_pos = std::max(max_pos, qpos[r]);
+            const int32_t k1 = (max_pos + C) / C;
+            if (k1 <= lcp) continue;                // every key it sees is common
+            // rows before the first private key see nothing of it
+            int64_t q0 = pc.r0;
+            while (q0 < pc.r1 && qpos[q0] < static_cast<int64_t>(lcp) * C) ++q0;
+            pend.push_back({q0, pc.r1, pc.p, lcp, k1, max_pos});
+        }
+    }
+    // cut into units of at most S chunks; count units per row
+    struct Cut { int64_t r0, r1; int32_t p, k0, k1; };
+    std::vector<Cut> cuts_v;
+    for (const Pending& pd : pend) {
+        const int32_t m = pd.k1 - pd.k0;
+        const int32_t k_items = (m + S - 1) / S;
+        int32_t a2 = pd.k0;
+        for (int32_t q = 0; q < k_items; ++q) {
+            const int32_t e = a2 + m / k_items + (q < m % k_items ? 1 : 0);
+            // runs of rows that see at least the first key of this cut (a
+            // block of several sequences has no order of positions)
+            int64_t q0 = pd.r0;
+            while (q0 < pd.r1) {
+                while (q0 < pd.r1 && qpos[q0] < static_cast<int64_t>(a2) * C) ++q0;
+                int64_t q1 = q0;
+                while (q1 < pd.r1 && qpos[q1] >= static_cast<int64_t>(a2) * C) ++q1;
+                if (q1 > q0) {
+                    cuts_v.push_back({q0, q1, pd.p, a2, e});
+                    for (int64_t r = q0; r < q1; ++r) n_units_of[r]++;
+                }
+                q0 = q1;
+            }
+            a2 = e;
+        }
+    }
     std::vector<std::vector<int32_t>> mslots(R);
     int32_t n_slots = 0;
-    for (size_t sg = 0; sg < segs.size(); ++sg) {
-        const std::vector<int32_t>& ch = segs[sg];
-        const int32_t m = static_cast<int32_t>(ch.size());
-        const int32_t k_items = (m + S - 1) / S;
-        int32_t a = 0;
-        for (int32_t q = 0; q < k_items; ++q) {
-            const int32_t e = a + m / k_items + (q < m % k_items ? 1 : 0);
-            const int32_t item = static_cast<int32_t>(item_chunks.size());
-            item_chunks.emplace_back(ch.begin() + a, ch.begin() + e);
-            int64_t n_keys = 0;
-            for (int32_t i = a; i < e; ++i) n_keys += t.node(ch[i]).fill;
-            const int64_t kb = static_cast<int64_t>(seg_depth[sg] + a) * C;
-            // runs of consecutive rows that see at least the item's first key
-            std::vector<std::pair<int64_t, int64_t>> runs;
-            for (int32_t p = seg_range[sg].i; p < seg_range[sg].j; ++p) {
-                const int32_t s = dfs_seq[p];
-                const int64_t first = std::max<int64_t>(0, kb - q_from[s]);
-                if (first >= nrows[s]) continue;
-                const int64_t r0 = dfs_start[p] + first, r1 = dfs_start[p + 1];
-                if (!runs.empty() && runs.back().second == r0)
-                    runs.back().second = r1;
-                else
-                    runs.push_back({r0, r1});
-            }
-            for (const auto& run : runs) {
-                const int64_t len = run.second - run.first;
-                const int64_t kblk = (len + kRowsPerUnit - 1) / kRowsPerUnit;
-                int64_t b0 = run.first;
-                for (int64_t bi = 0; bi < kblk; ++bi) {
-                    const int64_t rows = len / kblk + (bi < len % kblk ? 1 : 0);
-                    int32_t max_pos = 0;
-                    for (int64_t r = b0; r < b0 + rows; ++r) max_pos = std::max(max_pos, qpos[r]);
-                    // keys past the block's last position are masked for every row
-                    const int64_t keys = std::min<int64_t>(n_keys, max_pos - kb + 1);
-                    PUnit u;
-                    u.item = item;
-                    u.keys = static_cast<int32_t>(keys);
-                    u.n_chunks = static_cast<int32_t>((keys + C - 1) / C);
-                    u.row_lo = static_cast<int32_t>(b0);
-                    u.n_rows = static_cast<int32_t>(rows);
-                    u.out = n_slots;
-                    u.key_base = static_cast<int32_t>(kb);
-                    u.cost = unit_cost(keys);
-                    for (int64_t r = b0; r < b0 + rows; ++r) mslots[r].push_back(n_slots + static_cast<int32_t>(r - b0));
-                    n_slots += static_cast<int32_t>(rows);
-                    blocks.push_back(u);
-                    b0 += rows;
-                }
-            }
-            a = e;
+    for (const Cut& ct : cuts_v) {
+        const Seq* sq = seqs[dfs_seq[ct.p]];
+        const int64_t kb = static_cast<int64_t>(ct.k0) * C;
+        int64_t n_keys = 0;
+        for (int32_t k = ct.k0; k < ct.k1; ++k) n_keys += t.node(sq->path[k]).fill;
+        int32_t max_pos = 0;
+        bool direct = true;
+        for (int64_t r = ct.r0; r < ct.r1; ++r) {
+            max_pos = std::max(max_pos, qpos[r]);
+            direct = direct && n_units_of[r] == 1;
         }
+        const int64_t keys = std::min<int64_t>(n_keys, max_pos - kb + 1);
+        PUnit u;
+        u.keys = static_cast<int32_t>(keys);
+        u.chunk_off = path_off[ct.p] + ct.k0;
+        u.n_chunks = static_cast<int32_t>((keys + C - 1) / C);
+        u.row_lo = static_cast<int32_t>(ct.r0);
+        u.n_rows = static_cast<int32_t>(ct.r1 - ct.r0);
+        u.key_base = static_cast<int32_t>(kb);
+        u.cost = unit_cost(keys);
+        if (direct) {
+            u.out = -1;
+        } else {
+            u.out = n_slots;
+            for (int64_t r = ct.r0; r < ct.r1; ++r)
+                mslots[r].push_back(n_slots + static_cast<int32_t>(r - ct.r0));
+            n_slots += u.n_rows;
+        }
+        blocks.push_back(u);
     }
     for (int64_t r = 0; r < R; ++r) {
-        if (mslots[r].empty()) {
+        if (n_units_of[r] == 0) {
             err = "prefill_plan: internal error, a row reads no key";
             return PKVT_ERR_INVALID_ARG;
         }
@@ -861,18 +914,38 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
         err = "prefill_plan: too many work units";
         return PKVT_ERR_INVALID_ARG;
     }
-    std::vector<int64_t> cost(n_units64);
-    for (size_t bi = 0; bi < blocks.size(); ++bi)
-        for (int32_t h = 0; h < H; ++h) cost[bi * H + h] = blocks[bi].cost;
-    std::vector<std::vector<int32_t>> wg_units;
-    std::vector<int64_t> wg_load;
-    assign_units(cost, G, wg_units, wg_load);
+    // Workgroups are spread round-robin over the 8 accelerator dies (XCDs),
+    // each with its own L2.  With heads a multiple of 8, the units of head h
+    // go to workgroups g = h (mod 8), so the blocks that re-read a head's K/V
+    // find it in one die's L2.
+    std::vector<std::vector<int32_t>> wg_units(G);
+    {
+        constexpr int32_t kDies = 8;
+        const bool by_die = H % kDies == 0 && G % (2 * kDies) == 0;
+        const int32_t groups = by_die ? kDies : 1;
+        for (int32_t x = 0; x < groups; ++x) {
+            std::vector<int64_t> cost;
+            std::vector<int32_t> ids;
+            for (size_t bi = 0; bi < blocks.size(); ++bi)
+                for (int32_t h = x; h < H; h += groups) {
+                    cost.push_back(blocks[bi].cost);
+                    ids.push_back(static_cast<int32_t>(bi * H + h));
+                }
+            std::vector<std::vector<int32_t>> wu;
+            std::vector<int64_t> wl;
+            assign_units(cost, G / groups, wu, wl);
+            for (int32_t i = 0; i < G / groups; ++i)
+                for (int32_t k : wu[i]) wg_units[i * groups + x].push_back(ids[k]);
+        }
+    }
+    std::vector<int32_t> merge_rows;
+    for (int64_t r = 0; r < R; ++r)
+        if (!mslots[r].empty()) merge_rows.push_back(static_cast<int32_t>(r));
 
     // ---- emit the blob ------------------------------------------------------------
     const int32_t Ri = static_cast<int32_t>(R);
     const int32_t n_units = static_cast<int32_t>(n_units64);
-    int64_t total_chunks = 0;
-    for (const auto& c : item_chunks) total_chunks += static_cast<int64_t>(c.size());
+    const int64_t total_chunks = path_off[n];
     int64_t n_mslots = 0;
     for (const auto& m : mslots) n_mslots += static_cast<int64_t>(m.size());
     std::vector<int32_t> blob(kHeaderWords, 0);
@@ -888,7 +961,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     section(kOffUnits, static_cast<size_t>(n_units) * 8);
     section(kOffChunks, static_cast<size_t>(total_chunks));
     section(kOffRows, R);
-    section(kOffMerge, R);
+    section(kOffMerge, merge_rows.size());
     section(kOffMptr, R + 1);
     section(kOffMslots, static_cast<size_t>(n_mslots));
     section(kOffSeqlen, R);
@@ -898,12 +971,10 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
         err = "prefill_plan: metadata too large";
         return PKVT_ERR_INVALID_ARG;
     }
-    std::vector<int32_t> chunk_off(item_chunks.size());
     {
-        int32_t coff = 0;
-        for (size_t i = 0; i < item_chunks.size(); ++i) {
-            chunk_off[i] = coff;
-            for (int32_t id : item_chunks[i]) blob[blob[kOffChunks] + coff++] = id;
+        for (int32_t p = 0; p < n; ++p) {
+            const std::vector<int32_t>& path = seqs[dfs_seq[p]]->path;
+            std::copy(path.begin(), path.end(), &blob[blob[kOffChunks] + path_off[p]]);
         }
         int32_t ua = 0;
         for (int32_t g = 0; g < G; ++g) {
@@ -913,7 +984,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
                 const PUnit& u = blocks[ui / H];
                 UnitDesc d{};
                 d.n_keys = u.keys;
-                d.chunk_off = chunk_off[u.item];
+                d.chunk_off = u.chunk_off;
                 d.n_chunks = u.n_chunks;
                 d.head = ui % H;
                 d.row_lo = u.row_lo;
@@ -928,9 +999,9 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     }
     {
         int32_t at = 0;
+        for (size_t m = 0; m < merge_rows.size(); ++m) blob[blob[kOffMerge] + m] = merge_rows[m];
         for (int32_t r = 0; r < Ri; ++r) {
             blob[blob[kOffRows] + r] = row_of[r];
-            blob[blob[kOffMerge] + r] = r;
             blob[blob[kOffQpos] + r] = qpos[r];
             blob[blob[kOffMptr] + r] = at;
             for (int32_t sl : mslots[r]) blob[blob[kOffMslots] + at++] = sl;
@@ -944,7 +1015,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     blob[kNTasks] = 0;
     blob[kNUnits] = n_units;
     blob[kNSlots] = n_slots;
-    blob[kNMerge] = Ri;
+    blob[kNMerge] = static_cast<int32_t>(merge_rows.size());
     blob[kTotalWords] = static_cast<int32_t>(blob.size());
 
     int64_t unique = 0, logical = 0;
@@ -959,14 +1030,14 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     plan.b = Ri;
     plan.q_order.assign(seq_ids, seq_ids + n);
     plan.opts = in_opts;
-    plan.phase1_items = static_cast<int32_t>(item_chunks.size());
+    plan.phase1_items = static_cast<int32_t>(blocks.size());
     plan.phase2_items = 0;
     plan.n_waves = 0;
     plan.n_wg = G;
     plan.n_tasks = 0;
     plan.n_units = n_units;
     plan.n_slots = n_slots;
-    plan.n_merge = Ri;
+    plan.n_merge = static_cast<int32_t>(merge_rows.size());
     plan.split1_chunks = S;
     plan.split2_chunks = 0;
     int32_t shared = 0;

@@ -184,6 +184,8 @@ def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: 
     assert len(plan["waves"]) == 0 and len(plan["tasks"]) == 0
     seen = defaultdict(lambda: defaultdict(int))        # (row, head) -> position -> count
     slot_rows = {}
+    direct = defaultdict(int)                           # row -> units writing O directly (head 0)
+    units_of = defaultdict(int)                         # row -> units reading it (head 0)
     for u, ch in zip(plan["units"], plan["unit_chunks"]):
         n_keys, chunk_off, n_chunks, head, row_lo, n_rows, out, key_base = [int(v) for v in u]
         assert 1 <= n_rows <= ROWS_PER_UNIT and 1 <= n_chunks <= 64 and 0 <= head < heads
@@ -198,8 +200,12 @@ def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: 
             for pos in range(key_base, min(key_base + n_keys, p + 1)):
                 seen[(r, head)][pos] += 1
             if head == 0:
-                assert out + i not in slot_rows, "slot written twice"
-                slot_rows[out + i] = r
+                units_of[r] += 1
+                if out < 0:
+                    direct[r] += 1
+                else:
+                    assert out + i not in slot_rows, "slot written twice"
+                    slot_rows[out + i] = r
     for r in range(R):
         s, p = rows_meta[caller[r]]
         for h in range(heads):
@@ -207,7 +213,12 @@ def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: 
             assert sorted(got) == list(range(p + 1)), f"row {r} head {h} keys"
             assert all(v == 1 for v in got.values()), f"row {r} head {h} reads a key twice"
     assert set(slot_rows) == set(range(plan["n_slots"]))
-    assert [int(m) for m in plan["merge"]] == list(range(R))
+    merge = [int(m) for m in plan["merge"]]
+    assert merge == sorted(set(slot_rows.values())), "merge rows are the rows with partials"
     for r in range(R):
         sl = sorted(int(x) for x in plan["mslots"][plan["mptr"][r]:plan["mptr"][r + 1]])
         assert sl == sorted(k for k, v in slot_rows.items() if v == r)
+        if direct[r]:
+            assert direct[r] == 1 and units_of[r] == 1 and not sl, "a direct row reads one unit only"
+        else:
+            assert sl

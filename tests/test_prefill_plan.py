@@ -47,8 +47,9 @@ def test_prefill_batch_plans(b, prefix, new, c):
 
 
 def test_shared_prefix_read_once_per_row_block():
-    """64 sequences x 8 new tokens over a stored 4-chunk prefix: 512 rows,
-    so each prefix chunk is read by 8 row blocks (per head), not 64."""
+    """64 sequences x 8 new tokens over a stored 4-chunk prefix: 512 rows in
+    blocks of 8 sequences, so each prefix chunk is read by 8 row blocks (per
+    head), not 64."""
     pb = W.prefill_batch(3, 64, 64, 8, h=1, d=64, c=16, with_kv=False)
     t = _tree(1, 64, 16)
     try:
@@ -123,5 +124,36 @@ def test_prefill_plan_errors_and_staleness():
         with pytest.raises(B.PkvtError) as e:
             B.pkvt_prefill_upload(t, 0x1000, 1 << 20)
         assert e.value.status == "STALE_PLAN"
+    finally:
+        B.pkvt_tree_destroy(t)
+
+
+def test_single_sequence_blocks_write_output_directly():
+    """Sequences with many new rows: every block holds rows of one sequence
+    and reads its whole visible path in one unit, so no row needs a merge."""
+    pb = W.prefill_batch(5, 4, 96, 130, h=2, d=64, c=16, with_kv=False)
+    t = _tree(2, 64, 16)
+    try:
+        B.pkvt_tree_build(t, [pb.w.segments[s].tokens for s in pb.residents])
+        ids, _ = B.pkvt_tree_build(t, [pb.w.seq_tokens(u) for u in pb.seqs])
+        plan, info = _check(t, ids, pb.q_from, 16, 2)
+        assert info["slots"] == 0 and info["merge_rows"] == 0
+        assert all(int(u[6]) == -1 for u in plan["units"])
+    finally:
+        B.pkvt_tree_destroy(t)
+
+
+def test_heads_follow_dies():
+    """With 8k heads, the units of head h run on workgroups g = h (mod 8)."""
+    pb = W.prefill_batch(9, 6, 64, 40, h=16, d=64, c=16, with_kv=False)
+    t = _tree(16, 64, 16)
+    try:
+        B.pkvt_tree_build(t, [pb.w.segments[s].tokens for s in pb.residents])
+        ids, _ = B.pkvt_tree_build(t, [pb.w.seq_tokens(u) for u in pb.seqs])
+        plan, _ = _check(t, ids, pb.q_from, 16, 16, workgroups=64)
+        at = 0
+        for g, (first, cnt) in enumerate(plan["wg_units"]):
+            for k in range(first, first + cnt):
+                assert int(plan["units"][k][3]) % 8 == g % 8
     finally:
         B.pkvt_tree_destroy(t)
