@@ -386,6 +386,185 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
     if (computes) finish<D, DT>(a, o, m_run, l_run, qrow, wout, head, col, grp);
 }
 
+// A prefill unit: like run_unit with the causal mask, but every wave
+// computes RT tiles of 16 query rows (a unit covers up to 64 RT rows), so
+// each K/V fragment read from LDS feeds RT matrix instructions, and the
+// unit may read up to 128 chunks (ids in two registers per lane).  From
+// head_dim 128 on, K/V go from memory straight into LDS (global_load_lds,
+// 16 bytes per lane, lanes at consecutive 16-byte LDS addresses) into two
+// images used in turn: the loads of step s + 1 fly while step s is computed,
+// with one barrier per step and no staging registers.  At head_dim 64 a V
+// load spans two padded 4-key groups, so the register path is kept.
+template <int D, int C, int RT>
+__device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wave, int lane,
+                                              char* img0, char* img1) {
+    constexpr int KS = D / 32, DT = D / 16, NT = Step<D>::kTiles;
+    constexpr int kPer = Img<D>::kPieces / kWaves;
+    constexpr int NL = kPer / 64;
+    constexpr int KP = Img<D>::kPiecesK;
+    constexpr int TPW = kPer >= 2 * D ? kPer / (2 * D) : 1;
+    constexpr bool kDirect = D >= 128;
+    static_assert(kPer % 64 == 0 && (2 * D) % 64 == 0 && (kPer % (2 * D) == 0 || NT == 1) &&
+                  NL % TPW == 0, "piece split");
+    static_assert(!kDirect || (D / 2) % 64 == 0, "a direct load must stay inside one V group");
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+    const int H = a.H;
+    const int n_keys = u[0];
+    cint* chunks = meta(a.chunks) + u[1];
+    const int n_chunks = u[2];
+    const int ids_lo = lane_ids(chunks, n_chunks, lane);
+    const int ids_hi = lane + 64 < n_chunks ? chunks[lane + 64] : 0;
+    const int head = u[3];
+    const int row_lo = u[4];
+    const int n_rows = u[5];
+    const int out = u[6];
+    const int key_base = u[7];
+    const int role = wave;
+    const bool computes = 16 * RT * role < n_rows;
+    const int n_steps = (n_keys + Step<D>::kKeys - 1) / Step<D>::kKeys;
+    const size_t slice = static_cast<size_t>(C) * D * 2;
+    const char* kbase = static_cast<const char*>(a.kpool) + static_cast<size_t>(head) * slice;
+    const char* vbase = static_cast<const char*>(a.vpool) + static_cast<size_t>(head) * slice;
+    const size_t cstride = static_cast<size_t>(H) * slice;
+    auto chunk_of = [&](int step, int tt) {
+        const int k = min((step * Step<D>::kKeys + 16 * tt) / C, (n_keys - 1) / C);
+        return k < 64 ? __builtin_amdgcn_readlane(ids_lo, k) : __builtin_amdgcn_readlane(ids_hi, k - 64);
+    };
+    const int ta = NT == 1 ? 0 : TPW * (role & 1);
+    // memory address of this lane's piece of load i of a step
+    auto src = [&](int step, int i, const int (&id)[TPW]) {
+        const int j0 = role * kPer + i * 64;
+        const bool is_k = j0 < KP;
+        const int jj = is_k ? j0 : j0 - KP;
+        const int ts = tile_start<D>(step, jj / (2 * D), n_keys);
+        const int rem = jj % (2 * D) + lane;
+        const size_t cbytes = static_cast<size_t>(id[i / (NL / TPW)]) * cstride;
+        const char* kp = kbase + cbytes + (static_cast<size_t>(rem >> 4) * C + ts % C + (rem & 15)) * 16;
+        const char* vp = vbase + cbytes + static_cast<size_t>((ts % C) / 4) * (D * 8) + rem * 16;
+        return reinterpret_cast<const h8*>(is_k ? kp : vp);
+    };
+    // LDS byte offset of the piece a lane of load i writes (lane offset excluded
+    // when lane_part is false)
+    auto dst = [&](int i, bool lane_part) {
+        const int j = role * kPer + i * 64 + (lane_part ? lane : 0);
+        const int jv = j - KP;
+        const int tt = jv / (2 * D);
+        const int rem = jv % (2 * D);
+        const int voff = Img<D>::kBytesK + (tt * 4 + rem / (D / 2)) * Img<D>::kGroupV +
+                         (rem % (D / 2)) * 16;
+        return j < KP ? j * 16 : voff;
+    };
+
+    h8 stg[kDirect ? 1 : NL];
+    auto stage = [&](int step, char* img) {
+        int id[TPW];
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) id[k] = chunk_of(step, ta + k);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            if constexpr (kDirect)
+                __builtin_amdgcn_global_load_lds(src(step, i, id),
+                                                 (__attribute__((address_space(3))) void*)(img + dst(i, false)),
+                                                 16, 0, 0);
+            else
+                stg[i] = __builtin_nontemporal_load(src(step, i, id));
+        }
+    };
+    auto commit = [&](char* img) {
+        if constexpr (!kDirect) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) *reinterpret_cast<h8*>(img + dst(i, true)) = stg[i];
+        }
+    };
+
+    h8 qb[RT][KS];
+    int qrow[RT];
+    int lim[RT];
+    f4 o[RT][DT];
+    float m_run[RT], l_run[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int r = 16 * (RT * role + rt) + col;
+        qrow[rt] = computes && r < n_rows ? a.rows[row_lo + r] : -1;
+        lim[rt] = computes && r < n_rows ? min(n_keys, a.qpos[row_lo + r] + 1 - key_base) : n_keys;
+        const _Float16* qp = static_cast<const _Float16*>(a.q) +
+                             (static_cast<size_t>(qrow[rt] < 0 ? 0 : qrow[rt]) * H + head) * D + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qb[rt][ks] = qrow[rt] >= 0 ? *reinterpret_cast<const h8*>(qp + 32 * ks) : h8{};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
+        m_run[rt] = -INFINITY;
+        l_run[rt] = 0.f;
+    }
+
+    auto compute = [&](const char* img, int step) {
+        f4 s[RT][NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) s[rt][tt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const h8 kf = *reinterpret_cast<const h8*>(
+                    img + ((tt * (D / 8) + 4 * ks + grp) * 16 + col) * 16);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    s[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qb[rt][ks], s[rt][tt], 0, 0, 0);
+            }
+        }
+        h4 pq[RT][NT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            softmax_step<NT, DT>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt], step, lim[rt], grp,
+                                 a.scale_log2e);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            h4 v[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                v[tt] = mask_v(
+                    *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
+                                                 (tt * 4 + grp) * Img<D>::kGroupV + (16 * dt + col) * 8),
+                    step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) o[rt][dt] = pv_tile<NT>(o[rt][dt], v, pq[rt]);
+        }
+    };
+
+    if constexpr (kDirect) {
+        // step s is computed from image s % 2 while step s + 1 loads into the other
+        auto body = [&](char* cur, char* nxt, int step) {
+            __syncthreads();                 // own loads done (the barrier waits for them), every
+                                             // wave done with step - 1's image
+            if (step + 1 < n_steps) stage(step + 1, nxt);
+            if (computes) compute(cur, step);
+        };
+        stage(0, img0);
+        for (int step = 0; step < n_steps; step += 2) {
+            body(img0, img1, step);
+            if (step + 1 < n_steps) body(img1, img0, step + 1);
+        }
+        __syncthreads();                     // the next unit reuses the images
+    } else {
+        stage(0, img0);
+        for (int step = 0; step < n_steps; ++step) {
+            __syncthreads();
+            commit(img0);
+            __syncthreads();
+            if (step + 1 < n_steps) stage(step + 1, img0);
+            if (computes) compute(img0, step);
+        }
+    }
+    if (computes) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            finish<D, DT>(a, o[rt], m_run[rt], l_run[rt], qrow[rt],
+                          out < 0 ? -1 : out + 16 * (RT * role + rt), head, col, grp);
+    }
+}
+
 // Wave-uniform description of one single-wave task.
 struct Task {
     int ids;                 // the task's chunk ids, one per lane (lane_ids)
@@ -547,13 +726,15 @@ void attn_kernel(AttnArgs a) {
 template <int D, int C>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[Img<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) char img0[Img<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) char img1[D >= 128 ? Img<D>::kBytes : 16];
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
     const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
     for (int k = 0; k < ucount; ++k)
-        run_unit<D, C, true>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
+        run_unit_wide<D, C, prefill_row_tiles(D)>(a, meta(a.units) + 8 * (ufirst + k), wave, lane,
+                                                  img0, img1);
 }
 
 // Fold every partial of one (sequence, head) with attn_reduce and divide.

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "shapes.h"
+
 namespace pkvt {
 
 struct AttnArgs {

@@ -717,9 +717,10 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     }
     const int32_t G = in_opts.workgroups > 0 ? in_opts.workgroups : kDefaultWorkgroups;
     const int32_t lanes = G * kWavesPerWg;
-    const int32_t S = in_opts.phase1_chunks > 0 ? std::min(in_opts.phase1_chunks, kMaxItemChunks)
-                                                : kMaxItemChunks;
+    const int32_t S = in_opts.phase1_chunks > 0 ? std::min(in_opts.phase1_chunks, kPrefillMaxChunks)
+                                                : kPrefillMaxChunks;
     const int32_t C = t.C;
+    const int32_t kRows = 16 * kWavesPerWg * prefill_row_tiles(t.D);   // rows per work unit
 
     // ---- validate; rows per sequence ------------------------------------------
     std::vector<const Seq*> seqs(n);
@@ -772,11 +773,11 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
         }
     }
 
-    // ---- row blocks: depth-first rows, up to 64 per block ------------------------
-    // Each sequence's rows are cut into near-equal pieces of at most 64 rows;
+    // ---- row blocks: depth-first rows, up to kRows per block ------------------------
+    // Each sequence's rows are cut into near-equal pieces of at most kRows rows;
     // consecutive pieces (of neighbouring sequences, which share the longest
     // prefixes in depth-first order) are packed into one block while it
-    // holds at most 64 rows.  A block reads, once for all its rows, the
+    // holds at most kRows rows.  A block reads, once for all its rows, the
     // chunks common to all its sequences (the chunk-first batching of Knowl
     // 2, over query rows), and each of its sequences reads its own chunks
     // beyond those for its rows.  A unit reads at most S chunks; the rows of
@@ -785,7 +786,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     std::vector<Piece> pieces;
     for (int32_t p = 0; p < n; ++p) {
         const int64_t len = nrows[dfs_seq[p]];
-        const int64_t k = (len + kRowsPerUnit - 1) / kRowsPerUnit;
+        const int64_t k = (len + kRows - 1) / kRows;
         int64_t r0 = dfs_start[p];
         for (int64_t i = 0; i < k; ++i) {
             const int64_t rows = len / k + (i < len % k ? 1 : 0);
@@ -797,7 +798,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     std::vector<Block> blks;
     for (size_t i = 0; i < pieces.size(); ++i) {
         if (!blks.empty() &&
-            pieces[i].r1 - pieces[blks.back().first].r0 <= kRowsPerUnit)
+            pieces[i].r1 - pieces[blks.back().first].r0 <= kRows)
             blks.back().last = i;
         else
             blks.push_back({i, i});

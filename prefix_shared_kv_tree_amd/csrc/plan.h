@@ -25,6 +25,7 @@
 #include <string>
 #include <vector>
 
+#include "shapes.h"
 #include "tree.h"
 
 namespace pkvt {
@@ -123,14 +124,15 @@ int make_plan(const Tree& tree, int32_t b, const int32_t* q_order, const PlanOpt
 
 // Prefill plan: the query rows are positions q_from[s] .. len - 1 of each of
 // the n sequences seq_ids[s] (in that order, positions ascending), and a row
-// at position p attends to its sequence's tokens 0 .. p.  Every chunk on a
-// batch path is read once per block of up to 64 rows that see it: the rows
-// of all batch sequences that share it (a stored prefix) are batched, and a
-// sequence's own new chunks are read by its rows with the causal mask
+// at position p attends to its sequence's tokens 0 .. p.  Rows are cut into
+// blocks of up to 64 * prefill_row_tiles(d) depth-first rows; a block reads
+// the chunks common to its sequences once for all its rows and each
+// sequence's own chunks for that sequence's rows, with the causal mask
 // applied per row in the kernel.  The blob has the decode layout with no
 // single-wave tasks, plus qpos [R] (position of every depth-first row); b is
-// the row count R, every row is merged from its partials.  Options used:
-// phase1_chunks (item length cap, 0 = 64 chunks) and workgroups.
+// the row count R; rows read by one unit only get O from it directly, the
+// others are merged from their partials.  Options used: phase1_chunks
+// (chunks per unit, 0 = kPrefillMaxChunks) and workgroups.
 int make_prefill_plan(const Tree& tree, int32_t n, const int32_t* seq_ids, const int64_t* q_from,
                       const PlanOpts& opts, Plan& plan, std::string& err);
 

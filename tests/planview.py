@@ -167,7 +167,8 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
             assert int(w[5]) <= max_rows
 
 
-def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: int, heads: int):
+def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: int, heads: int,
+                       d: int = 64):
     """Every prefill row (sequence s, position p) reads exactly the keys
     0 .. p of s, each once, from the chunks on s's path, in units of at most
     64 rows whose first key it can see; its partial slots are its merge list."""
@@ -188,7 +189,7 @@ def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: 
     units_of = defaultdict(int)                         # row -> units reading it (head 0)
     for u, ch in zip(plan["units"], plan["unit_chunks"]):
         n_keys, chunk_off, n_chunks, head, row_lo, n_rows, out, key_base = [int(v) for v in u]
-        assert 1 <= n_rows <= ROWS_PER_UNIT and 1 <= n_chunks <= 64 and 0 <= head < heads
+        assert 1 <= n_rows <= (128 if d <= 128 else 64) and 1 <= n_chunks <= 128 and 0 <= head < heads
         assert (n_keys + c - 1) // c == n_chunks and key_base % c == 0
         for i in range(n_rows):
             r = row_lo + i
