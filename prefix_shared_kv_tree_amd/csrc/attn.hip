@@ -386,7 +386,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
     if (computes) finish<D, DT>(a, o, m_run, l_run, qrow, wout, head, col, grp);
 }
 
-// A prefill unit: like run_unit with the causal mask, but every wave
+// A wide unit: like run_unit (with the causal mask for prefill), but every wave
 // computes RT tiles of 16 query rows (a unit covers up to 64 RT rows), so
 // each K/V fragment read from LDS feeds RT matrix instructions, and the
 // unit may read up to 128 chunks (ids in two registers per lane).  From
@@ -395,7 +395,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 // images used in turn: the loads of step s + 1 fly while step s is computed,
 // with one barrier per step and no staging registers.  At head_dim 64 a V
 // load spans two padded 4-key groups, so the register path is kept.
-template <int D, int C, int RT>
+template <int D, int C, int RT, bool kCausal>
 __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wave, int lane,
                                               char* img0, char* img1) {
     constexpr int KS = D / 32, DT = D / 16, NT = Step<D>::kTiles;
@@ -419,7 +419,7 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     const int row_lo = u[4];
     const int n_rows = u[5];
     const int out = u[6];
-    const int key_base = u[7];
+    const int key_base = kCausal ? u[7] : 0;
     const int role = wave;
     const bool computes = 16 * RT * role < n_rows;
     const int n_steps = (n_keys + Step<D>::kKeys - 1) / Step<D>::kKeys;
@@ -487,7 +487,8 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     for (int rt = 0; rt < RT; ++rt) {
         const int r = 16 * (RT * role + rt) + col;
         qrow[rt] = computes && r < n_rows ? a.rows[row_lo + r] : -1;
-        lim[rt] = computes && r < n_rows ? min(n_keys, a.qpos[row_lo + r] + 1 - key_base) : n_keys;
+        lim[rt] = kCausal && computes && r < n_rows ? min(n_keys, a.qpos[row_lo + r] + 1 - key_base)
+                                                    : n_keys;
         const _Float16* qp = static_cast<const _Float16*>(a.q) +
                              (static_cast<size_t>(qrow[rt] < 0 ? 0 : qrow[rt]) * H + head) * D + 8 * grp;
 #pragma unroll
@@ -536,8 +537,11 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     if constexpr (kDirect) {
         // step s is computed from image s % 2 while step s + 1 loads into the other
         auto body = [&](char* cur, char* nxt, int step) {
-            __syncthreads();                 // own loads done (the barrier waits for them), every
-                                             // wave done with step - 1's image
+            // The loads into LDS count as vector-memory operations: wait for this
+            // wave's own (the workgroup barrier alone does not), then for every
+            // wave -- the image of step is complete and nobody reads step - 1's.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
             if (step + 1 < n_steps) stage(step + 1, nxt);
             if (computes) compute(cur, step);
         };
@@ -604,7 +608,9 @@ void attn_kernel(AttnArgs a) {
     constexpr int KS = D / 32;     // 32-dim k-steps of Q K^T
     constexpr int DT = D / 16;     // 16-dim output tiles of P V
     constexpr int NT = Step<D>::kTiles;
+    // units: two LDS images, filled in turn straight from memory (D >= 128)
     __shared__ __attribute__((aligned(16))) char lds[Img<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) char lds1[D >= 128 ? Img<D>::kBytes : 16];
     const int H = a.H;
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -615,8 +621,12 @@ void attn_kernel(AttnArgs a) {
     {
         const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
         const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
-        for (int k = 0; k < ucount; ++k)
-            run_unit<D, C, false>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
+        for (int k = 0; k < ucount; ++k) {
+            if constexpr (D >= 128)
+                run_unit_wide<D, C, 1, false>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds, lds1);
+            else
+                run_unit<D, C, false>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
+        }
     }
 
     // ---- this wave's single-wave tasks ------------------------------------------
@@ -733,8 +743,8 @@ void prefill_kernel(AttnArgs a) {
     const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
     const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
     for (int k = 0; k < ucount; ++k)
-        run_unit_wide<D, C, prefill_row_tiles(D)>(a, meta(a.units) + 8 * (ufirst + k), wave, lane,
-                                                  img0, img1);
+        run_unit_wide<D, C, prefill_row_tiles(D), true>(a, meta(a.units) + 8 * (ufirst + k), wave,
+                                                        lane, img0, img1);
 }
 
 // Fold every partial of one (sequence, head) with attn_reduce and divide.
