@@ -379,6 +379,48 @@ def summarize_loop_trace(args):
     print("\n".join(out + [""]))
 
 
+def summarize_prefill(args):
+    """Kernel trace (--trace-csv) and MFMA counters (--mfma-csv) of a
+    `bench.py --prefill --prefill-case N` run, with that run's JSON line
+    (--bench-log), as the committed prefill-kernel summary."""
+    import csv as _csv
+    bench_row = None
+    for line in open(args.bench_log):
+        if line.startswith('{"prefill"'):
+            bench_row = json.loads(line)["prefill"][0]
+    stats = list(_csv.DictReader(open(args.trace_csv)))
+    kname = "prefill_kernel"
+    kern = [r for r in stats if kname in r["Name"]][0]
+    avg_ns = float(kern["AverageNs"])
+    m, n = _counter_means(args.mfma_csv, kname)
+    flops_issued = m["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512
+    useful = bench_row["useful_gflop"] * 1e9
+    busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (m["GRBM_GUI_ACTIVE"] / 8 * SIMDS)
+    out = [f"# prefill_kernel<{bench_row['d']},{bench_row['c']}> -- workload {bench_row['workload']}", "",
+           f"Prefill of {bench_row['b']} sequences over a stored {bench_row['prefix']}-token prefix "
+           f"({bench_row['rows']} query rows; h = {bench_row['h']}, d = {bench_row['d']}, c = {bench_row['c']}; "
+           "Q, K/V drawn on the device).", "",
+           "Commands (GPU box, repository root as $R):", "", "```"] + list(args.command) + [
+           "```", "",
+           "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for r in stats:
+        nm = r["Name"].replace("pkvt::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        out.append(f"| `{nm[:70]}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} |")
+    out += ["", "| quantity | value |", "|---|---|",
+            f"| useful FLOPs per launch (4 d per row, head, visible key) | {useful:,.0f} |",
+            f"| MFMA f16 FLOPs issued per launch (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512, mean of "
+            f"{n.get('SQ_INSTS_VALU_MFMA_MOPS_F16', 0)} dispatches) | {flops_issued:,.0f} |",
+            f"| issued / useful (masked keys, padded tiles) | {flops_issued / useful:.3f} |",
+            f"| prefill_kernel average (us, kernel trace) | {avg_ns / 1e3:.1f} |",
+            f"| useful TFLOP/s over that average | {useful / avg_ns / 1e3:.1f} |",
+            f"| useful fraction of the {MFMA_F16_PEAK_TFLOPS:.0f} TFLOP/s dense f16 peak | "
+            f"{useful / avg_ns / 1e3 / MFMA_F16_PEAK_TFLOPS * 100:.1f} % |",
+            f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x {SIMDS})) | {busy * 100:.1f} % |",
+            "", f"Same run, bench.py: {bench_row['shared_us_per_layer']} us per layer "
+            f"(prefill kernel + merge, HIP events), {bench_row['shared_tflops']} TFLOP/s.", ""]
+    print("\n".join(out))
+
+
 def copy_probe(torch, mib):
     """A plain copy of known size (torch's elementwise kernel: `mib` MiB read,
     `mib` MiB written), launched three times.  Under a counter-collection run
@@ -674,6 +716,9 @@ def main():
                     help="(no GPU) print the kernel-trace summary of --config from a rocprofv3 stats CSV")
     ap.add_argument("--bench-log")
     ap.add_argument("--trace-dir")
+    ap.add_argument("--summarize-prefill", action="store_true",
+                    help="(no GPU) print the prefill-kernel summary from --trace-csv, --mfma-csv "
+                         "and --bench-log")
     ap.add_argument("--summarize-loop-trace", action="store_true",
                     help="(no GPU) print the decode-loop trace summary from a rocprofv3 output "
                          "directory (--trace-dir) and the run's log (--bench-log)")
@@ -705,6 +750,9 @@ def main():
         return
     if args.summarize_loop_trace:
         summarize_loop_trace(args)
+        return
+    if args.summarize_prefill:
+        summarize_prefill(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the decode attention of one "

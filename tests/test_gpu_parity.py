@@ -295,3 +295,19 @@ def test_single_key_bit_exact_head_dim_256():
         K, V = A.materialize(w, u)
         assert np.array_equal(got[u], V[0].astype(np.float16))
     ds.close()
+
+
+def test_items_of_64_chunks_and_long_private_contexts():
+    """Items at the 64-chunk limit (one chunk id per lane, lane 63 used) and
+    two sequences with ~20K private tokens each over a shared 4096-token
+    prefix: many phase-2 pieces merged per row."""
+    _torch()
+    w = W.one_prefix(777, 3, 4096, [20000, 17, 12345], h=4, d=128, c=64)
+    rows = [0, 1, 2]
+    ref = A.attention_batch(w, seqs=rows)
+    for p1, p2 in [(64, 64), (0, 0), (7, 3)]:
+        ds = _setup(w, phase1_chunks=p1, phase2_chunks=p2)
+        err = _err(_run(ds), ref)
+        print(f"\n[case] long contexts p1={p1} p2={p2} err={err:.3e} info={ds.info}", flush=True)
+        assert err <= TOL
+        ds.close()

@@ -196,3 +196,20 @@ def test_chunked_prefill_matches_whole_prefill():
     print(f"\n[case] chunked vs whole prefill: max diff {np.abs(results[0] - results[1]).max():.3e}",
           flush=True)
     assert float(np.abs(results[0] - results[1]).max()) <= 2 * TOL
+
+
+@pytest.mark.parametrize("d,c,prefix,new", [(128, 16, 90 * 16 + 5, [40, 300]), (64, 16, 1700, 70),
+                                            (256, 16, 1500, [3, 64])])
+def test_prefill_units_over_64_chunks(d, c, prefix, new):
+    """Rows whose visible path is longer than 64 chunks: a unit reads up to
+    128 chunks, its chunk ids held in two registers per lane."""
+    _torch()
+    b = 1 if np.isscalar(new) else len(new)
+    pb = W.prefill_batch(31 + d, b, prefix, new, h=2, d=d, c=c)
+    ps = _setup(pb)
+    blob_units = ps.info["wg_units"]
+    err = float(np.abs(_run(ps) - A.prefill_attention(pb.w, pb.seqs, pb.q_from, pb.q)).max())
+    print(f"\n[case] prefill > 64 chunks d={d} c={c} prefix={prefix} new={new} err={err:.3e} "
+          f"units={blob_units}", flush=True)
+    assert err <= TOL
+    ps.close()
