@@ -131,21 +131,34 @@ __device__ __forceinline__ void qk(f4 (&s)[NT], const h8 (&kr)[NT][KS], const h8
 // 16tt + 4grp + i.  Returns P^T in fp16, pq[tt] = keys 16tt + 4grp .. +3 of
 // row col (the B-operand layout of the P V product), and rescales o to the
 // new running max.
-template <int NT, int DT>
+// kSkip (compute-bound prefill units): the key mask and the rescale of o
+// are skipped, wave-wide, on steps where no lane needs them (no lane's keys
+// end inside the step; no lane's running max moved).
+template <int NT, int DT, bool kSkip = false>
 __device__ __forceinline__ void softmax_step(f4 (&s)[NT], h4 (&pq)[NT], f4 (&o)[DT], float& m_run,
                                              float& l_run, int step, int n_valid, int grp,
                                              float scale_log2e) {
     const int key0 = step * 16 * NT;
     const bool tail = key0 + 16 * NT > n_valid;
     float mx = -INFINITY;
+    if (kSkip && !__any(tail)) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x = s[tt][i] * scale_log2e;
-            if (tail && key0 + 16 * tt + 4 * grp + i >= n_valid) x = -INFINITY;
-            s[tt][i] = x;
-            mx = fmaxf(mx, x);
+            for (int i = 0; i < 4; ++i) {
+                s[tt][i] *= scale_log2e;
+                mx = fmaxf(mx, s[tt][i]);
+            }
+    } else {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x = s[tt][i] * scale_log2e;
+                if (tail && key0 + 16 * tt + 4 * grp + i >= n_valid) x = -INFINITY;
+                s[tt][i] = x;
+                mx = fmaxf(mx, x);
+            }
         }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -161,8 +174,10 @@ __device__ __forceinline__ void softmax_step(f4 (&s)[NT], h4 (&pq)[NT], f4 (&o)[
         lsum += static_cast<float>(p);
     }
     l_run = l_run * alpha + lsum;
+    if (!kSkip || __any(alpha != 1.0f)) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+        for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
 }
 
 // Keys past the end hold stale pool contents (possibly NaN bit patterns):
@@ -518,8 +533,8 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         h4 pq[RT][NT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-            softmax_step<NT, DT>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt], step, lim[rt], grp,
-                                 a.scale_log2e);
+            softmax_step<NT, DT, kCausal>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt], step, lim[rt],
+                                          grp, a.scale_log2e);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             h4 v[NT];
