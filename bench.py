@@ -252,7 +252,7 @@ def summarize_pmc(args):
             rec["mfma_busy_frac"] = round(m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS), 4)
     out = [f"# {rec['kernel']} -- HBM traffic per launch, workload {args.config}", "",
            f"Workload: {W.CONFIG_DESCRIPTIONS[args.config]}.", "",
-           "Commands (GPU box, repository root as $R):", "", "```"]
+           "Commands (repository root as $R):", "", "```"]
     out += [c for c in args.command]
     out += ["```", "",
             "FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch and scaled by what",
@@ -298,7 +298,7 @@ def summarize_trace(args):
                 bench = json.loads(line)
     out = [f"# {ATTN_KERNEL} -- kernel trace, workload {args.config}", "",
            f"Workload: {W.CONFIG_DESCRIPTIONS[args.config]}.", "",
-           "Commands (GPU box, repository root as $R):", "", "```"] + list(args.command) + [
+           "Commands (repository root as $R):", "", "```"] + list(args.command) + [
            "```", "",
            "| kernel | calls | total ns | avg ns | % | min ns | max ns | stddev |",
            "|---|---|---|---|---|---|---|---|"]
@@ -355,7 +355,7 @@ def summarize_loop_trace(args):
            f"Workload: {W.CONFIG_DESCRIPTIONS[args.config]}; {L} layers, decoded for "
            f"{warm} + {T} (pipelined) + {loop['steps_synced']} (synchronised) steps, a row "
            f"replaced every {loop['churn_every']} steps.", "",
-           "Commands (GPU box, repository root as $R):", "", "```"] + list(args.command) + [
+           "Commands (repository root as $R):", "", "```"] + list(args.command) + [
            "```", "",
            "| kernel | calls | total ns | avg ns | % | min ns | max ns |",
            "|---|---|---|---|---|---|---|"]
@@ -400,7 +400,7 @@ def summarize_prefill(args):
            f"Prefill of {bench_row['b']} sequences over a stored {bench_row['prefix']}-token prefix "
            f"({bench_row['rows']} query rows; h = {bench_row['h']}, d = {bench_row['d']}, c = {bench_row['c']}; "
            "Q, K/V drawn on the device).", "",
-           "Commands (GPU box, repository root as $R):", "", "```"] + list(args.command) + [
+           "Commands (repository root as $R):", "", "```"] + list(args.command) + [
            "```", "",
            "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
     for r in stats:
@@ -755,7 +755,7 @@ def main():
         summarize_prefill(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the decode attention of one "
+        print("bench.py measures one GPU only: it runs the decode attention of one "
               "GPU's share and has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

@@ -1,6 +1,6 @@
 """Build libpkvt.so in-tree: host C++ with g++, HIP kernels with hipcc for gfx950.
 
-    python -m prefix_shared_kv_tree_amd.build        # or __graft_entry__.build()
+    python -m prefix_shared_kv_tree_amd.build
 
 Objects go to ``_build/`` at the repository root; the library lands next to
 this file as ``libpkvt.so``.  Always recompiles (a few seconds).
