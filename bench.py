@@ -435,6 +435,26 @@ def copy_probe(torch, mib):
     del src, dst
 
 
+def copy_probe_gbps(torch, gib: int = 2, reps: int = 10) -> float:
+    """HBM bandwidth a plain library copy reaches on this device, as context
+    for the roofline (whose peak is the published 8 TB/s): torch's
+    elementwise negation of a `gib` GiB fp16 tensor into another, counted as
+    the bytes read plus the bytes written."""
+    x = torch.ones(gib * 2 ** 30 // 2, dtype=torch.float16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(2):
+        torch.neg(x, out=y)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.neg(x, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * gib * 2 ** 30 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    return round(gbps, 1)
+
+
 def decode_loop(args, name, layers, static_us_layer):
     """Decoding iterations with the tree changing under the kernels: per step
     a token appended to every row (K/V written by pkvt_kv_scatter), the plan
@@ -881,6 +901,7 @@ def main():
             "algorithmic_bytes_per_launch": int(attn_bytes),
         },
         "workload_gen_s": round(gen_s, 1),
+        "hbm_copy_probe_gbps": copy_probe_gbps(torch),
     }
 
     if not args.no_plain:

@@ -311,3 +311,16 @@ def test_items_of_64_chunks_and_long_private_contexts():
         print(f"\n[case] long contexts p1={p1} p2={p2} err={err:.3e} info={ds.info}", flush=True)
         assert err <= TOL
         ds.close()
+
+
+def test_many_sequences():
+    """600 sequences in a three-level forest (many units, thousands of
+    single-wave tasks and merges): every output row."""
+    _torch()
+    w = W.layered_tree(901, 600, 5, h=2, d=64, c=16, max_chunks=4)
+    ref = A.attention_batch(w)
+    ds = _setup(w)
+    err = _err(_run(ds), ref)
+    print(f"\n[case] 600 sequences err={err:.3e} info={ds.info}", flush=True)
+    assert err <= TOL
+    ds.close()
