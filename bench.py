@@ -616,6 +616,31 @@ def run_sweep(args):
                           "dtype": "f16", "data": "synthetic, device N(0,1)",
                           "steps_per_point": args.sweep_steps, "points": points}), flush=True)
         return
+    if args.sweep == "shard":
+        # one GPU's share of the long-shared-prompt batch when G GPUs split the
+        # 32 heads (h = 32 / G at the real b, d, c): the work per GPU shrinks G
+        # times and so does the number of (item, head) pieces to spread over
+        # the 512 workgroups
+        rng = np.random.Generator(np.random.PCG64(1002))
+        priv = [int(x) for x in rng.integers(256, 1025, size=64)]
+        points = []
+        for g in (1, 2, 4, 8):
+            h = 32 // g
+            row = {"gpus_sharing_heads": g, "h": h}
+            for variant in ("tpp", "plain"):
+                t, info, unique = sweep_time(torch, B, W, 64, 4096, priv, 3200 + g, variant,
+                                             args.sweep_steps, 10, ev, h=h, d=128, c=64)
+                row[f"{variant}_us_per_layer"] = round(t, 2)
+                if variant == "tpp":
+                    row["effective_gbps"] = round(unique / (t * 1e-6) / 1e9, 1)
+                    row["frac_hbm_peak"] = round(unique / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                    row["plan"] = {k: info[k] for k in ("wg_units", "tasks", "phase1_split", "phase2_split")}
+            print(json.dumps(row), file=sys.stderr, flush=True)
+            points.append(row)
+        print(json.dumps({"sweep": "shard", "b": 64, "n_s": 4096, "private": "uniform [256, 1024]",
+                          "d": 128, "c": 64, "dtype": "f16", "data": "synthetic, device N(0,1)",
+                          "points": points}), flush=True)
+        return
     if args.sweep == "divergence":
         grid = [(32, n_s, n_c) for n_s, n_c in sorted(PAGE_DIVERGENCE)]
         grid += [(32, n_s, 0) for n_s in (1024, 2048, 4096)]
@@ -750,7 +775,7 @@ def main():
     ap.add_argument("--loop-churn", type=int, default=16,
                     help="a row gets a new sequence every this many decode-loop steps")
     ap.add_argument("--no-loop", action="store_true")
-    ap.add_argument("--sweep", choices=["divergence", "batch", "shapes"],
+    ap.add_argument("--sweep", choices=["divergence", "batch", "shapes", "shard"],
                     help="time the decode-throughput sweeps of the pages' divergence (Knowl 8) "
                          "or batch-size (Knowl 9) experiments instead of the benchmark")
     ap.add_argument("--sweep-steps", type=int, default=60)
