@@ -206,8 +206,11 @@ def summarize_pmc(args):
     fetch, n_fetch = _counter_means(args.fetch_csv, ATTN_KERNEL)
     write, n_write = _counter_means(args.write_csv, ATTN_KERNEL)
     copy_bytes = args.copy_mib * 2 ** 20
-    cf, _ = _counter_means(args.fetch_csv, "neg_kernel")
-    cw, _ = _counter_means(args.write_csv, "neg_kernel")
+    cf, ncf = _counter_means(args.fetch_csv, "neg_kernel")
+    cw, ncw = _counter_means(args.write_csv, "neg_kernel")
+    if ncf.get("FETCH_SIZE") != 3 or ncw.get("WRITE_SIZE") != 3:
+        raise SystemExit(f"summarize-pmc: expected the 3 calibration copies, found "
+                         f"{ncf.get('FETCH_SIZE')} / {ncw.get('WRITE_SIZE')} neg_kernel dispatches")
     # the copy runs three times after a fill: take the copies' own rows
     f_fetch = copy_bytes / (cf["FETCH_SIZE"] * 1024)
     f_write = copy_bytes / (cw["WRITE_SIZE"] * 1024)
@@ -926,7 +929,9 @@ def main():
             "algorithmic_bytes_per_launch": int(attn_bytes),
         },
         "workload_gen_s": round(gen_s, 1),
-        "hbm_copy_probe_gbps": copy_probe_gbps(torch),
+        # a counter-collection run calibrates on its own copy's dispatches
+        # alone, so it leaves this (differently sized) copy out
+        "hbm_copy_probe_gbps": None if args.copy_probe_mib else copy_probe_gbps(torch),
     }
 
     if not args.no_plain:

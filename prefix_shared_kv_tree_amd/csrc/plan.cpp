@@ -377,7 +377,10 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     // items are cut at T.  Phase-2 items are cut at T when nothing is shared
     // (all tasks then tend to be alike and need no merge); with a shared
     // prefix the phase-1 units make the per-wave loads uneven and finer
-    // phase-2 pieces (4 steps, or T/4 if larger) fill the gaps better.
+    // phase-2 pieces (T/4, but at least 4 steps) fill the gaps better.  The
+    // floor holds also when T is below it: a small batch cut into 1- or
+    // 2-step pieces spends more on the extra partials and their merge than
+    // the finer balance wins back.
     int32_t s1 = opts.phase1_chunks, s2 = opts.phase2_chunks;
     if (s1 == 0 || s2 == 0) {
         int64_t quarters = 0;
@@ -396,7 +399,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         const int64_t mean = std::max<int64_t>(1, (quarters * t.H + 4 * lanes - 1) / (4 * lanes));
         if (s1 == 0) s1 = steps_to_chunks(mean, t.C);
         if (s2 == 0) {
-            const int64_t fine = std::min<int64_t>(mean, std::max<int64_t>(4, (mean + 3) / 4));
+            const int64_t fine = std::max<int64_t>(4, (mean + 3) / 4);
             s2 = steps_to_chunks(segs.empty() ? mean : fine, t.C);
         }
     }
