@@ -15,6 +15,20 @@ Readings of the page used here (the page leaves them open):
     from then on and can be matched by later arrivals; nodes are never
     merged or de-duplicated.  When several live children of one node carry
     the same c tokens, a lookup takes the earliest created one.
+
+Token-granular variant (TokenSharingModel; the page's nodes are whole
+chunks, this is the variant that shares a prefix which ends inside a chunk):
+  * a node holds 1..c tokens at the start of its chunk;
+  * an arrival descends from the root, at each node into the child whose
+    tokens share the longest common prefix with the rest of the prompt
+    (ties: the earliest created); a child matched only in its first t
+    tokens is split: it keeps those t tokens and a new node, inserted below
+    it and above its old children, takes the rest (their K/V move to the new
+    node's chunk); the unmatched rest of the prompt becomes a new branch;
+  * a decode append writes into the sequence's leaf only while that leaf is
+    partial, private and childless; otherwise it opens a new leaf chunk (a
+    shared or split chunk is never written again);
+  * nodes are never merged.
 """
 from __future__ import annotations
 
@@ -205,3 +219,96 @@ class SharingModel:
 
     def seq_len(self, sid: int) -> int:
         return sum(len(n.tokens) for n in self.seqs[sid])
+
+
+# --------------------------------------------------------------------------
+# Token-granular variant (see the module header).
+# --------------------------------------------------------------------------
+
+def common_prefix_len(a: Sequence[int], b: Sequence[int]) -> int:
+    """Length of the longest common prefix of two token lists."""
+    n = min(len(a), len(b))
+    k = 0
+    while k < n and int(a[k]) == int(b[k]):
+        k += 1
+    return k
+
+
+def distinct_prefixes(token_seqs: Sequence[Sequence[int]]) -> int:
+    """Number of distinct non-empty token prefixes over the sequences: the
+    tokens a token-granular tree stores when every shared prefix is stored
+    once."""
+    seen = set()
+    for toks in token_seqs:
+        t = tuple(int(x) for x in toks)
+        for k in range(1, len(t) + 1):
+            seen.add(t[:k])
+    return len(seen)
+
+
+class TokenSharingModel(SharingModel):
+    """SharingModel with token-granular matching and node splitting."""
+
+    def _split(self, node: _Node, t: int) -> _Node:
+        """Keep the first t tokens in node; a new node below it takes the
+        rest and node's children; every sequence through node now also
+        passes through the new node."""
+        tail = _Node(self.next_id, node, node.tokens[t:])
+        self.next_id += 1
+        tail.children = node.children
+        for ch in tail.children:
+            ch.parent = tail
+        node.tokens = node.tokens[:t]
+        node.children = [tail]
+        tail.refs = set(node.refs)
+        for sid in node.refs:
+            path = self.seqs[sid]
+            i = path.index(node)
+            path.insert(i + 1, tail)
+        return tail
+
+    def insert(self, tokens: Sequence[int]) -> int:
+        toks = [int(t) for t in tokens]
+        if not toks:
+            raise ValueError("empty sequence")
+        sid = self.next_seq
+        self.next_seq += 1
+        node = self.root
+        path: List[_Node] = []
+        pos = 0
+        while pos < len(toks):
+            best, best_len = None, 0
+            for ch in node.children:            # creation order: earliest wins ties
+                k = common_prefix_len(ch.tokens, toks[pos:])
+                if k > best_len:
+                    best, best_len = ch, k
+            if best is None:
+                break
+            if best_len < len(best.tokens):
+                self._split(best, best_len)
+            path.append(best)
+            node = best
+            pos += best_len
+        while pos < len(toks):
+            piece = toks[pos:pos + self.c]
+            node = self._new(node, piece)
+            path.append(node)
+            pos += len(piece)
+        for n in path:
+            n.refs.add(sid)
+        self.seqs[sid] = path
+        return sid
+
+    def append(self, sid: int, token: int) -> None:
+        path = self.seqs[sid]
+        leaf = path[-1]
+        if len(leaf.tokens) < self.c and leaf.refs == {sid} and not leaf.children:
+            leaf.tokens.append(int(token))
+        else:
+            n = self._new(leaf, [int(token)])
+            n.refs.add(sid)
+            path.append(n)
+
+    def node_tokens(self, sid: int) -> List[List[int]]:
+        """The sequence's path as the token lists of its nodes."""
+        return [list(n.tokens) for n in self.seqs[sid]]

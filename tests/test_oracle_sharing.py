@@ -182,3 +182,131 @@ def test_model_random_ops_invariants(seed):
     for s in list(m.live()):
         m.remove(s)
     assert m.used_chunks() == 0 and not m.root.children
+
+
+# --------------------------------------------------------------------------
+# Token-granular variant of the tree.
+# --------------------------------------------------------------------------
+
+def test_token_model_matches_hand_worked_fixture():
+    with open(os.path.join(GOLDEN, "token_sharing_c4.json")) as f:
+        fx = json.load(f)
+    m = S.TokenSharingModel(fx["c"])
+    for op in fx["ops"]:
+        if op[0] == "insert":
+            m.insert(op[1])
+        elif op[0] == "append":
+            m.append(op[1], op[2])
+        elif op[0] == "remove":
+            m.remove(op[1])
+        else:
+            exp = op[1]
+            assert m.live() == exp["live"]
+            assert [m.node_tokens(s) for s in m.live()] == exp["tokens"]
+            assert [list(x) for x in S.canonicalize(m.paths())] == exp["labels"]
+            rc = m.refcounts()
+            assert [[rc[n] for n in p] for p in m.paths()] == exp["refcounts"]
+            assert m.used_chunks() == exp["used"]
+
+
+def _shared_tokens(m, u, v):
+    """Tokens that sequences u and v read from the same stored nodes."""
+    n = 0
+    for a, b in zip(m.seqs[u], m.seqs[v]):
+        if a is not b:
+            break
+        n += len(a.tokens)
+    return n
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_token_model_static_builds_store_each_prefix_once(seed):
+    """Arrivals only: two sequences share exactly their longest common token
+    prefix, every distinct prefix is stored once (the count of distinct
+    prefixes, an order-free quantity), each node holds 1..c tokens and
+    siblings start with different tokens."""
+    rng = np.random.default_rng(500 + seed)
+    c = int(rng.integers(1, 6))
+    vocab = int(rng.integers(2, 4))
+    seqs = []
+    for _ in range(int(rng.integers(1, 10))):
+        base = []
+        if seqs and rng.random() < 0.7:
+            src = seqs[int(rng.integers(0, len(seqs)))]
+            base = src[:int(rng.integers(0, len(src) + 1))]
+        t = base + [int(x) for x in rng.integers(0, vocab, size=int(rng.integers(0 if base else 1, 15)))]
+        seqs.append(t)
+    m = S.TokenSharingModel(c)
+    ids = [m.insert(t) for t in seqs]
+    for i, u in enumerate(ids):
+        assert sum(m.node_tokens(u), []) == seqs[i]
+        for j, v in enumerate(ids):
+            if i != j:
+                assert _shared_tokens(m, u, v) == S.common_prefix_len(seqs[i], seqs[j])
+    nodes = {n.nid: n for s in m.live() for n in m.seqs[s]}
+    assert sum(len(n.tokens) for n in nodes.values()) == S.distinct_prefixes(seqs)
+    assert all(1 <= len(n.tokens) <= c for n in nodes.values())
+    for n in list(nodes.values()) + [m.root]:
+        firsts = [ch.tokens[0] for ch in n.children]
+        assert len(firsts) == len(set(firsts))
+
+
+@pytest.mark.parametrize("name", ["tiny", "c2", "c4"])
+def test_token_model_reduces_to_chunk_model_on_aligned_prefixes(name):
+    """When every shared prefix ends on a chunk boundary and diverging
+    prompts differ in their first token after it (random ids out of 32000
+    here), both readings give the same sharing map."""
+    w = W.make_config(name, with_kv=False)
+    a, b = S.SharingModel(w.c), S.TokenSharingModel(w.c)
+    for t in w.all_seq_tokens():
+        a.insert(t)
+        b.insert(t)
+    assert [list(x) for x in S.canonicalize(a.paths())] == [list(x) for x in S.canonicalize(b.paths())]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_token_model_random_ops_invariants(seed):
+    """Random insert/append/remove: every live path spells the sequence's
+    tokens, nodes hold 1..c tokens, refcounts count covering sequences, a
+    shared node never grows (a split only shortens it), and removing
+    everything frees everything."""
+    rng = np.random.default_rng(700 + seed)
+    c = int(rng.integers(2, 6))
+    m = S.TokenSharingModel(c)
+    toks = {}
+    for _ in range(200):
+        r = rng.random()
+        if r < 0.35 or not m.live():
+            base = []
+            if m.live() and rng.random() < 0.7:
+                src = toks[int(rng.choice(m.live()))]
+                base = src[:int(rng.integers(0, len(src) + 1))]
+            t = base + [int(x) for x in rng.integers(0, 2, size=int(rng.integers(1 if not base else 0, 12)))]
+            if not t:
+                t = [0]
+            sid = m.insert(t)
+            toks[sid] = list(t)
+        elif r < 0.85:
+            sid = int(rng.choice(m.live()))
+            before = {n.nid: len(n.tokens) for s in m.live() for n in m.seqs[s] if len(n.refs) > 1}
+            tok = int(rng.integers(0, 2))
+            m.append(sid, tok)
+            toks[sid].append(tok)
+            for s in m.live():
+                for n in m.seqs[s]:
+                    if n.nid in before:
+                        assert len(n.tokens) == before[n.nid]
+        else:
+            sid = int(rng.choice(m.live()))
+            m.remove(sid)
+            del toks[sid]
+        rc = m.refcounts()
+        for s in m.live():
+            path = m.seqs[s]
+            assert sum((n.tokens for n in path), []) == toks[s]
+            assert all(1 <= len(n.tokens) <= c for n in path)
+            for n in path:
+                assert rc[n.nid] == sum(1 for s2 in m.live() if n in m.seqs[s2])
+    for s in list(m.live()):
+        m.remove(s)
+    assert m.used_chunks() == 0 and not m.root.children
