@@ -88,6 +88,33 @@ pkvt_status pkvt_tree_create(int32_t n_heads, int32_t head_dim, int32_t chunk_si
                              int32_t pool_chunks, pkvt_tree** out);
 void        pkvt_tree_destroy(pkvt_tree* tree);
 
+/* pkvt_tree_create with a choice of prefix matching:
+ *   PKVT_MATCH_CHUNKS -- whole-chunk matching (Knowl 1's nodes are whole
+ *                        chunks); what pkvt_tree_create gives.
+ *   PKVT_MATCH_TOKENS -- token-granular matching, a variant the page does not
+ *                        describe: an arrival shares its longest common token
+ *                        prefix with the tree even when that prefix ends
+ *                        inside a chunk.  A node then holds 1..c tokens at the
+ *                        start of its chunk.  The arrival descends into the
+ *                        child whose tokens share the longest prefix with the
+ *                        rest of its prompt (ties: the earliest created) and
+ *                        SPLITS a child it matches only in part: the child
+ *                        keeps the matched tokens, a new node (a new chunk)
+ *                        below it takes the rest and the old children.  The
+ *                        K/V of those tokens must then move: see
+ *                        pkvt_tree_moves / pkvt_kv_move.  A decode append
+ *                        writes into the leaf only while that leaf is partial,
+ *                        private and childless, else it opens a new leaf.
+ *                        Nodes are never merged.  The decode planner and
+ *                        kernels accept such trees; pkvt_prefill_plan rejects
+ *                        a batch whose paths hold a partial chunk before
+ *                        their leaf (INVALID_ARG).
+ * INVALID_ARG also for any other match value. */
+#define PKVT_MATCH_CHUNKS 0
+#define PKVT_MATCH_TOKENS 1
+pkvt_status pkvt_tree_create_ex(int32_t n_heads, int32_t head_dim, int32_t chunk_size,
+                                int32_t pool_chunks, int32_t match, pkvt_tree** out);
+
 /* Sequence arrival (Knowl 1): insert n_seqs prompts.
  *   tokens  : int32 token ids of all prompts, concatenated.
  *   offsets : int64 [n_seqs+1]; prompt s is tokens[offsets[s] .. offsets[s+1]).
@@ -95,6 +122,10 @@ void        pkvt_tree_destroy(pkvt_tree* tree);
  * c tokens (and therefore whole prefix) equal an existing full chunk on the
  * path is shared (refcount + 1); the remaining tokens are stored in newly
  * allocated chunks, inserted as a branch; a partial last chunk is private.
+ * (Token matching, pkvt_tree_create_ex: the longest common token prefix is
+ * shared, splitting a node where it ends inside one; slots are then final
+ * positions after every split of the call, and the K/V of tokens stored
+ * before the call that a split relocated are listed by pkvt_tree_moves.)
  * Prompts inserted earlier in the same call can be matched by later ones.
  * Outputs:
  *   seq_ids : int32 [n_seqs], the new sequences' ids (never reused).
@@ -107,7 +138,8 @@ pkvt_status pkvt_tree_build(pkvt_tree* tree, int32_t n_seqs, const int32_t* toke
                             const int64_t* offsets, int32_t* seq_ids, int64_t* slots);
 
 /* Decode append (Knowl 1): token i goes to sequence seq_ids[i]'s leaf chunk
- * until that chunk is full, then to a new private leaf chunk.  Several
+ * until that chunk is full, then to a new private leaf chunk (under token
+ * matching also when the leaf is shared or has children).  Several
  * entries may name the same sequence; they are applied in order.
  * slots[i] receives chunk_id*c + position for token i (never -1).
  * Errors: UNKNOWN_SEQ, NO_CHUNKS, INVALID_ARG.  All-or-nothing. */
@@ -137,6 +169,22 @@ pkvt_status pkvt_tree_chunk_path(const pkvt_tree* tree, int32_t seq_id, int32_t*
 pkvt_status pkvt_tree_seq_len(const pkvt_tree* tree, int32_t seq_id, int64_t* len);
 /* Live sequences through the chunk (0 for a free chunk). */
 pkvt_status pkvt_tree_chunk_refcount(const pkvt_tree* tree, int32_t chunk_id, int32_t* refs);
+/* Tokens stored in the chunk (0 for a free chunk; below c only for a leaf
+ * under whole-chunk matching, anywhere under token matching). */
+pkvt_status pkvt_tree_chunk_fill(const pkvt_tree* tree, int32_t chunk_id, int32_t* fill);
+
+/* K/V moves made necessary by the most recent pkvt_tree_build (token
+ * matching; always none under whole-chunk matching): the token whose K/V is
+ * at slot src[i] now belongs at slot dst[i] (slot = chunk_id*c + position).
+ * Sources lie in chunks that existed before that build, destinations in
+ * chunks it allocated, so the two sets are disjoint, and none of them is a
+ * slot the build returned for a new token: apply the moves (pkvt_kv_move,
+ * once per layer's pools) and write the new tokens in either order, both
+ * before the next attention call.  *n receives the number of moves; at most
+ * cap are written (BUFFER_TOO_SMALL if cap < *n, so cap 0 with NULL src/dst
+ * asks for the count).  The list is replaced by every pkvt_tree_build call. */
+pkvt_status pkvt_tree_moves(const pkvt_tree* tree, int64_t* src, int64_t* dst, int64_t cap,
+                            int64_t* n);
 
 /* ------------------------------------------------------------------------
  * Plan = context generation (Knowl 5): the host walks the tree and emits the
@@ -325,6 +373,15 @@ pkvt_status pkvt_kv_scatter(const pkvt_tree* tree, void* k_pool, void* v_pool,
 pkvt_status pkvt_kv_scatter_host_slots(const pkvt_tree* tree, void* k_pool, void* v_pool,
                                        const int64_t* slots, const void* k_new,
                                        const void* v_new, int64_t n_tokens, void* stream);
+
+/* Move n tokens' K/V inside one layer's pools: slot src[i] -> slot dst[i],
+ * all heads (the moves of pkvt_tree_moves).
+ *   src, dst : device int64 [n]; pairs with an entry outside
+ *              [0, pool_chunks*c) are skipped.  The source and destination
+ *              slot sets must be disjoint (pkvt_tree_moves' are).
+ * Errors: INVALID_ARG, UNSUPPORTED_SHAPE, HIP. */
+pkvt_status pkvt_kv_move(const pkvt_tree* tree, void* k_pool, void* v_pool, const int64_t* src,
+                         const int64_t* dst, int64_t n, void* stream);
 
 const char* pkvt_last_error(void);
 

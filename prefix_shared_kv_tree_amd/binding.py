@@ -61,6 +61,7 @@ _sz = C.c_size_t
 _SIGNATURES = {
     "pkvt_pool_bytes": [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.POINTER(_sz)],
     "pkvt_tree_create": [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.POINTER(_vp)],
+    "pkvt_tree_create_ex": [C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.POINTER(_vp)],
     "pkvt_tree_destroy": [_vp],
     "pkvt_tree_build": [_vp, C.c_int32, _i32p, _i64p, _i32p, _i64p],
     "pkvt_tree_append": [_vp, C.c_int32, _i32p, _i32p, _i64p],
@@ -69,6 +70,8 @@ _SIGNATURES = {
     "pkvt_tree_chunk_path": [_vp, C.c_int32, _i32p, C.c_int32, _i32p],
     "pkvt_tree_seq_len": [_vp, C.c_int32, _i64p],
     "pkvt_tree_chunk_refcount": [_vp, C.c_int32, _i32p],
+    "pkvt_tree_chunk_fill": [_vp, C.c_int32, _i32p],
+    "pkvt_tree_moves": [_vp, _i64p, _i64p, C.c_int64, _i64p],
     "pkvt_plan": [_vp, C.c_int32, _i32p, C.POINTER(PlanOpts), C.POINTER(_sz), C.POINTER(_sz)],
     "pkvt_plan_info_get": [_vp, C.POINTER(PlanInfo)],
     "pkvt_plan_blob": [_vp, _i32p, C.c_int32, _i32p],
@@ -83,6 +86,7 @@ _SIGNATURES = {
     "pkvt_prefill_attn": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp],
     "pkvt_kv_scatter": [_vp, _vp, _vp, _vp, _vp, _vp, C.c_int64, _vp],
     "pkvt_kv_scatter_host_slots": [_vp, _vp, _vp, _i64p, _vp, _vp, C.c_int64, _vp],
+    "pkvt_kv_move": [_vp, _vp, _vp, _vp, _vp, C.c_int64, _vp],
     "pkvt_last_error": [],
 }
 _RESTYPE = {"pkvt_tree_destroy": None, "pkvt_last_error": C.c_char_p}
@@ -143,10 +147,22 @@ def pkvt_pool_bytes(n_heads: int, head_dim: int, chunk_size: int, pool_chunks: i
 
 # ---- tree ---------------------------------------------------------------------
 
-def pkvt_tree_create(n_heads: int, head_dim: int, chunk_size: int, pool_chunks: int) -> int:
+PKVT_MATCH_CHUNKS = 0
+PKVT_MATCH_TOKENS = 1
+
+
+def pkvt_tree_create(n_heads: int, head_dim: int, chunk_size: int, pool_chunks: int,
+                     match: str = "chunks") -> int:
+    """match: "chunks" (whole-chunk prefix matching) or "tokens" (token-granular,
+    with node splits; pkvt_tree_create_ex)."""
     h = _vp()
-    _check("pkvt_tree_create", load().pkvt_tree_create(n_heads, head_dim, chunk_size, pool_chunks,
-                                                       C.byref(h)))
+    if match == "chunks":
+        _check("pkvt_tree_create", load().pkvt_tree_create(n_heads, head_dim, chunk_size,
+                                                           pool_chunks, C.byref(h)))
+    else:
+        mode = {"tokens": PKVT_MATCH_TOKENS}.get(match, -1)
+        _check("pkvt_tree_create_ex", load().pkvt_tree_create_ex(n_heads, head_dim, chunk_size,
+                                                                 pool_chunks, mode, C.byref(h)))
     return h.value
 
 
@@ -214,6 +230,25 @@ def pkvt_tree_chunk_refcount(tree: int, chunk_id: int) -> int:
     _check("pkvt_tree_chunk_refcount", load().pkvt_tree_chunk_refcount(tree, int(chunk_id),
                                                                        C.byref(n)))
     return n.value
+
+
+def pkvt_tree_chunk_fill(tree: int, chunk_id: int) -> int:
+    n = C.c_int32()
+    _check("pkvt_tree_chunk_fill", load().pkvt_tree_chunk_fill(tree, int(chunk_id), C.byref(n)))
+    return n.value
+
+
+def pkvt_tree_moves(tree: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(src, dst) int64 slot arrays of the K/V moves of the last build."""
+    n = C.c_int64()
+    rc = load().pkvt_tree_moves(tree, None, None, 0, C.byref(n))
+    if rc not in (PKVT_OK, -6):
+        _check("pkvt_tree_moves", rc)
+    src = np.zeros(max(n.value, 1), dtype=np.int64)
+    dst = np.zeros(max(n.value, 1), dtype=np.int64)
+    _check("pkvt_tree_moves", load().pkvt_tree_moves(tree, _p64(src), _p64(dst), src.size,
+                                                     C.byref(n)))
+    return src[:n.value], dst[:n.value]
 
 
 # ---- plan ---------------------------------------------------------------------
@@ -315,6 +350,13 @@ def pkvt_kv_scatter(tree: int, k_pool: int, v_pool: int, slots: int, k_new: int,
                     n_tokens: int, stream: int = 0) -> None:
     _check("pkvt_kv_scatter", load().pkvt_kv_scatter(tree, k_pool, v_pool, slots, k_new, v_new,
                                                      int(n_tokens), stream or None))
+
+
+def pkvt_kv_move(tree: int, k_pool: int, v_pool: int, src: int, dst: int, n: int,
+                 stream: int = 0) -> None:
+    """src / dst: device int64 slot arrays of n moves."""
+    _check("pkvt_kv_move", load().pkvt_kv_move(tree, k_pool, v_pool, src, dst, int(n),
+                                               stream or None))
 
 
 PKVT_INLINE_SLOTS = 256

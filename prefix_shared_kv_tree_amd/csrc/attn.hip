@@ -609,7 +609,7 @@ __device__ __forceinline__ Task fetch_task(const AttnArgs& a, int idx) {
     t.row_lo = wd[4];
     t.n_rows = wd[5];
     t.out = wd[6];
-    int n_valid = n_chunks * C;
+    int n_valid = n_chunks * C - wd[7];          // wd[7]: keys the last chunk lacks
     if (len_row >= 0) n_valid = min(n_valid, meta(a.seqlen)[len_row] - key_base);
     t.n_valid = n_valid;
     t.n_steps = (n_valid + Step<D>::kKeys - 1) / Step<D>::kKeys;
@@ -879,6 +879,32 @@ __global__ __launch_bounds__(256) void scatter_inline_kernel(ScatterArgs a, Inli
     scatter_piece<D, C>(a, gid, is.slot[tok], tok);
 }
 
+// Move tokens' K/V between pool slots (the split of a node under token
+// matching).  One thread per (move, head, 8 dims): a 16-byte K piece and the
+// same 8 dims of V, which sit 4 halves apart in the [c/4][d][4] layout.
+template <int D, int C>
+__global__ __launch_bounds__(256) void move_kernel(MoveArgs a) {
+    constexpr int P = D / 8;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= a.n * a.H * P) return;
+    const int64_t i = gid / (static_cast<int64_t>(a.H) * P);
+    const int piece = static_cast<int>(gid % P);
+    const int head = static_cast<int>((gid / P) % a.H);
+    const int64_t from = a.src[i], to = a.dst[i];
+    if (from < 0 || from >= a.slot_limit || to < 0 || to >= a.slot_limit) return;
+    const size_t fb = (static_cast<size_t>(from / C) * a.H + head) * C * D;
+    const size_t tb = (static_cast<size_t>(to / C) * a.H + head) * C * D;
+    const int ft = static_cast<int>(from % C), tt = static_cast<int>(to % C);
+    _Float16* kp = static_cast<_Float16*>(a.kpool);
+    *reinterpret_cast<h8*>(kp + tb + (static_cast<size_t>(piece) * C + tt) * 8) =
+        *reinterpret_cast<const h8*>(kp + fb + (static_cast<size_t>(piece) * C + ft) * 8);
+    _Float16* vp = static_cast<_Float16*>(a.vpool);
+    const _Float16* vf = vp + fb + (static_cast<size_t>(ft / 4) * D + piece * 8) * 4 + (ft % 4);
+    _Float16* vt = vp + tb + (static_cast<size_t>(tt / 4) * D + piece * 8) * 4 + (tt % 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt[e * 4] = vf[e * 4];
+}
+
 __global__ __launch_bounds__(256) void copy_words_kernel(const int32_t* __restrict__ src,
                                                          int32_t* __restrict__ dst, int64_t n) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
@@ -919,6 +945,14 @@ hipError_t scatter_inline_dc(const ScatterArgs& a, const InlineSlots& is, hipStr
     return hipGetLastError();
 }
 
+template <int D, int C>
+hipError_t move_dc(const MoveArgs& a, hipStream_t s) {
+    const int64_t threads = a.n * a.H * (D / 8);
+    if (threads == 0) return hipSuccess;
+    move_kernel<D, C><<<dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 #define PKVT_DISPATCH(FN, D, C, ...)                                  \
@@ -954,6 +988,10 @@ hipError_t launch_scatter_inline(const ScatterArgs& a, const InlineSlots& is, in
                                  hipStream_t s) {
     if (a.n_tokens > kInlineSlots) return hipErrorInvalidValue;
     PKVT_DISPATCH(scatter_inline_dc, D, C, a, is, s)
+}
+
+hipError_t launch_move(const MoveArgs& a, int D, int C, hipStream_t s) {
+    PKVT_DISPATCH(move_dc, D, C, a, s)
 }
 
 hipError_t launch_copy_words(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s) {

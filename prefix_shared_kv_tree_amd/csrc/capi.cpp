@@ -41,7 +41,7 @@ struct pkvt_tree {
     Staging staging[kStagingRing];
     int next_staging = 0;
 
-    pkvt_tree(int32_t h, int32_t d, int32_t c, int32_t n) : tree(h, d, c, n) {}
+    pkvt_tree(int32_t h, int32_t d, int32_t c, int32_t n, pkvt::Match m) : tree(h, d, c, n, m) {}
     ~pkvt_tree() {
         for (Staging& st : staging) {
             if (st.in_flight) (void)hipEventSynchronize(st.done);
@@ -189,19 +189,27 @@ pkvt_status pkvt_pool_bytes(int32_t n_heads, int32_t head_dim, int32_t chunk_siz
     return PKVT_OK;
 }
 
-pkvt_status pkvt_tree_create(int32_t n_heads, int32_t head_dim, int32_t chunk_size,
-                             int32_t pool_chunks, pkvt_tree** out) {
+pkvt_status pkvt_tree_create_ex(int32_t n_heads, int32_t head_dim, int32_t chunk_size,
+                                int32_t pool_chunks, int32_t match, pkvt_tree** out) {
     if (!out) return fail(PKVT_ERR_INVALID_ARG, "tree_create: out is NULL");
     *out = nullptr;
     if (n_heads < 1 || head_dim < 1 || chunk_size < 1 || chunk_size > 4096 || pool_chunks < 1)
         return fail(PKVT_ERR_INVALID_ARG, "tree_create: need n_heads, head_dim, pool_chunks >= 1 "
                                           "and chunk_size in [1, 4096]");
+    if (match != PKVT_MATCH_CHUNKS && match != PKVT_MATCH_TOKENS)
+        return fail(PKVT_ERR_INVALID_ARG, "tree_create: match must be PKVT_MATCH_CHUNKS or PKVT_MATCH_TOKENS");
     try {
-        *out = new pkvt_tree(n_heads, head_dim, chunk_size, pool_chunks);
+        *out = new pkvt_tree(n_heads, head_dim, chunk_size, pool_chunks,
+                             match == PKVT_MATCH_TOKENS ? pkvt::Match::kTokens : pkvt::Match::kChunks);
     } catch (const std::bad_alloc&) {
         return fail(PKVT_ERR_HOST_MEMORY, "tree_create: out of host memory");
     }
     return PKVT_OK;
+}
+
+pkvt_status pkvt_tree_create(int32_t n_heads, int32_t head_dim, int32_t chunk_size,
+                             int32_t pool_chunks, pkvt_tree** out) {
+    return pkvt_tree_create_ex(n_heads, head_dim, chunk_size, pool_chunks, PKVT_MATCH_CHUNKS, out);
 }
 
 void pkvt_tree_destroy(pkvt_tree* tree) { delete tree; }
@@ -277,6 +285,29 @@ pkvt_status pkvt_tree_chunk_refcount(const pkvt_tree* t, int32_t chunk_id, int32
         return fail(PKVT_ERR_INVALID_ARG, "chunk_refcount: chunk id out of range");
     const pkvt::Node& x = t->tree.node(chunk_id);
     *refs = x.live ? x.refs : 0;
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_tree_chunk_fill(const pkvt_tree* t, int32_t chunk_id, int32_t* fill) {
+    if (!t || !fill) return fail(PKVT_ERR_INVALID_ARG, "chunk_fill: NULL argument");
+    if (chunk_id < 0 || chunk_id >= t->tree.N)
+        return fail(PKVT_ERR_INVALID_ARG, "chunk_fill: chunk id out of range");
+    const pkvt::Node& x = t->tree.node(chunk_id);
+    *fill = x.live ? x.fill : 0;
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_tree_moves(const pkvt_tree* t, int64_t* src, int64_t* dst, int64_t cap, int64_t* n) {
+    if (!t || !n) return fail(PKVT_ERR_INVALID_ARG, "tree_moves: NULL argument");
+    const auto& mv = t->tree.moves();
+    *n = static_cast<int64_t>(mv.size());
+    if (mv.empty()) return PKVT_OK;
+    if (cap < *n) return fail(PKVT_ERR_BUFFER_TOO_SMALL, "tree_moves: cap < number of moves");
+    if (!src || !dst) return fail(PKVT_ERR_INVALID_ARG, "tree_moves: NULL output array");
+    for (size_t i = 0; i < mv.size(); ++i) {
+        src[i] = mv[i].first;
+        dst[i] = mv[i].second;
+    }
     return PKVT_OK;
 }
 
@@ -422,6 +453,26 @@ pkvt_status pkvt_kv_scatter(const pkvt_tree* t, void* k_pool, void* v_pool, cons
     a.H = t->tree.H;
     hipError_t e = pkvt::launch_scatter(a, t->tree.D, t->tree.C, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_scatter");
+    return PKVT_OK;
+}
+
+pkvt_status pkvt_kv_move(const pkvt_tree* t, void* k_pool, void* v_pool, const int64_t* src,
+                         const int64_t* dst, int64_t n, void* stream) {
+    if (!t || n < 0) return fail(PKVT_ERR_INVALID_ARG, "kv_move: bad arguments");
+    if (!shape_ok(t->tree.D, t->tree.C))
+        return fail(PKVT_ERR_UNSUPPORTED_SHAPE, "kv_move: unsupported head_dim / chunk_size");
+    if (n == 0) return PKVT_OK;
+    if (!k_pool || !v_pool || !src || !dst) return fail(PKVT_ERR_INVALID_ARG, "kv_move: NULL argument");
+    pkvt::MoveArgs a{};
+    a.kpool = k_pool;
+    a.vpool = v_pool;
+    a.src = src;
+    a.dst = dst;
+    a.n = n;
+    a.slot_limit = static_cast<int64_t>(t->tree.N) * t->tree.C;
+    a.H = t->tree.H;
+    hipError_t e = pkvt::launch_move(a, t->tree.D, t->tree.C, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kv_move");
     return PKVT_OK;
 }
 

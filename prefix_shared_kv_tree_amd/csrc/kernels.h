@@ -54,6 +54,17 @@ struct ScatterArgs {
     int32_t H;
 };
 
+// Token K/V moves inside the pools: token at slot src[i] -> slot dst[i].
+struct MoveArgs {
+    void* kpool;
+    void* vpool;
+    const int64_t* src;
+    const int64_t* dst;
+    int64_t n;
+    int64_t slot_limit;       // pool_chunks * C
+    int32_t H;
+};
+
 constexpr int kInlineSlots = 256;
 struct InlineSlots {
     int64_t slot[kInlineSlots];
@@ -69,5 +80,8 @@ hipError_t launch_scatter_inline(const ScatterArgs& a, const InlineSlots& is, in
 hipError_t launch_copy_words(const int32_t* src, int32_t* dst, int64_t n, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, int D, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs& a, int D, int C, hipStream_t s);
+// moves with a source or destination outside [0, slot_limit) are skipped;
+// sources and destinations must be disjoint slot sets
+hipError_t launch_move(const MoveArgs& a, int D, int C, hipStream_t s);
 
 }  // namespace pkvt

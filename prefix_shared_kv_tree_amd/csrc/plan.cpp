@@ -10,6 +10,11 @@
 // 3. Phase 2 (sequence-first): the rest of each sequence's path -- always a
 //    suffix, since coverage can only shrink towards the leaves -- cut into
 //    items of at most phase2_chunks chunks.
+//    Under token-granular matching a node may hold fewer than C tokens
+//    anywhere on a path.  A kernel item addresses key k at chunk k / C, so an
+//    item may end with a partial chunk but hold none before that: segments
+//    and phase-2 runs are cut after every partial node, and an item that
+//    ends in one carries the keys it lacks (tail).
 // 4. A sequence with exactly one item, a phase-2 one, is finalised by that
 //    item; every other sequence's partials are merged afterwards.
 // 5. The attention kernel runs G persistent workgroups of 4 waves.  Work is
@@ -174,6 +179,7 @@ struct Item {
     std::vector<int32_t> chunks;
     int32_t key_base = 0;
     int32_t len_row = -1;
+    int32_t tail = 0;            // keys missing from the last chunk when len_row < 0
     int32_t row_lo = 0;
     int32_t n_rows = 0;
     int32_t out = -1;
@@ -353,7 +359,8 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     for (int32_t x : preorder) {
         if (cov(x) < opts.min_share) continue;
         const int32_t p = t.node(x).parent;
-        if (p != root && info[p].seg >= 0 && info[p].i == info[x].i && info[p].j == info[x].j) {
+        if (p != root && info[p].seg >= 0 && info[p].i == info[x].i && info[p].j == info[x].j &&
+            t.node(p).fill == t.C) {
             segs[info[p].seg].push_back(x);
             info[x].seg = info[p].seg;
         } else {
@@ -362,14 +369,21 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
             seg_range.push_back(Range{info[x].i, info[x].j});
         }
     }
-    // private suffix of every sequence: path[k0[p] ..)
+    // private suffix of every sequence: path[k0[p] ..), starting at token pos0[p]
     std::vector<int32_t> k0(b);
+    std::vector<int64_t> pos0(b);
     for (int32_t p = 0; p < b; ++p) {
-        const std::vector<int32_t>& path = seqs[dfs_row[p]]->path;
+        const Seq* sq = seqs[dfs_row[p]];
+        const std::vector<int32_t>& path = sq->path;
         int32_t k = static_cast<int32_t>(path.size());
-        while (k > 0 && cov(path[k - 1]) < opts.min_share) --k;
+        int64_t pos = sq->len;
+        while (k > 0 && cov(path[k - 1]) < opts.min_share) pos -= t.node(path[--k]).fill;
         k0[p] = k;
+        pos0[p] = pos;
     }
+    std::vector<int64_t> seg_keys(segs.size(), 0);
+    for (size_t s = 0; s < segs.size(); ++s)
+        for (int32_t x : segs[s]) seg_keys[s] += t.node(x).fill;
 
     // ---- item size ----------------------------------------------------------------
     // T = the mean per-wave load in 64-key steps with nothing cut (a unit
@@ -385,7 +399,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     if (s1 == 0 || s2 == 0) {
         int64_t quarters = 0;
         for (size_t s = 0; s < segs.size(); ++s) {
-            const int64_t st = steps_of(static_cast<int64_t>(segs[s].size()) * t.C);
+            const int64_t st = steps_of(seg_keys[s]);
             const int32_t rows = seg_range[s].j - seg_range[s].i;
             for (const int32_t rb : row_blocks(rows, opts.unit_rows)) {
                 if (rb >= opts.unit_rows)
@@ -395,7 +409,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
             }
         }
         for (int32_t p = 0; p < b; ++p)
-            quarters += 4 * steps_of(seqs[dfs_row[p]]->len - static_cast<int64_t>(k0[p]) * t.C);
+            quarters += 4 * steps_of(seqs[dfs_row[p]]->len - pos0[p]);
         const int64_t mean = std::max<int64_t>(1, (quarters * t.H + 4 * lanes - 1) / (4 * lanes));
         if (s1 == 0) s1 = steps_to_chunks(mean, t.C);
         if (s2 == 0) {
@@ -434,6 +448,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         for (size_t q = 0; q + 1 < at.size(); ++q) {
             Item it;
             it.chunks.assign(segs[s].begin() + at[q], segs[s].begin() + at[q + 1]);
+            it.tail = t.C - t.node(it.chunks.back()).fill;     // only a segment's last node is partial
             it.row_lo = seg_range[s].i;
             it.n_rows = seg_range[s].j - seg_range[s].i;
             for (int32_t p = seg_range[s].i; p < seg_range[s].j; ++p) src_count[p]++;
@@ -444,19 +459,28 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     for (int32_t p = 0; p < b; ++p) {
         const std::vector<int32_t>& path = seqs[dfs_row[p]]->path;
         const int32_t n = static_cast<int32_t>(path.size());
-        if (k0[p] == n) continue;
-        const std::vector<int32_t> at = cuts(n - k0[p], s2);
-        for (size_t q = 0; q + 1 < at.size(); ++q) {
-            Item it;
-            const int32_t a = k0[p] + at[q];
-            const int32_t e = k0[p] + at[q + 1];
-            it.chunks.assign(path.begin() + a, path.begin() + e);
-            it.key_base = a * t.C;
-            it.len_row = (e == n) ? p : -1;
-            it.row_lo = p;
-            it.n_rows = 1;
-            src_count[p]++;
-            items2.push_back(std::move(it));
+        int64_t pos = pos0[p];
+        // runs of full chunks ending at a partial node or at the leaf
+        for (int32_t r0 = k0[p]; r0 < n;) {
+            int32_t r1 = r0;
+            while (r1 < n - 1 && t.node(path[r1]).fill == t.C) ++r1;
+            ++r1;
+            const std::vector<int32_t> at = cuts(r1 - r0, s2);
+            for (size_t q = 0; q + 1 < at.size(); ++q) {
+                Item it;
+                const int32_t a = r0 + at[q];
+                const int32_t e = r0 + at[q + 1];
+                it.chunks.assign(path.begin() + a, path.begin() + e);
+                it.key_base = static_cast<int32_t>(pos + static_cast<int64_t>(at[q]) * t.C);
+                it.len_row = (e == n) ? p : -1;
+                if (e < n) it.tail = t.C - t.node(path[e - 1]).fill;
+                it.row_lo = p;
+                it.n_rows = 1;
+                src_count[p]++;
+                items2.push_back(std::move(it));
+            }
+            for (int32_t k = r0; k < r1; ++k) pos += t.node(path[k]).fill;
+            r0 = r1;
         }
     }
 
@@ -483,7 +507,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     std::vector<const std::vector<int32_t>*> wave_chunks;
     std::vector<int64_t> wave_cost;
     auto item_keys = [&](const Item& it) {
-        int64_t keys = static_cast<int64_t>(it.chunks.size()) * t.C;
+        int64_t keys = static_cast<int64_t>(it.chunks.size()) * t.C - it.tail;
         if (it.len_row >= 0)
             keys = std::min<int64_t>(keys, seqs[dfs_row[it.len_row]]->len - it.key_base);
         return keys;
@@ -493,6 +517,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         w.n_chunks = static_cast<int32_t>(it.chunks.size());
         w.key_base = it.key_base;
         w.len_row = it.len_row;
+        w.tail = it.tail;
         w.row_lo = it.row_lo + row_off;
         w.n_rows = std::min(kRowsPerWave, it.n_rows - row_off);
         w.out = it.out < 0 ? -1 : it.out + row_off;
@@ -746,6 +771,14 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
                       " must lie in [0, length)";
                 return PKVT_ERR_INVALID_ARG;
             }
+            // positions map to chunks as pos / C: every chunk before the leaf full
+            for (size_t k = 0; k + 1 < sq->path.size(); ++k)
+                if (t.node(sq->path[k]).fill != C) {
+                    err = "prefill_plan: sequence " + std::to_string(seq_ids[s]) +
+                          " holds a partial chunk before its leaf (token-granular sharing); "
+                          "prefill plans need whole chunks up to the leaf";
+                    return PKVT_ERR_INVALID_ARG;
+                }
             seqs[s] = sq;
             nrows[s] = sq->len - q_from[s];
             R += nrows[s];
@@ -757,7 +790,6 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     }
 
     // ---- depth-first order; row numbering -------------------------------------
-    const int32_t root = t.root();
     std::vector<int32_t> dfs_seq, preorder;
     if (!batch_dfs(t, seqs, plan.scratch, dfs_seq, preorder)) {
         err = "prefill_plan: internal error, depth-first order lost rows";

@@ -40,7 +40,7 @@ struct WaveDesc {
     int32_t row_lo;      // depth-first position of query row 0
     int32_t n_rows;      // 1..16
     int32_t out;         // partial slot of row 0, or -1: write O directly (n_rows == 1)
-    int32_t pad;
+    int32_t tail;        // keys missing from the last chunk (len_row < 0): C minus its fill
 };
 static_assert(sizeof(WaveDesc) == 32, "WaveDesc is 8 int32");
 

@@ -4,13 +4,14 @@
 
 #include <algorithm>
 #include <cstring>
+#include <memory>
 
 #include "pkvt.h"
 
 namespace pkvt {
 
-Tree::Tree(int32_t h, int32_t d, int32_t c, int32_t pool_chunks)
-    : H(h), D(d), C(c), N(pool_chunks), nodes_(static_cast<size_t>(pool_chunks) + 1) {
+Tree::Tree(int32_t h, int32_t d, int32_t c, int32_t pool_chunks, Match m)
+    : H(h), D(d), C(c), N(pool_chunks), match(m), nodes_(static_cast<size_t>(pool_chunks) + 1) {
     free_.reserve(pool_chunks);
     for (int32_t i = pool_chunks - 1; i >= 0; --i) free_.push_back(i);   // pops 0, 1, 2, ...
     nodes_[N].live = true;                                               // the root
@@ -38,6 +39,7 @@ int32_t Tree::find_full_child(int32_t parent, const int32_t* t) const {
 }
 
 void Tree::index_full(int32_t id) {
+    if (match != Match::kChunks) return;                 // token matching compares prefixes
     Node& n = nodes_[id];
     n.key_hash = hash_tokens(n.tokens.data());
     auto& bucket = nodes_[n.parent].full_children[n.key_hash];
@@ -47,6 +49,7 @@ void Tree::index_full(int32_t id) {
 }
 
 void Tree::unindex_full(int32_t id) {
+    if (match != Match::kChunks) return;
     Node& n = nodes_[id];
     auto& map = nodes_[n.parent].full_children;
     auto it = map.find(n.key_hash);
@@ -101,6 +104,7 @@ const Seq* Tree::find_seq(int32_t id) const {
 
 int Tree::build(int32_t n_seqs, const int32_t* tokens, const int64_t* offsets,
                 int32_t* seq_ids, int64_t* slots, std::string& err) {
+    moves_.clear();
     if (n_seqs < 0 || (n_seqs > 0 && (!tokens || !offsets || !seq_ids || !slots))) {
         err = "tree_build: null pointer or negative n_seqs";
         return PKVT_ERR_INVALID_ARG;
@@ -119,6 +123,7 @@ int Tree::build(int32_t n_seqs, const int32_t* tokens, const int64_t* offsets,
             return PKVT_ERR_EMPTY_SEQ;
         }
     }
+    if (match == Match::kTokens) return build_tokens(n_seqs, tokens, offsets, seq_ids, slots, err);
     // Everything below is undone on NO_CHUNKS.
     std::vector<int32_t> created;
     std::vector<int32_t> added;
@@ -207,8 +212,9 @@ int Tree::append(int32_t n, const int32_t* seq_ids, const int32_t* tokens, int64
         Seq& s = it->second;
         const int32_t leaf = s.path.back();
         Node& x = nodes_[leaf];
-        if (x.fill < C) {
-            // a partial leaf is always private to its sequence
+        if (x.fill < C && x.refs == 1 && x.children.empty()) {
+            // a partial, private, childless leaf (with whole-chunk matching
+            // every partial leaf is one)
             x.tokens.push_back(tokens[i]);
             x.fill++;
             const bool filled = (x.fill == C);
@@ -232,6 +238,131 @@ int Tree::append(int32_t n, const int32_t* seq_ids, const int32_t* tokens, int64
     }
     if (n > 0) ++len_version_;
     if (structural) ++struct_version_;
+    return PKVT_OK;
+}
+
+// Token-granular arrival (see tree.h).  Slots are assigned once all prompts
+// are in, from the final paths, because a later prompt of the same call may
+// split a node an earlier one created.  A split's new node records where its
+// tokens' K/V physically are (src); nodes created by this call that are not
+// in src hold only tokens the caller has yet to write.
+int Tree::build_tokens(int32_t n_seqs, const int32_t* tokens, const int64_t* offsets,
+                       int32_t* seq_ids, int64_t* slots, std::string& err) {
+    // At most one split and ceil(L / c) new chunks per prompt: with that many
+    // free chunks the call cannot fail, otherwise keep a copy to roll back to.
+    int64_t bound = 0;
+    for (int32_t s = 0; s < n_seqs; ++s) bound += (offsets[s + 1] - offsets[s] + C - 1) / C + 1;
+    struct Snapshot {
+        std::vector<Node> nodes;
+        std::vector<int32_t> free;
+        std::unordered_map<int32_t, Seq> seqs;
+        int32_t next_seq;
+        int64_t next_created;
+    };
+    std::unique_ptr<Snapshot> snap;
+    if (bound > static_cast<int64_t>(free_.size()))
+        snap.reset(new Snapshot{nodes_, free_, seqs_, next_seq_, next_created_});
+    auto out_of_chunks = [&]() {
+        nodes_ = std::move(snap->nodes);
+        free_ = std::move(snap->free);
+        seqs_ = std::move(snap->seqs);
+        next_seq_ = snap->next_seq;
+        next_created_ = snap->next_created;
+        moves_.clear();
+        err = "tree_build: chunk pool exhausted (" + std::to_string(N) + " chunks)";
+        return PKVT_ERR_NO_CHUNKS;
+    };
+    const int64_t created_mark = next_created_;
+    std::unordered_map<int32_t, std::vector<int64_t>> src;
+    auto src_of = [&](int32_t id, int32_t k) -> int64_t {
+        auto it = src.find(id);
+        if (it != src.end()) return it->second[k];
+        return nodes_[id].created >= created_mark ? -1 : static_cast<int64_t>(id) * C + k;
+    };
+    auto split = [&](int32_t y, int32_t t) {
+        const int32_t id = free_.back();
+        free_.pop_back();
+        Node& x = nodes_[id];
+        Node& old = nodes_[y];
+        x.parent = y;
+        x.fill = old.fill - t;
+        x.refs = old.refs;
+        x.created = next_created_++;
+        x.live = true;
+        x.full_children.clear();
+        x.tokens.assign(old.tokens.begin() + t, old.tokens.end());
+        x.children = std::move(old.children);
+        for (int32_t ch : x.children) nodes_[ch].parent = id;
+        std::vector<int64_t> from(x.fill);
+        bool any = false;
+        for (int32_t k = 0; k < x.fill; ++k) any |= (from[k] = src_of(y, t + k)) >= 0;
+        if (any) src[id] = std::move(from);
+        auto it = src.find(y);
+        if (it != src.end()) it->second.resize(t);
+        old.children.assign(1, id);
+        old.tokens.resize(t);
+        old.fill = t;
+        for (auto& kv : seqs_) {
+            std::vector<int32_t>& path = kv.second.path;
+            auto at = std::find(path.begin(), path.end(), y);
+            if (at != path.end()) path.insert(at + 1, id);
+        }
+    };
+    std::vector<int64_t> matched(n_seqs);
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        const int64_t beg = offsets[s], L = offsets[s + 1] - offsets[s];
+        const int32_t* t = tokens + beg;
+        Seq seq;
+        seq.len = L;
+        int32_t at = root();
+        int64_t pos = 0;
+        while (pos < L) {
+            int32_t best = -1, best_len = 0;
+            for (int32_t ch : nodes_[at].children) {          // creation order
+                const Node& x = nodes_[ch];
+                const int32_t lim = static_cast<int32_t>(std::min<int64_t>(x.fill, L - pos));
+                int32_t k = 0;
+                while (k < lim && x.tokens[k] == t[pos + k]) ++k;
+                if (k > best_len) {
+                    best = ch;
+                    best_len = k;
+                }
+            }
+            if (best < 0) break;
+            if (best_len < nodes_[best].fill) {
+                if (free_.empty()) return out_of_chunks();
+                split(best, best_len);
+            }
+            seq.path.push_back(best);
+            at = best;
+            pos += best_len;
+        }
+        matched[s] = pos;
+        while (pos < L) {
+            if (free_.empty()) return out_of_chunks();
+            const int32_t n = static_cast<int32_t>(std::min<int64_t>(C, L - pos));
+            at = alloc_node(at, t + pos, n);
+            seq.path.push_back(at);
+            pos += n;
+        }
+        for (int32_t x : seq.path) nodes_[x].refs++;
+        const int32_t sid = next_seq_++;
+        seqs_.emplace(sid, std::move(seq));
+        seq_ids[s] = sid;
+    }
+    // slots from the final paths: tokens a prompt did not match are its own
+    for (int32_t s = 0; s < n_seqs; ++s) {
+        int64_t p = 0;
+        int64_t* out = slots + offsets[s];
+        for (int32_t x : seqs_[seq_ids[s]].path)
+            for (int32_t k = 0; k < nodes_[x].fill; ++k, ++p)
+                out[p] = p >= matched[s] ? static_cast<int64_t>(x) * C + k : -1;
+    }
+    for (const auto& kv : src)
+        for (int32_t k = 0; k < nodes_[kv.first].fill; ++k)
+            if (kv.second[k] >= 0) moves_.emplace_back(kv.second[k], static_cast<int64_t>(kv.first) * C + k);
+    std::sort(moves_.begin(), moves_.end());
+    if (n_seqs > 0) ++struct_version_;
     return PKVT_OK;
 }
 

@@ -13,6 +13,17 @@
 //   * a chunk filled by decode appends becomes matchable; nodes are never
 //     merged; among live full children with equal tokens a lookup takes the
 //     earliest created one.
+//
+// Token-granular matching (Match::kTokens), a variant the page does not
+// describe (its nodes are whole chunks): a node holds 1..c tokens at the
+// start of its chunk.  An arrival descends into the child sharing the
+// longest common prefix with the rest of its prompt (ties: earliest created)
+// and splits a child it matches only in part: the child keeps the matched
+// tokens, a new node below it takes the rest and the old children, and the
+// rest's K/V must move to the new node's chunk (moves()).  A decode append
+// writes into the leaf only while it is partial, private and childless.
+// Shared prefixes that end inside a chunk are then stored once, at the cost
+// of partial chunks inside the tree.
 #pragma once
 
 #include <cstdint>
@@ -40,11 +51,14 @@ struct Seq {
     int64_t len = 0;
 };
 
+enum class Match : int32_t { kChunks = 0, kTokens = 1 };
+
 class Tree {
 public:
-    Tree(int32_t h, int32_t d, int32_t c, int32_t pool_chunks);
+    Tree(int32_t h, int32_t d, int32_t c, int32_t pool_chunks, Match match = Match::kChunks);
 
     int32_t H, D, C, N;
+    Match match;
     int32_t root() const { return N; }
 
     // Return codes are the PKVT_* status values; err receives a message.
@@ -60,6 +74,11 @@ public:
     int32_t shared_chunks() const;
     int32_t live_seqs() const { return (int32_t)seqs_.size(); }
 
+    // K/V that the last build moved between slots (token matching): the
+    // token at slot first now belongs at slot second.  Sources lie in chunks
+    // that existed before that build, destinations in chunks it allocated.
+    const std::vector<std::pair<int64_t, int64_t>>& moves() const { return moves_; }
+
     // Bumped on every change of which chunks form which paths.
     int64_t structure_version() const { return struct_version_; }
     // Bumped on every decode append (sequence lengths change).
@@ -73,6 +92,10 @@ private:
     int64_t next_created_ = 0;
     int64_t struct_version_ = 0;
     int64_t len_version_ = 0;
+    std::vector<std::pair<int64_t, int64_t>> moves_;
+
+    int build_tokens(int32_t n_seqs, const int32_t* tokens, const int64_t* offsets,
+                     int32_t* seq_ids, int64_t* slots, std::string& err);
 
     uint64_t hash_tokens(const int32_t* t) const;
     int32_t find_full_child(int32_t parent, const int32_t* t) const;

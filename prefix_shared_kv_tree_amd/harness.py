@@ -51,10 +51,16 @@ class DecodeSetup:
     def __init__(self, w, layers: Optional[int] = None, pool_slack: int = 0, device: str = "cuda",
                  phase1_chunks: int = 0, phase2_chunks: int = 0, min_share: int = 0,
                  pool_chunks: Optional[int] = None, unit_rows: int = 0,
-                 device_random_seed: Optional[int] = None):
+                 device_random_seed: Optional[int] = None, match: str = "chunks",
+                 build_groups: int = 1):
         """``device_random_seed``: instead of the workload's K/V (which may
         then be absent), fill the pools and Q with N(0,1) fp16 drawn on the
-        device (for timing sweeps that need no oracle)."""
+        device (for timing sweeps that need no oracle).  ``match``: the
+        tree's prefix matching ("chunks" or "tokens").  ``build_groups``:
+        insert the sequences in that many successive pkvt_tree_build calls
+        (in order); under token matching a later call may split nodes of an
+        earlier one, whose K/V then move (pkvt_kv_move) before the new
+        tokens are written."""
         import torch
         self.torch = torch
         self.w = w
@@ -62,11 +68,30 @@ class DecodeSetup:
         self.device = device
         total_tokens = sum(w.seq_len(u) for u in range(w.b))
         if pool_chunks is None:
-            # enough for a tree with nothing shared, plus slack
+            # enough for a tree with nothing shared (and, under token matching,
+            # one split per arrival), plus slack
             pool_chunks = sum(-(-w.seq_len(u) // w.c) for u in range(w.b)) + pool_slack
+            if match == "tokens":
+                pool_chunks += w.b
         self.pool_chunks = pool_chunks
-        self.tree = B.pkvt_tree_create(w.h, w.d, w.c, pool_chunks)
-        self.seq_ids, self.slots = B.pkvt_tree_build(self.tree, w.all_seq_tokens())
+        self.tree = B.pkvt_tree_create(w.h, w.d, w.c, pool_chunks, match=match)
+        prompts = w.all_seq_tokens()
+        bounds = np.linspace(0, w.b, max(1, build_groups) + 1).astype(int)
+        ids_parts, builds = [], []           # per call: (full-length slots, move src, move dst)
+        tok_at = np.cumsum([0] + [len(p) for p in prompts])
+        for a, e in zip(bounds[:-1], bounds[1:]):
+            if e <= a:
+                continue
+            ids, sl = B.pkvt_tree_build(self.tree, prompts[a:e])
+            full = np.full(int(tok_at[-1]), -1, np.int64)
+            full[tok_at[a]:tok_at[e]] = sl
+            src, dst = B.pkvt_tree_moves(self.tree)
+            ids_parts.append(ids)
+            builds.append((full, src, dst))
+        self.seq_ids = np.concatenate(ids_parts).astype(np.int32)
+        # each token's slot as its build returned it (later splits may move it)
+        self.slots = np.max(np.stack([bl[0] for bl in builds]), axis=0)
+        self.moves = sum(int(bl[1].size) for bl in builds)
         assert self.slots.shape[0] == total_tokens
         pool_elems = B.pkvt_pool_bytes(w.h, w.d, w.c, pool_chunks) // 2
         self.k_pools: List = []
@@ -85,15 +110,23 @@ class DecodeSetup:
                 self.k_pools.append(kp)
                 self.v_pools.append(vp)
                 continue
-            k_new, v_new, s_new = gather_new_tokens(w, self.slots, layer)
-            if s_new.size:
-                kd = torch.from_numpy(np.ascontiguousarray(k_new)).to(device)
-                vd = torch.from_numpy(np.ascontiguousarray(v_new)).to(device)
-                sd = torch.from_numpy(s_new).to(device)
-                B.pkvt_kv_scatter(self.tree, kp.data_ptr(), vp.data_ptr(), sd.data_ptr(),
-                                  kd.data_ptr(), vd.data_ptr(), s_new.size, stream)
-                torch.cuda.synchronize()
-                del kd, vd, sd
+            for full, src, dst in builds:
+                if src.size:
+                    ms = torch.from_numpy(src).to(device)
+                    md = torch.from_numpy(dst).to(device)
+                    B.pkvt_kv_move(self.tree, kp.data_ptr(), vp.data_ptr(), ms.data_ptr(),
+                                   md.data_ptr(), src.size, stream)
+                    torch.cuda.synchronize()
+                    del ms, md
+                k_new, v_new, s_new = gather_new_tokens(w, full, layer)
+                if s_new.size:
+                    kd = torch.from_numpy(np.ascontiguousarray(k_new)).to(device)
+                    vd = torch.from_numpy(np.ascontiguousarray(v_new)).to(device)
+                    sd = torch.from_numpy(s_new).to(device)
+                    B.pkvt_kv_scatter(self.tree, kp.data_ptr(), vp.data_ptr(), sd.data_ptr(),
+                                      kd.data_ptr(), vd.data_ptr(), s_new.size, stream)
+                    torch.cuda.synchronize()
+                    del kd, vd, sd
             self.k_pools.append(kp)
             self.v_pools.append(vp)
         if gen is not None:

@@ -306,6 +306,22 @@ def unshare(w: Workload, token_offset: int = 1 << 20) -> Workload:
                     seq_paths=paths, q=w.q, layers=w.layers)
 
 
+def unique_segment_starts(w: Workload, base: int = VOCAB) -> Workload:
+    """Give every segment a first token id that no other segment starts with
+    (ids from ``base`` on), so that two contexts share exactly their common
+    leading segments however finely a prefix tree matches tokens.  K/V values
+    belong to segments, so token-granular sharing then never joins tokens
+    with different K/V.  Lengths, K/V and Q are unchanged."""
+    segs = []
+    for i, sg in enumerate(w.segments):
+        t = sg.tokens.copy()
+        if t.size:
+            t[0] = base + i
+        segs.append(Segment(tokens=t, k=sg.k, v=sg.v))
+    return Workload(name=w.name, h=w.h, d=w.d, c=w.c, segments=segs,
+                    seq_paths=[list(p) for p in w.seq_paths], q=w.q, layers=w.layers)
+
+
 def unique_tokens(w: Workload) -> int:
     """Number of distinct token positions when every full-chunk prefix is
     stored once: this is the count of *stored* KV rows, used for the

@@ -41,10 +41,20 @@ def parse(blob: np.ndarray) -> dict:
 
 
 def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: int = 2,
-               max_rows: int = 16, heads: int = 1, unit_rows: int = 17):
-    """paths / lens: seq id -> chunk path / token count (from the tree).
-    Raises AssertionError on any violation."""
+               max_rows: int = 16, heads: int = 1, unit_rows: int = 17, fills: dict = None):
+    """paths / lens: seq id -> chunk path / token count (from the tree);
+    fills: chunk id -> tokens stored (default: whole-chunk matching, every
+    chunk before a leaf full).  Raises AssertionError on any violation."""
     assert plan["magic"] == MAGIC
+    if fills is None:
+        fills = {}
+        for sid, path in paths.items():
+            for k, x in enumerate(path):
+                fills[int(x)] = c if k + 1 < len(path) else lens[sid] - c * (len(path) - 1)
+
+    def start_of(path, k):
+        """Sequence position of the first token of path[k]."""
+        return sum(fills[int(y)] for y in path[:k])
     b = plan["b"]
     q_order = [int(x) for x in q_order]
     rows = [int(r) for r in plan["rows"]]
@@ -67,7 +77,7 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
     direct = set()
     phase1 = []
     for wi, (w, ch) in enumerate(zip(plan["waves"], plan["wave_chunks"])):
-        chunk_off, n_chunks, key_base, len_row, row_lo, n_rows, out, _ = [int(v) for v in w]
+        chunk_off, n_chunks, key_base, len_row, row_lo, n_rows, out, tail = [int(v) for v in w]
         assert n_chunks == len(ch) >= 1 and 1 <= n_rows <= max_rows
         multi = None
         for x in ch:
@@ -86,14 +96,14 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
         p0 = row_lo
         path = [int(y) for y in paths[seq_at[p0]]]
         last = path.index(int(ch[-1]))
+        # every chunk but the last is full (keys map to chunk k / c)
+        for x in ch[:-1]:
+            assert fills[int(x)] == c
         if last == len(path) - 1 and not multi:
-            assert len_row == p0 and key_base == path.index(int(ch[0])) * c
+            assert len_row == p0 and key_base == start_of(path, path.index(int(ch[0]))) and tail == 0
         else:
             assert len_row == -1
-            # all chunks of such a wave are full
-            for x in ch:
-                k = path.index(int(x))
-                assert (k + 1) * c <= lens[seq_at[p0]]
+            assert n_chunks * c - tail == sum(fills[int(x)] for x in ch)
         if out < 0:
             assert n_rows == 1
             direct.add(row_lo)
@@ -112,7 +122,8 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
     assert at == len(plan["units"])
     for u, ch in zip(plan["units"], plan["unit_chunks"]):
         n_keys, chunk_off, n_chunks, head, row_lo, n_rows, out, _ = [int(v) for v in u]
-        assert n_chunks == len(ch) >= 1 and n_keys == n_chunks * c
+        assert n_chunks == len(ch) >= 1 and n_keys == sum(fills[int(x)] for x in ch)
+        assert all(fills[int(x)] == c for x in ch[:-1])
         assert max(max_rows + 1, unit_rows) <= n_rows <= ROWS_PER_UNIT
         assert 0 <= head < heads and out >= 0
         unit_heads[(row_lo, n_rows, out, tuple(int(x) for x in ch))].append(head)
@@ -122,9 +133,6 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
             assert len(cover[x]) >= min_share, "a unit reads an unshared chunk"
             for p in range(row_lo, row_lo + n_rows):
                 assert x in [int(y) for y in paths[seq_at[p]]], "unit reads a chunk not on the row's path"
-                # full chunks only
-                k = [int(y) for y in paths[seq_at[p]]].index(x)
-                assert (k + 1) * c <= lens[seq_at[p]]
                 seen[(p, x)] += 1
                 chunk_rows[x].add(p)
         for r in range(n_rows):
