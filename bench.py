@@ -564,21 +564,25 @@ PAGE_DIVERGENCE = {
 PAGE_BATCH = {16: 155.0, 96: 224.0}
 
 
-def sweep_time(torch, B, W, b, n_s, private, seed, variant, steps, warmup, ev, h=32, d=128, c=64):
+def sweep_time(torch, B, W, b, n_s, private, seed, variant, steps, warmup, ev, h=32, d=128, c=64,
+               match="chunks"):
     """µs per layer of one decode batch: b sequences sharing n_s prompt
     tokens, each with `private` tokens of its own (a count, or one per
     sequence), K/V and Q drawn on the device; steps rotate over enough layer
-    pools to defeat the Infinity Cache."""
+    pools to defeat the Infinity Cache.  `match`: the tree's prefix matching;
+    under "chunks" a prefix that ends inside a chunk leaves that chunk's
+    tokens private to every sequence."""
     from prefix_shared_kv_tree_amd.harness import DecodeSetup
-    w = W.one_prefix(seed, b, n_s, private, h=h, d=d, c=c, with_kv=False)
+    w = W.unique_segment_starts(W.one_prefix(seed, b, n_s, private, h=h, d=d, c=c, with_kv=False))
     b_tok = w.h * w.d * 2 * 2
     unique = (n_s + int(np.sum(np.broadcast_to(private, (b,))))) * b_tok
     layers = max(2, math.ceil(2 * 2 ** 30 / unique))
-    ds = DecodeSetup(w, layers=layers, device_random_seed=seed,
+    ds = DecodeSetup(w, layers=layers, device_random_seed=seed, match=match,
                      min_share=(1 << 20) if variant == "plain" else 0)
     stream = torch.cuda.current_stream().cuda_stream
     total_ms, _, _, _ = time_region(ds, B, ev, stream, steps, warmup, per_kernel=False)
     info = dict(ds.info)
+    info["used_chunks"] = B.pkvt_tree_stats(ds.tree)["used_chunks"]
     ds.close()
     del ds
     return total_ms / steps * 1e3, info, unique
@@ -618,6 +622,32 @@ def run_sweep(args):
         print(json.dumps({"sweep": "shapes", "b": 64, "n_s": 4096, "private": "uniform [256, 1024]",
                           "dtype": "f16", "data": "synthetic, device N(0,1)",
                           "steps_per_point": args.sweep_steps, "points": points}), flush=True)
+        return
+    if args.sweep == "tokens":
+        # shared prompts that end inside a chunk: whole-chunk matching keeps the
+        # prompt's last partial chunk private (one copy per sequence, read per
+        # sequence); token-granular matching stores and reads it once
+        rng = np.random.Generator(np.random.PCG64(1002))
+        priv = [int(x) for x in rng.integers(256, 1025, size=64)]
+        points = []
+        for n_s in (40, 1000, 2000, 4000):
+            row = {"n_s": n_s, "n_s_mod_c": n_s % 64}
+            for match in ("chunks", "tokens"):
+                t, info, unique = sweep_time(torch, B, W, 64, n_s, priv, 3400 + n_s, "tpp",
+                                             args.sweep_steps, 10, ev, match=match)
+                stored = info["unique_tokens"] * 32 * 128 * 4
+                row[match] = {"us_per_layer": round(t, 2), "stored_tokens": info["unique_tokens"],
+                              "used_chunks": info["used_chunks"],
+                              "stored_kv_gbps": round(stored / (t * 1e-6) / 1e9, 1),
+                              "frac_hbm_peak": round(stored / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                              "phase1_items": info["phase1_items"], "wg_units": info["wg_units"]}
+            row["speedup_tokens_vs_chunks"] = round(row["chunks"]["us_per_layer"] /
+                                                    row["tokens"]["us_per_layer"], 3)
+            print(json.dumps(row), file=sys.stderr, flush=True)
+            points.append(row)
+        print(json.dumps({"sweep": "tokens", "b": 64, "private": "uniform [256, 1024]", "h": 32,
+                          "d": 128, "c": 64, "dtype": "f16", "data": "synthetic, device N(0,1)",
+                          "points": points}), flush=True)
         return
     if args.sweep == "shard":
         # one GPU's share of the long-shared-prompt batch when G GPUs split the
@@ -778,7 +808,7 @@ def main():
     ap.add_argument("--loop-churn", type=int, default=16,
                     help="a row gets a new sequence every this many decode-loop steps")
     ap.add_argument("--no-loop", action="store_true")
-    ap.add_argument("--sweep", choices=["divergence", "batch", "shapes", "shard"],
+    ap.add_argument("--sweep", choices=["divergence", "batch", "shapes", "shard", "tokens"],
                     help="time the decode-throughput sweeps of the pages' divergence (Knowl 8) "
                          "or batch-size (Knowl 9) experiments instead of the benchmark")
     ap.add_argument("--sweep-steps", type=int, default=60)
