@@ -57,6 +57,7 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;          // waves per workgroup
@@ -74,6 +75,13 @@ struct Step {
 };
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// A compile-time flag passed to generic lambdas (two instantiations of a
+// loop body chosen by a wave-uniform branch).
+template <bool B>
+struct Flag {
+    static constexpr bool value = B;
+};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -134,44 +142,49 @@ __device__ __forceinline__ void qk(f4 (&s)[NT], const h8 (&kr)[NT][KS], const h8
 // kSkip (compute-bound prefill units): the key mask and the rescale of o
 // are skipped, wave-wide, on steps where no lane needs them (no lane's keys
 // end inside the step; no lane's running max moved).
+// With a positive scale (the attention scale always is) the scores stay
+// unscaled: their max is scaled once and each weight is exp2 of one fused
+// multiply-add, s * scale - m.  Other scales scale the scores first.  The
+// running sum adds the fp16 weights that the P V product uses, two at a
+// time with a packed dot product against (1, 1).
 template <int NT, int DT, bool kSkip = false>
 __device__ __forceinline__ void softmax_step(f4 (&s)[NT], h4 (&pq)[NT], f4 (&o)[DT], float& m_run,
                                              float& l_run, int step, int n_valid, int grp,
                                              float scale_log2e) {
     const int key0 = step * 16 * NT;
     const bool tail = key0 + 16 * NT > n_valid;
-    float mx = -INFINITY;
-    if (kSkip && !__any(tail)) {
+    const bool raw = scale_log2e > 0.f;          // kernel argument: uniform
+    const float sc = raw ? scale_log2e : 1.f;
+    if (!raw) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) s[tt] *= scale_log2e;
+    }
+    if (!kSkip || __any(tail)) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[tt][i] *= scale_log2e;
-                mx = fmaxf(mx, s[tt][i]);
-            }
-    } else {
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x = s[tt][i] * scale_log2e;
-                if (tail && key0 + 16 * tt + 4 * grp + i >= n_valid) x = -INFINITY;
-                s[tt][i] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
+            for (int i = 0; i < 4; ++i)
+                if (tail && key0 + 16 * tt + 4 * grp + i >= n_valid) s[tt][i] = -INFINITY;
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);        // finite: every step has a valid key
+    const float m_new = fmaxf(m_run, mx * sc);   // finite: every step has a valid key
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
     float lsum = 0.f;
+    const h2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 #pragma unroll
-    for (int e = 0; e < 4 * NT; ++e) {
-        const _Float16 p = static_cast<_Float16>(fast_exp2(s[e >> 2][e & 3] - m_new));
-        pq[e >> 2][e & 3] = p;
-        lsum += static_cast<float>(p);
+    for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pq[tt][i] = static_cast<_Float16>(fast_exp2(__builtin_fmaf(s[tt][i], sc, -m_new)));
+        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pq[tt], pq[tt], 0, 1), one, lsum, false);
+        lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pq[tt], pq[tt], 2, 3), one, lsum, false);
     }
     l_run = l_run * alpha + lsum;
     if (!kSkip || __any(alpha != 1.0f)) {
@@ -383,17 +396,26 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
             h4 pq[NT];
             softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, kCausal ? lim : n_keys, grp,
                                  a.scale_log2e);
+            // V entries past the last key are zeroed on the last step only
+            auto pv = [&](auto masked) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                h4 v[NT];
+                for (int dt = 0; dt < DT; ++dt) {
+                    h4 v[NT];
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
-                    v[tt] = mask_v(
-                        *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
-                                                     (tt * 4 + grp) * Img<D>::kGroupV + (16 * dt + col) * 8),
-                        step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
-                o[dt] = pv_tile<NT>(o[dt], v, pq);
-            }
+                    for (int tt = 0; tt < NT; ++tt) {
+                        v[tt] = *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
+                                                             (tt * 4 + grp) * Img<D>::kGroupV +
+                                                             (16 * dt + col) * 8);
+                        if constexpr (decltype(masked)::value)
+                            v[tt] = mask_v(v[tt], step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+                    }
+                    o[dt] = pv_tile<NT>(o[dt], v, pq);
+                }
+            };
+            if ((step + 1) * Step<D>::kKeys > n_keys)
+                pv(Flag<true>{});
+            else
+                pv(Flag<false>{});
         }
     }
     // a prefill unit whose rows read nothing else writes O itself (out < 0)
@@ -535,18 +557,27 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         for (int rt = 0; rt < RT; ++rt)
             softmax_step<NT, DT, kCausal>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt], step, lim[rt],
                                           grp, a.scale_log2e);
+        // V entries past the last key are zeroed on the last step only
+        auto pv = [&](auto masked) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            h4 v[NT];
+            for (int dt = 0; dt < DT; ++dt) {
+                h4 v[NT];
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-                v[tt] = mask_v(
-                    *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
-                                                 (tt * 4 + grp) * Img<D>::kGroupV + (16 * dt + col) * 8),
-                    step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+                for (int tt = 0; tt < NT; ++tt) {
+                    v[tt] = *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
+                                                         (tt * 4 + grp) * Img<D>::kGroupV +
+                                                         (16 * dt + col) * 8);
+                    if constexpr (decltype(masked)::value)
+                        v[tt] = mask_v(v[tt], step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+                }
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) o[rt][dt] = pv_tile<NT>(o[rt][dt], v, pq[rt]);
-        }
+                for (int rt = 0; rt < RT; ++rt) o[rt][dt] = pv_tile<NT>(o[rt][dt], v, pq[rt]);
+            }
+        };
+        if ((step + 1) * Step<D>::kKeys > n_keys)
+            pv(Flag<true>{});
+        else
+            pv(Flag<false>{});
     };
 
     if constexpr (kDirect) {
