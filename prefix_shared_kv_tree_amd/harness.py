@@ -202,17 +202,21 @@ class HostDecoder:
         self.count[key] += 1
 
     def joins(self, t: int):
-        """Apply step t's departures/arrivals.  Returns [(join, prompt slots)]."""
+        """Apply step t's departures/arrivals.  Returns [(join, prompt slots,
+        (move src, move dst))]: under token matching an arrival may split a
+        node, whose moved tokens' K/V the caller relocates before it writes
+        the new tokens."""
         import time
         out = []
         for j in self.tr.joins_at(t):
             t0 = time.perf_counter_ns()
             B.pkvt_tree_remove(self.tree, int(self.rows[j.row]))
             ids, slots = B.pkvt_tree_build(self.tree, [self.tr.prompt_tokens(j)])
+            moves = B.pkvt_tree_moves(self.tree)
             self.rows[j.row] = ids[0]
             self._time("join", t0)
             self.structural = True
-            out.append((j, slots))
+            out.append((j, slots, moves))
         return out
 
     def append(self, t: int) -> np.ndarray:
@@ -269,8 +273,8 @@ class DecodeLoop:
                 [torch.from_numpy(np.ascontiguousarray(j.suffix.k[l])).to(dev) for l in range(ds.layers)],
                 [torch.from_numpy(np.ascontiguousarray(j.suffix.v[l])).to(dev) for l in range(ds.layers)])
         self.out = torch.empty((ds.layers, w.b, w.h, w.d), dtype=torch.float16, device=dev)
-        cap = max([w.b] + [len(j.suffix) + sum(len(w.segments[s]) for s in j.shared)
-                           for j in trace.joins])
+        cap = max([w.b, w.c] + [len(j.suffix) + sum(len(w.segments[s]) for s in j.shared)
+                                for j in trace.joins])
         self.ring = [(torch.empty(cap, dtype=torch.int64).pin_memory(),
                       torch.empty(cap, dtype=torch.int64, device=dev),
                       torch.cuda.Event()) for _ in range(ring)]
@@ -338,7 +342,12 @@ class DecodeLoop:
         t_enter = time.perf_counter_ns()
         torch, ds = self.torch, self.ds
         stream = torch.cuda.current_stream().cuda_stream
-        for j, slots in self.host.joins(t):
+        for j, slots, (src, dst) in self.host.joins(t):
+            if src.size:
+                d_src, d_dst = self._to_device(src), self._to_device(dst)
+                for l in range(ds.layers):
+                    B.pkvt_kv_move(ds.tree, ds.k_pools[l].data_ptr(), ds.v_pools[l].data_ptr(),
+                                   d_src.data_ptr(), d_dst.data_ptr(), src.size, stream)
             self._join_kv(j, slots, stream)
         slots = self.host.append(t)
         b = self.tr.base.b
@@ -380,14 +389,15 @@ class DecodeLoop:
 def loop_pool_chunks(trace) -> int:
     """A pool size that a decode trace cannot exhaust: every base sequence's
     chunks as if nothing were shared, plus, for every row and every join,
-    the chunks its appends and prompt could open."""
+    the chunks its appends and prompt could open (and one for the node it
+    may split under token matching)."""
     w = trace.base
     c = w.c
     grow = trace.steps // c + 2
     n = sum(-(-w.seq_len(u) // c) for u in range(w.b)) + w.b * grow
     for j in trace.joins:
         n_pre = sum(len(w.segments[s]) for s in j.shared)
-        n += -(-(n_pre + len(j.suffix)) // c) + grow
+        n += -(-(n_pre + len(j.suffix)) // c) + grow + 1
     return n
 
 

@@ -398,7 +398,7 @@ class DecodeTrace:
 
 
 def decode_trace(w: Workload, steps: int, seed: int, churn_every: int = 0,
-                 suffix=None) -> DecodeTrace:
+                 suffix=None, unique_starts: bool = False) -> DecodeTrace:
     """Draw a decode trace of ``steps`` iterations over the batch of ``w``.
 
     Every ``churn_every`` steps (0 = never) one row, drawn uniformly, gets a
@@ -406,7 +406,11 @@ def decode_trace(w: Workload, steps: int, seed: int, churn_every: int = 0,
     (inclusive; default [c/2, 4c]).  Draw order, from one PCG64 generator
     seeded with ``seed``: tokens [T, b]; per join (in step order) its row,
     suffix length and suffix tokens; Q [T, b, h, d]; then for each layer:
-    K [T, b, h, d], V [T, b, h, d], and every join's suffix K then V."""
+    K [T, b, h, d], V [T, b, h, d], and every join's suffix K then V.
+    ``unique_starts``: every join's suffix starts with a token id no segment
+    or other join starts with (ids from VOCAB + 2^20 on; use with a base
+    workload from ``unique_segment_starts``), so that a join shares exactly
+    its shared segments however finely the tree matches tokens."""
     if steps < 1:
         raise ValueError("steps must be >= 1")
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -419,6 +423,8 @@ def decode_trace(w: Workload, steps: int, seed: int, churn_every: int = 0,
             row = int(rng.integers(0, b))
             n = int(rng.integers(lo, hi + 1))
             toks = rng.integers(0, VOCAB, size=n, dtype=np.int64).astype(np.int32)
+            if unique_starts:
+                toks[0] = VOCAB + (1 << 20) + len(joins)
             joins.append(Join(step=t, row=row, shared=list(w.seq_paths[row][:-1]),
                               suffix=Segment(tokens=toks, k=[], v=[])))
     q = _normal_f16(rng, (steps, b, h, d))

@@ -84,7 +84,7 @@ def test_host_decoder_follows_trace(name, steps, churn, check_every):
         structural_steps = 0
         for step in range(steps):
             joined = hd.joins(step)
-            for j, slots in joined:
+            for j, slots, _ in joined:
                 # the kept shared prefix is already stored: only the tail of a
                 # partially filled chunk and the suffix need writing
                 n_pre = sum(len(w.segments[s]) for s in j.shared)
@@ -113,5 +113,73 @@ def test_host_decoder_follows_trace(name, steps, churn, check_every):
             B.pkvt_tree_remove(t, int(s))
         st = B.pkvt_tree_stats(t)
         assert st["used_chunks"] == 0 and st["free_chunks"] == st["capacity"]
+    finally:
+        B.pkvt_tree_destroy(t)
+
+
+@pytest.mark.parametrize("seed,c", [(5, 16), (6, 32), (7, 4)])
+def test_host_decoder_token_matching(seed, c):
+    """HostDecoder on a token-granular tree: a shared prompt that ends inside
+    a chunk, joins whose prompts split nodes of live sequences.  Replays the
+    slots and each join's K/V moves on an emulated pool (slot -> the token's
+    whole prefix, which is what its K/V depend on) and checks every live
+    sequence's path against it, plus the plan invariants with partial
+    chunks."""
+    rng = np.random.default_rng(seed)
+    b = 10
+    prefix = 3 * c + int(rng.integers(1, c))
+    w = W.unique_segment_starts(W.one_prefix(seed, b, prefix, [int(x) for x in rng.integers(1, 3 * c, b)],
+                                             h=1, d=64, c=c, with_kv=False))
+    tr = W.decode_trace(w, 3 * c + 7, seed=seed, churn_every=4, suffix=(1, 2 * c), unique_starts=True)
+    t = B.pkvt_tree_create(w.h, w.d, w.c, loop_pool_chunks(tr), match="tokens")
+    try:
+        # the batch arrives one prompt per call: the second splits the first's
+        # node at the prompt's end, whose tail K/V moves
+        prompts = [list(int(x) for x in p) for p in w.all_seq_tokens()]
+        pool = {}
+        moved = 0
+        ids = []
+        for p in prompts:
+            i, sl = B.pkvt_tree_build(t, [p])
+            src, dst = B.pkvt_tree_moves(t)
+            pool.update({int(d): pool[int(s)] for s, d in zip(src, dst)})
+            moved += src.size
+            for k in range(len(p)):
+                if sl[k] >= 0:
+                    pool[int(sl[k])] = tuple(p[:k + 1])
+            ids.append(int(i[0]))
+        assert moved > 0
+        seqs = {i: list(p) for i, p in zip(ids, prompts)}
+        hd = HostDecoder(t, tr, np.array(ids, np.int32))
+        hd.plan()
+        for step in range(tr.steps):
+            old_rows = [int(x) for x in hd.rows]
+            for j, sl, (src, dst) in hd.joins(step):
+                assert not set(src.tolist()) & set(dst.tolist())
+                pool.update({int(d): pool[int(s)] for s, d in zip(src, dst)})
+                moved += src.size
+                p = [int(x) for x in tr.prompt_tokens(j)]
+                for k in range(len(p)):
+                    if sl[k] >= 0:
+                        pool[int(sl[k])] = tuple(p[:k + 1])
+                del seqs[old_rows[j.row]]
+                seqs[int(hd.rows[j.row])] = p
+            sl = hd.append(step)
+            for r, s in enumerate(hd.rows):
+                seqs[int(s)].append(int(tr.tokens[step, r]))
+                pool[int(sl[r])] = tuple(seqs[int(s)])
+            hd.plan()
+            for s, toks in seqs.items():
+                pos = 0
+                for x in B.pkvt_tree_chunk_path(t, s):
+                    for k in range(B.pkvt_tree_chunk_fill(t, int(x))):
+                        assert pool[int(x) * c + k] == tuple(toks[:pos + 1]), (step, s, pos)
+                        pos += 1
+                assert pos == len(toks)
+            plan = PV.parse(B.pkvt_plan_blob(t))
+            paths = {int(s): [int(x) for x in B.pkvt_tree_chunk_path(t, int(s))] for s in hd.rows}
+            fills = {x: B.pkvt_tree_chunk_fill(t, x) for p in paths.values() for x in p}
+            PV.check_plan(plan, hd.rows, paths, {int(s): len(seqs[int(s)]) for s in hd.rows}, c,
+                          heads=w.h, fills=fills)
     finally:
         B.pkvt_tree_destroy(t)

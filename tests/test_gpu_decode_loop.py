@@ -88,6 +88,35 @@ def test_decode_loop_unaligned_prefix(seed, d, c):
     ds.close()
 
 
+@pytest.mark.parametrize("seed,d,c", [(41, 128, 32), (42, 64, 16), (43, 256, 64)])
+def test_decode_loop_token_matching(seed, d, c):
+    """The loop over a token-granular tree: a shared prompt that ends inside
+    a chunk is stored once (the batch arrives one prompt per build call: the second
+    calls split earlier nodes and their K/V move), decode appends fill the
+    split leaves, joins every 5 steps; every step against the oracle."""
+    _torch()
+    from prefix_shared_kv_tree_amd import binding as B
+    from prefix_shared_kv_tree_amd.harness import DecodeLoop, DecodeSetup, loop_pool_chunks
+    B.load()
+    rng = np.random.default_rng(seed)
+    b = 12
+    prefix = 2 * c + int(rng.integers(1, c))
+    suffix = [int(x) for x in rng.integers(1, 2 * c, size=b)]
+    print(f"\n[case] decode loop token matching seed={seed} d={d} c={c} prefix={prefix}", flush=True)
+    w = W.unique_segment_starts(W.one_prefix(seed, b, prefix, suffix, h=2, d=d, c=c))
+    tr = W.decode_trace(w, c + 9, seed=seed, churn_every=5, suffix=(1, 2 * c), unique_starts=True)
+    ds = DecodeSetup(w, layers=1, pool_chunks=loop_pool_chunks(tr) + b, match="tokens",
+                     build_groups=b)
+    assert ds.moves > 0
+    loop = DecodeLoop(ds, tr)
+    worst = 0.0
+    for t in range(tr.steps):
+        loop.step(t)
+        worst = max(worst, _check(loop, tr, t, 1))
+    print(f"[case]   moves {ds.moves} worst err {worst:.3e} host counts {loop.host.count}", flush=True)
+    ds.close()
+
+
 def test_decode_loop_long_prefix_sampled():
     """The 4096-token shared prefix batch of 64 (head_dim 128, chunk 64,
     32 heads), 40 steps with a join every 8: sampled rows, including the

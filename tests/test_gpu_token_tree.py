@@ -82,14 +82,16 @@ def test_random_token_trees(seed):
 def test_unaligned_shared_prompt(d):
     """40 sequences share a 1000-token prompt (chunk 64: 15 full chunks and a
     shared 40-token chunk, read by workgroup units whose keys end inside it),
-    then private suffixes of 1..300 tokens; built in two calls, so the second
-    call's prompts split the first call's leaves."""
+    then private suffixes of 1..300 tokens; one prompt per build call, so the
+    second call splits the first sequence's node at the end of the prompt
+    and its tail K/V moves."""
     _torch()
     rng = np.random.default_rng(d)
     suffix = [int(x) for x in rng.integers(1, 301, size=40)]
     w = W.unique_segment_starts(W.one_prefix(600 + d, 40, 1000, suffix, h=2, d=d, c=64))
     ref = A.attention_batch(w)
-    ds = _setup(w, match="tokens", build_groups=2)
+    ds = _setup(w, match="tokens", build_groups=40)
+    assert ds.moves == 64 - 1000 % 64
     err = _err(_run(ds), ref)
     print(f"\n[case] unaligned prompt d={d} moves={ds.moves} info={ds.info} err={err:.3e}", flush=True)
     assert err <= TOL
