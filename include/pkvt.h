@@ -105,10 +105,9 @@ void        pkvt_tree_destroy(pkvt_tree* tree);
  *                        pkvt_tree_moves / pkvt_kv_move.  A decode append
  *                        writes into the leaf only while that leaf is partial,
  *                        private and childless, else it opens a new leaf.
- *                        Nodes are never merged.  The decode planner and
- *                        kernels accept such trees; pkvt_prefill_plan rejects
- *                        a batch whose paths hold a partial chunk before
- *                        their leaf (INVALID_ARG).
+ *                        Nodes are never merged.  The planners and kernels
+ *                        (decode and prefill) accept such trees: a work item
+ *                        ends at every partial chunk.
  * INVALID_ARG also for any other match value. */
 #define PKVT_MATCH_CHUNKS 0
 #define PKVT_MATCH_TOKENS 1

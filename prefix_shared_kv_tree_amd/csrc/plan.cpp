@@ -771,14 +771,6 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
                       " must lie in [0, length)";
                 return PKVT_ERR_INVALID_ARG;
             }
-            // positions map to chunks as pos / C: every chunk before the leaf full
-            for (size_t k = 0; k + 1 < sq->path.size(); ++k)
-                if (t.node(sq->path[k]).fill != C) {
-                    err = "prefill_plan: sequence " + std::to_string(seq_ids[s]) +
-                          " holds a partial chunk before its leaf (token-granular sharing); "
-                          "prefill plans need whole chunks up to the leaf";
-                    return PKVT_ERR_INVALID_ARG;
-                }
             seqs[s] = sq;
             nrows[s] = sq->len - q_from[s];
             R += nrows[s];
@@ -838,10 +830,22 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
         else
             blks.push_back({i, i});
     }
-    // chunks: every batch sequence's path, once
+    // chunks: every batch sequence's path, once; pstart[p][k] = sequence
+    // position of the first token of chunk k (chunks may be partial anywhere
+    // under token-granular matching)
     std::vector<int32_t> path_off(n + 1, 0);
-    for (int32_t p = 0; p < n; ++p)
-        path_off[p + 1] = path_off[p] + static_cast<int32_t>(seqs[dfs_seq[p]]->path.size());
+    std::vector<std::vector<int64_t>> pstart(n);
+    for (int32_t p = 0; p < n; ++p) {
+        const std::vector<int32_t>& path = seqs[dfs_seq[p]]->path;
+        path_off[p + 1] = path_off[p] + static_cast<int32_t>(path.size());
+        pstart[p].assign(path.size() + 1, 0);
+        for (size_t k = 0; k < path.size(); ++k) pstart[p][k + 1] = pstart[p][k] + t.node(path[k]).fill;
+    }
+    // chunks of sequence p holding a position <= pos
+    auto chunks_upto = [&](int32_t p, int64_t pos) {
+        const std::vector<int64_t>& ps = pstart[p];
+        return static_cast<int32_t>(std::upper_bound(ps.begin(), ps.end() - 1, pos) - ps.begin());
+    };
 
     struct PUnit { int32_t keys, chunk_off, n_chunks, row_lo, n_rows, out, key_base; int64_t cost; };
     std::vector<PUnit> blocks;                      // work units (x heads below)
@@ -856,7 +860,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
         if (pa == pb_) {
             int32_t max_pos = 0;
             for (int64_t r = r0; r < r1; ++r) max_pos = std::max(max_pos, qpos[r]);
-            pend.push_back({r0, r1, pa, 0, (max_pos + C) / C, max_pos});
+            pend.push_back({r0, r1, pa, 0, chunks_upto(pa, max_pos), max_pos});
             continue;
         }
         int32_t lcp = 0;                            // chunks common to every sequence of the block
@@ -866,51 +870,60 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
         if (lcp > 0) {
             int32_t max_pos = 0;
             for (int64_t r = r0; r < r1; ++r) max_pos = std::max(max_pos, qpos[r]);
-            const int32_t k1 = std::min(lcp, (max_pos + C) / C);
+            const int32_t k1 = std::min(lcp, chunks_upto(pa, max_pos));
             pend.push_back({r0, r1, pa, 0, k1, max_pos});
         }
         for (size_t i = bk.first; i <= bk.last; ++i) {
             const Piece& pc = pieces[i];
             int32_t max_pos = 0;
             for (int64_t r = pc.r0; r < pc.r1; ++r) max_pos = std::max(max_pos, qpos[r]);
-            const int32_t k1 = (max_pos + C) / C;
+            const int32_t k1 = chunks_upto(pc.p, max_pos);
             if (k1 <= lcp) continue;                // every key it sees is common
             // rows before the first private key see nothing of it
             int64_t q0 = pc.r0;
-            while (q0 < pc.r1 && qpos[q0] < static_cast<int64_t>(lcp) * C) ++q0;
+            while (q0 < pc.r1 && qpos[q0] < pstart[pc.p][lcp]) ++q0;
             pend.push_back({q0, pc.r1, pc.p, lcp, k1, max_pos});
         }
     }
-    // cut into units of at most S chunks; count units per row
+    // cut into units of at most S chunks, each holding full chunks but its
+    // last (a unit addresses key k at chunk k / C); count units per row
     struct Cut { int64_t r0, r1; int32_t p, k0, k1; };
     std::vector<Cut> cuts_v;
     for (const Pending& pd : pend) {
-        const int32_t m = pd.k1 - pd.k0;
-        const int32_t k_items = (m + S - 1) / S;
-        int32_t a2 = pd.k0;
-        for (int32_t q = 0; q < k_items; ++q) {
-            const int32_t e = a2 + m / k_items + (q < m % k_items ? 1 : 0);
-            // runs of rows that see at least the first key of this cut (a
-            // block of several sequences has no order of positions)
-            int64_t q0 = pd.r0;
-            while (q0 < pd.r1) {
-                while (q0 < pd.r1 && qpos[q0] < static_cast<int64_t>(a2) * C) ++q0;
-                int64_t q1 = q0;
-                while (q1 < pd.r1 && qpos[q1] >= static_cast<int64_t>(a2) * C) ++q1;
-                if (q1 > q0) {
-                    cuts_v.push_back({q0, q1, pd.p, a2, e});
-                    for (int64_t r = q0; r < q1; ++r) n_units_of[r]++;
+        const std::vector<int32_t>& path = seqs[dfs_seq[pd.p]]->path;
+        for (int32_t g0 = pd.k0; g0 < pd.k1;) {
+            int32_t g1 = g0;
+            while (g1 < pd.k1 - 1 && t.node(path[g1]).fill == C) ++g1;
+            ++g1;                                   // [g0, g1): full chunks, then any
+            const int32_t m = g1 - g0;
+            const int32_t k_items = (m + S - 1) / S;
+            int32_t a2 = g0;
+            for (int32_t q = 0; q < k_items; ++q) {
+                const int32_t e = a2 + m / k_items + (q < m % k_items ? 1 : 0);
+                // runs of rows that see at least the first key of this cut (a
+                // block of several sequences has no order of positions)
+                const int64_t first = pstart[pd.p][a2];
+                int64_t q0 = pd.r0;
+                while (q0 < pd.r1) {
+                    while (q0 < pd.r1 && qpos[q0] < first) ++q0;
+                    int64_t q1 = q0;
+                    while (q1 < pd.r1 && qpos[q1] >= first) ++q1;
+                    if (q1 > q0) {
+                        cuts_v.push_back({q0, q1, pd.p, a2, e});
+                        for (int64_t r = q0; r < q1; ++r) n_units_of[r]++;
+                    }
+                    q0 = q1;
                 }
-                q0 = q1;
+                a2 = e;
             }
-            a2 = e;
+            g0 = g1;
         }
     }
     std::vector<std::vector<int32_t>> mslots(R);
     int32_t n_slots = 0;
     for (const Cut& ct : cuts_v) {
         const Seq* sq = seqs[dfs_seq[ct.p]];
-        const int64_t kb = static_cast<int64_t>(ct.k0) * C;
+        const int64_t kb = pstart[ct.p][ct.k0];
         int64_t n_keys = 0;
         for (int32_t k = ct.k0; k < ct.k1; ++k) n_keys += t.node(sq->path[k]).fill;
         int32_t max_pos = 0;

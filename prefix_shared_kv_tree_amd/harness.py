@@ -410,7 +410,7 @@ class PrefillSetup:
 
     def __init__(self, pb, layers: Optional[int] = None, device: str = "cuda",
                  phase1_chunks: int = 0, device_random_seed: Optional[int] = None,
-                 pool_slack: int = 0):
+                 pool_slack: int = 0, match: str = "chunks"):
         import torch
         self.torch = torch
         self.pb = pb
@@ -421,13 +421,16 @@ class PrefillSetup:
         c = w.c
         pool_chunks = (sum(-(-len(w.segments[s]) // c) for s in pb.residents) +
                        sum(-(-w.seq_len(u) // c) for u in pb.seqs) + pool_slack)
-        self.tree = B.pkvt_tree_create(w.h, w.d, c, pool_chunks)
+        if match == "tokens":
+            pool_chunks += len(pb.seqs)                  # a split per arrival at most
+        self.tree = B.pkvt_tree_create(w.h, w.d, c, pool_chunks, match=match)
         stream = torch.cuda.current_stream().cuda_stream
         res_slots = np.zeros(0, np.int64)
         if pb.residents:
             self.resident_ids, res_slots = B.pkvt_tree_build(
                 self.tree, [w.segments[s].tokens for s in pb.residents])
         self.seq_ids, slots = B.pkvt_tree_build(self.tree, [w.seq_tokens(u) for u in pb.seqs])
+        move_src, move_dst = B.pkvt_tree_moves(self.tree)      # token matching: split tails
         pos = 0
         for u, a in zip(pb.seqs, pb.q_from):
             L = w.seq_len(u)
@@ -456,8 +459,18 @@ class PrefillSetup:
                     at += len(seg)
                     need = np.nonzero(rs >= 0)[0]
                     writes.append((seg.k[layer][need], seg.v[layer][need], rs[need]))
+                writes.append(None)                  # the batch's moves of stored tokens
                 writes.append(gather_new_tokens(w, slots, layer))
-                for k_new, v_new, s_new in writes:
+                for item in writes:
+                    if item is None:
+                        if move_src.size:
+                            ms = torch.from_numpy(move_src).to(device)
+                            md = torch.from_numpy(move_dst).to(device)
+                            B.pkvt_kv_move(self.tree, kp.data_ptr(), vp.data_ptr(), ms.data_ptr(),
+                                           md.data_ptr(), move_src.size, stream)
+                            torch.cuda.synchronize()
+                        continue
+                    k_new, v_new, s_new = item
                     if s_new.size == 0:
                         continue
                     kd = torch.from_numpy(np.ascontiguousarray(k_new)).to(device)

@@ -461,18 +461,23 @@ class PrefillBatch:
 
 
 def prefill_batch(seed: int, b: int, prefix: int, new, h: int = 2, d: int = 64, c: int = 16,
-                  layers: int = 1, with_kv: bool = True) -> PrefillBatch:
+                  layers: int = 1, with_kv: bool = True, match: str = "chunks") -> PrefillBatch:
     """b sequences = one shared prefix of ``prefix`` tokens + ``new`` tokens
     each (a count or b counts).  The prefix is stored beforehand; its full
     chunks are matched, so every sequence's new rows start at the prefix
     length rounded down to a whole chunk (a partial last prefix chunk is
     written again by each sequence, as whole-chunk matching dictates).
+    With ``match="tokens"`` (a token-granular tree) the whole prefix is
+    matched, the new rows start at the prefix length, and the workload goes
+    through ``unique_segment_starts``.
     Draw order (PCG64(seed)): the workload as ``one_prefix`` draws it
     (tokens, a decode Q that is not used, K/V), then the prefill Q [R, h, d]."""
     newl = [int(new)] * b if np.isscalar(new) else [int(x) for x in new]
     w = one_prefix(seed, b, prefix, newl, h=h, d=d, c=c, layers=layers, with_kv=with_kv)
+    if match == "tokens":
+        w = unique_segment_starts(w)
     rng = np.random.Generator(np.random.PCG64(seed + 7919))
-    a = (prefix // c) * c
+    a = prefix if match == "tokens" else (prefix // c) * c
     q_from = [a] * b
     R = sum(w.seq_len(u) - a for u in range(b))
     q = _normal_f16(rng, (R, h, d))

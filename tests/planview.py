@@ -176,10 +176,17 @@ def check_plan(plan: dict, q_order, paths: dict, lens: dict, c: int, min_share: 
 
 
 def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: int, heads: int,
-                       d: int = 64):
+                       d: int = 64, fills: dict = None):
     """Every prefill row (sequence s, position p) reads exactly the keys
     0 .. p of s, each once, from the chunks on s's path, in units of at most
-    64 rows whose first key it can see; its partial slots are its merge list."""
+    64 rows whose first key it can see; its partial slots are its merge list.
+    fills: chunk id -> tokens stored (default: every chunk before a leaf
+    full); a unit holds full chunks but its last."""
+    if fills is None:
+        fills = {}
+        for sid, path in paths.items():
+            for k, x in enumerate(path):
+                fills[int(x)] = c if k + 1 < len(path) else lens[sid] - c * (len(path) - 1)
     R = plan["b"]
     rows_meta = []
     for s, a in zip(seq_ids, q_from):
@@ -198,13 +205,18 @@ def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: 
     for u, ch in zip(plan["units"], plan["unit_chunks"]):
         n_keys, chunk_off, n_chunks, head, row_lo, n_rows, out, key_base = [int(v) for v in u]
         assert 1 <= n_rows <= (128 if d <= 128 else 64) and 1 <= n_chunks <= 128 and 0 <= head < heads
-        assert (n_keys + c - 1) // c == n_chunks and key_base % c == 0
+        assert (n_keys + c - 1) // c == n_chunks
+        assert all(fills[int(x)] == c for x in ch[:-1]) and n_keys <= sum(fills[int(x)] for x in ch)
         for i in range(n_rows):
             r = row_lo + i
             s, p = rows_meta[caller[r]]
             assert p >= key_base, "a row that sees none of the unit's keys"
             path = [int(x) for x in paths[s]]
-            k0 = key_base // c
+            starts = [0]
+            for x in path:
+                starts.append(starts[-1] + fills[x])
+            assert key_base in starts[:-1], "a unit that starts inside a chunk"
+            k0 = starts.index(key_base)
             assert [int(x) for x in ch] == path[k0:k0 + n_chunks], "unit chunks are not on the row's path"
             for pos in range(key_base, min(key_base + n_keys, p + 1)):
                 seen[(r, head)][pos] += 1

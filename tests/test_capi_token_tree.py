@@ -291,15 +291,19 @@ def test_plan_invariants_with_partial_nodes(seed):
     for _ in range(int(rng.integers(0, 30))):                # decode appends grow some leaves
         who = [int(x) for x in rng.choice(ids, size=3)]
         B.pkvt_tree_append(box.t, who, [int(x) for x in rng.integers(0, 3, size=3)])
-    partial_inside = any(B.pkvt_tree_chunk_fill(box.t, int(x)) < c
-                         for i in ids for x in B.pkvt_tree_chunk_path(box.t, i)[:-1])
     for kw in [dict(), dict(phase1_chunks=1, phase2_chunks=1), dict(phase2_chunks=2, unit_rows=17),
                dict(min_share=3), dict(workgroups=3)]:
         order = [int(x) for x in rng.permutation(ids)]
         _plan_and_check(box, order, h, **kw)
-    if partial_inside:
-        with pytest.raises(B.PkvtError):
-            B.pkvt_prefill_plan(box.t, ids, [0] * len(ids))
+    # prefill of every sequence's last few positions (and of whole sequences)
+    from tests import planview
+    paths = {i: [int(x) for x in B.pkvt_tree_chunk_path(box.t, i)] for i in ids}
+    lens = {i: B.pkvt_tree_seq_len(box.t, i) for i in ids}
+    fills = {x: B.pkvt_tree_chunk_fill(box.t, x) for p in paths.values() for x in p}
+    for q_from in ([0] * len(ids), [max(0, lens[i] - int(rng.integers(1, 9))) for i in ids]):
+        B.pkvt_prefill_plan(box.t, ids, q_from)
+        plan = planview.parse(B.pkvt_prefill_blob(box.t))
+        planview.check_prefill_plan(plan, ids, q_from, paths, lens, c, h, fills=fills)
 
 
 def test_plan_wide_shared_partial_prefix():
@@ -315,3 +319,15 @@ def test_plan_wide_shared_partial_prefix():
     plan = _plan_and_check(box, ids, 2)
     assert len(plan["units"]) > 0
     assert sorted({int(u[0]) for u in plan["units"]}) == [70]
+    # prefill of the private tokens: rows read the shared 70 tokens (a unit
+    # ending inside chunk 4) and then their own chunks, whose keys start at 70
+    from tests import planview
+    q_from = [71] * len(ids)
+    B.pkvt_prefill_plan(box.t, ids, q_from)
+    pplan = planview.parse(B.pkvt_prefill_blob(box.t))
+    paths = {i: [int(x) for x in B.pkvt_tree_chunk_path(box.t, i)] for i in ids}
+    lens = {i: B.pkvt_tree_seq_len(box.t, i) for i in ids}
+    fills = {x: B.pkvt_tree_chunk_fill(box.t, x) for p in paths.values() for x in p}
+    assert sorted(fills[p[4]] for p in paths.values())[0] == 6
+    planview.check_prefill_plan(pplan, ids, q_from, paths, lens, 16, 2, fills=fills)
+    assert 70 in {int(u[7]) for u in pplan["units"]}

@@ -54,6 +54,28 @@ def test_prefill_batch_all_rows(b, prefix, new, d, c):
         ps.close()
 
 
+@pytest.mark.parametrize("b,prefix,new,d,c", [
+    (12, 1000, [int(x) for x in np.random.default_rng(1).integers(1, 200, 12)], 128, 64),
+    (7, 40, [3, 90, 17, 1, 64, 33, 5], 64, 16), (5, 130, [70, 1, 129, 3, 40], 256, 64)])
+def test_prefill_token_matching(b, prefix, new, d, c):
+    """Prefill over a token-granular tree: the stored prefix ends inside a
+    chunk and is matched whole, so the new rows start at the prefix length,
+    read the shared partial chunk through a unit that ends inside it, and
+    their own chunks from a key base that is not a multiple of the chunk
+    size."""
+    _torch()
+    print(f"\n[case] token prefill b={b} prefix={prefix} d={d} c={c}", flush=True)
+    pb = W.prefill_batch(57 + b, b, prefix, new, h=2, d=d, c=c, match="tokens")
+    assert pb.q_from == [prefix] * b
+    ref = A.prefill_attention(pb.w, pb.seqs, pb.q_from, pb.q)
+    for ch in (0, 1):
+        ps = _setup(pb, phase1_chunks=ch, match="tokens")
+        err = float(np.abs(_run(ps) - ref).max())
+        print(f"[case]   phase1_chunks={ch} err={err:.3e} info={ps.info}", flush=True)
+        assert err <= TOL
+        ps.close()
+
+
 def test_prefill_first_row_is_value_row_bit_exact():
     """A sequence prefilled from position 0: its first row sees one key, so
     its output is that key's V row exactly."""
