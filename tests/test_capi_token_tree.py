@@ -331,3 +331,38 @@ def test_plan_wide_shared_partial_prefix():
     assert sorted(fills[p[4]] for p in paths.values())[0] == 6
     planview.check_prefill_plan(pplan, ids, q_from, paths, lens, 16, 2, fills=fills)
     assert 70 in {int(u[7]) for u in pplan["units"]}
+
+
+def test_new_entry_points_reject_bad_arguments(lib):
+    import ctypes as C
+    t = B.pkvt_tree_create(2, 64, 4, 8, match="tokens")
+    try:
+        n = C.c_int64()
+        assert lib.pkvt_tree_moves(t, None, None, 0, None) == -1          # NULL count
+        assert lib.pkvt_tree_moves(None, None, None, 0, C.byref(n)) == -1
+        f = C.c_int32()
+        assert lib.pkvt_tree_chunk_fill(t, 8, C.byref(f)) == -1           # chunk id out of range
+        assert lib.pkvt_tree_chunk_fill(t, 0, None) == -1
+        B.pkvt_tree_build(t, [[1, 2, 3, 4, 5]])
+        B.pkvt_tree_build(t, [[1, 2, 9]])                                 # splits [1 2 3 4]
+        assert lib.pkvt_tree_moves(t, None, None, 0, C.byref(n)) == -6    # BUFFER_TOO_SMALL
+        assert n.value == 2
+        src = (C.c_int64 * 2)()
+        assert lib.pkvt_tree_moves(t, src, None, 2, C.byref(n)) == -1     # NULL dst
+    finally:
+        B.pkvt_tree_destroy(t)
+    # kv_move: argument checks happen before any device work
+    t = B.pkvt_tree_create(2, 64, 16, 8, match="tokens")
+    try:
+        assert lib.pkvt_kv_move(t, None, None, None, None, -1, None) == -1
+        assert lib.pkvt_kv_move(t, None, None, None, None, 0, None) == 0
+        assert lib.pkvt_kv_move(t, None, None, None, None, 3, None) == -1
+    finally:
+        B.pkvt_tree_destroy(t)
+    odd = B.pkvt_tree_create(2, 32, 4, 8)                                 # head_dim 32: no kernels
+    try:
+        assert lib.pkvt_kv_move(odd, None, None, None, None, 1, None) == -5
+    finally:
+        B.pkvt_tree_destroy(odd)
+    out = C.c_void_p()
+    assert lib.pkvt_tree_create_ex(2, 64, 4, 8, 7, C.byref(out)) == -1 and not out.value
