@@ -388,7 +388,10 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     // ---- item size ----------------------------------------------------------------
     // T = the mean per-wave load in 64-key steps with nothing cut (a unit
     // step counted at its cost relative to a single-wave step).  Phase-1
-    // items are cut at T.  Phase-2 items are cut at T when nothing is shared
+    // items read by single-wave tasks are cut at T, those read by workgroup
+    // units at 5T / kUnitStepCost steps, which a unit takes 5/4 of T to run
+    // (fewer, longer units: fewer partials to write and merge; measured on
+    // the 1K-, 4K-prefix and two-level-tree batches).  Phase-2 items are cut at T when nothing is shared
     // (all tasks then tend to be alike and need no merge); with a shared
     // prefix the phase-1 units make the per-wave loads uneven and finer
     // phase-2 pieces (T/4, but at least 4 steps) fill the gaps better.  The
@@ -396,6 +399,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     // 2-step pieces spends more on the extra partials and their merge than
     // the finer balance wins back.
     int32_t s1 = opts.phase1_chunks, s2 = opts.phase2_chunks;
+    int32_t s1_unit = s1;                 // phase-1 items whose rows form workgroup units
     if (s1 == 0 || s2 == 0) {
         int64_t quarters = 0;
         for (size_t s = 0; s < segs.size(); ++s) {
@@ -411,7 +415,13 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         for (int32_t p = 0; p < b; ++p)
             quarters += 4 * steps_of(seqs[dfs_row[p]]->len - pos0[p]);
         const int64_t mean = std::max<int64_t>(1, (quarters * t.H + 4 * lanes - 1) / (4 * lanes));
-        if (s1 == 0) s1 = steps_to_chunks(mean, t.C);
+        if (s1 == 0) {
+            s1 = steps_to_chunks(mean, t.C);
+            // a unit step takes a wave kUnitStepCost / 4 of a task step: units
+            // of up to 5/4 T * 4 / kUnitStepCost steps last at most 5/4 of a
+            // mean wave load
+            s1_unit = steps_to_chunks(mean * 5 / kUnitStepCost, t.C);
+        }
         if (s2 == 0) {
             const int64_t fine = std::max<int64_t>(4, (mean + 3) / 4);
             s2 = steps_to_chunks(segs.empty() ? mean : fine, t.C);
@@ -441,8 +451,9 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         int32_t limit = s1;
         if (opts.phase1_chunks == 0) {
             const int64_t rows = seg_range[s].j - seg_range[s].i;
+            if (rows >= opts.unit_rows) limit = s1_unit;
             const int64_t need = (8 * rows * (t.D + 2) * 4 + 4LL * t.C * t.D - 1) / (4LL * t.C * t.D);
-            limit = static_cast<int32_t>(std::min<int64_t>(kMaxItemChunks, std::max<int64_t>(s1, need)));
+            limit = static_cast<int32_t>(std::min<int64_t>(kMaxItemChunks, std::max<int64_t>(limit, need)));
         }
         const std::vector<int32_t> at = cuts(static_cast<int32_t>(segs[s].size()), limit);
         for (size_t q = 0; q + 1 < at.size(); ++q) {
