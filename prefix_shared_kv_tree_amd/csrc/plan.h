@@ -31,12 +31,13 @@
 namespace pkvt {
 
 // One 64-lane unit of work of the attention kernel: up to 16 query rows
-// against a list of chunks of one head (the head comes from the grid).
+// against a list of chunks of one head (the head comes from the task list).
+// Every chunk but the last is full; key k lies in chunk k / C.
 struct WaveDesc {
     int32_t chunk_off;   // first entry in the chunks section
     int32_t n_chunks;
     int32_t key_base;    // index, within its sequence, of the first key (len_row >= 0)
-    int32_t len_row;     // depth-first row whose length bounds the keys, -1 = all full
+    int32_t len_row;     // depth-first row whose length bounds the keys, -1 = tail bounds them
     int32_t row_lo;      // depth-first position of query row 0
     int32_t n_rows;      // 1..16
     int32_t out;         // partial slot of row 0, or -1: write O directly (n_rows == 1)
@@ -44,12 +45,13 @@ struct WaveDesc {
 };
 static_assert(sizeof(WaveDesc) == 32, "WaveDesc is 8 int32");
 
-// A workgroup unit: query rows [row_lo, row_lo + n_rows), 17 <= n_rows <= 64,
-// of one head against a list of full chunks.  All 4 waves of one workgroup
-// run it in lock step (two barriers per 64-key step): each loads a quarter
-// of every step into LDS and computes 16 of the rows from there.
+// A workgroup unit: query rows [row_lo, row_lo + n_rows) (17..64 rows in
+// decode, up to 64 per row tile count in prefill) of one head against a list
+// of chunks, every one but the last full.  All 4 waves of one workgroup run
+// it in lock step: each loads a quarter of every 64-key step into LDS and
+// computes its rows from there.
 struct UnitDesc {
-    int32_t n_keys;      // n_chunks * C
+    int32_t n_keys;      // keys read: (n_chunks - 1) * C plus what the last chunk holds (or less)
     int32_t chunk_off;   // first entry in the chunks section
     int32_t n_chunks;
     int32_t head;
