@@ -138,16 +138,27 @@ def cpu_baseline(w, unique_bytes, budget_s):
     }
 
 
-KERNEL_SRC = os.path.join(ROOT, "prefix_shared_kv_tree_amd", "csrc", "attn.hip")
+# the sources that decide what the attention kernel reads and writes per launch:
+# the kernels and the planner that cuts the work
+KERNEL_SRCS = [os.path.join(ROOT, "prefix_shared_kv_tree_amd", "csrc", f)
+               for f in ("attn.hip", "kernels.h", "shapes.h", "plan.cpp", "plan.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 ATTN_KERNEL = "attn_kernel"
 
 
 def kernel_source_sha256():
-    """Identifies the attention kernel the counters were taken on."""
+    """Identifies the attention kernel and planner code the counters were
+    taken on: the SHA-256 of those sources with comments and blank space
+    removed, so that a comment edit does not void the committed counters."""
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    import re
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
 
 
 def algorithmic_bytes(w, info):

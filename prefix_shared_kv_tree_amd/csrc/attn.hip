@@ -1,4 +1,6 @@
-// HIP kernels for decode attention over a prefix-shared KV tree, gfx950.
+// HIP kernels for attention over a prefix-shared KV tree, gfx950: decode
+// (both phases), prefill of arriving sequences, the partial merge, and the
+// K/V scatter / move / metadata-copy helpers.
 //
 // Method: "ChunkAttention: Efficient Self-Attention with Prefix-Aware KV Cache
 // and Two-Phase Partition" (chapterpal digest).  Knowl 2 gives the two-phase
@@ -12,7 +14,7 @@
 //
 // One kernel serves both phases.  The grid is a fixed set of persistent
 // workgroups of 4 waves.  Every step of the streaming loop takes 64 keys of
-// one head through the matrix cores:
+// one head through the matrix cores (16 keys at head_dim 256):
 //
 //   S^T (keys x rows)  = K  . Q^T    v_mfma_f32_16x16x32_f16, K as the A operand
 //   O^T (dims x rows) += V^T . P^T   v_mfma_f32_16x16x32_f16, V^T as the A operand
@@ -20,12 +22,14 @@
 // so one wave covers up to 16 query rows.  Work comes in two forms:
 //
 //  * Workgroup units (phase-1 row blocks of 17..64 rows).  The unit's waves
-//    split the loads of every step (each reads 1/4 or 1/2 of the step's K
-//    and V into registers, then writes it to LDS), meet at a barrier, and
-//    each wave computes 16 of the rows from the LDS copy.  Every stored byte
-//    of a shared chunk is thus fetched once per row block, by one load
-//    instruction, however many rows read it.  Each workgroup runs its units
-//    first, all 4 waves in lock step.
+//    split the loads of every step (each loads a quarter of the step's K and
+//    V into LDS -- straight from memory into two images used in turn from
+//    head_dim 128 on, through registers at head_dim 64), meet at a barrier,
+//    and each wave computes 16 of the rows from the LDS copy.  Every stored
+//    byte of a shared chunk is thus fetched once per row block, however many
+//    rows read it.  Each workgroup runs its units first, all 4 waves in lock
+//    step.  Prefill uses the same units with a causal limit per row and up to
+//    two 16-row tiles per wave.
 //  * Single-wave tasks (phase-2 items, and phase-1 row blocks of <= 16
 //    rows): every wave then walks its own list of tasks, keeping the next
 //    step's K/V -- or the next task's queries and first K/V -- in flight
@@ -43,7 +47,8 @@
 //                        consecutive dims are 8 bytes apart.
 // The online softmax (max, exp2, rescale) runs in fp32 on the S^T fragments;
 // P is rounded to fp16 for the PV product and n sums those rounded weights.
-// Scores are scaled by scale*log2(e) in fp32 so exp2 gives exp.  K and V are
+// Scores are scaled by scale*log2(e) in fp32 (inside the exponent's FMA) so
+// exp2 gives exp.  K and V are
 // read with non-temporal loads.
 #include <hip/hip_runtime.h>
 
