@@ -428,26 +428,27 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
     if (computes) finish<D, DT>(a, o, m_run, l_run, qrow, wout, head, col, grp);
 }
 
-// A wide unit: like run_unit (with the causal mask for prefill), but every wave
-// computes RT tiles of 16 query rows (a unit covers up to 64 RT rows), so
-// each K/V fragment read from LDS feeds RT matrix instructions, and the
-// unit may read up to 128 chunks (ids in two registers per lane).  From
+// A wide unit: like run_unit (with the causal mask for prefill), but every one
+// of the W waves computes RT tiles of 16 query rows (a unit covers up to
+// 16 W RT rows), so each K/V fragment read from LDS feeds RT matrix
+// instructions, and the unit may read up to 128 chunks (ids in two registers
+// per lane).  Each wave loads 1/W of every step's image.  From
 // head_dim 128 on, K/V go from memory straight into LDS (global_load_lds,
 // 16 bytes per lane, lanes at consecutive 16-byte LDS addresses) into two
 // images used in turn: the loads of step s + 1 fly while step s is computed,
 // with one barrier per step and no staging registers.  At head_dim 64 a V
 // load spans two padded 4-key groups, so the register path is kept.
-template <int D, int C, int RT, bool kCausal>
+template <int D, int C, int RT, bool kCausal, int W = kWaves>
 __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wave, int lane,
                                               char* img0, char* img1) {
     constexpr int KS = D / 32, DT = D / 16, NT = Step<D>::kTiles;
-    constexpr int kPer = Img<D>::kPieces / kWaves;
+    constexpr int kPer = Img<D>::kPieces / W;
     constexpr int NL = kPer / 64;
     constexpr int KP = Img<D>::kPiecesK;
     constexpr int TPW = kPer >= 2 * D ? kPer / (2 * D) : 1;
     constexpr bool kDirect = D >= 128;
     static_assert(kPer % 64 == 0 && (2 * D) % 64 == 0 && (kPer % (2 * D) == 0 || NT == 1) &&
-                  NL % TPW == 0, "piece split");
+                  NL % TPW == 0 && (NT == 1 || (W / 2) * TPW == NT), "piece split");
     static_assert(!kDirect || (D / 2) % 64 == 0, "a direct load must stay inside one V group");
     const int col = lane & 15;
     const int grp = lane >> 4;
@@ -473,7 +474,9 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         const int k = min((step * Step<D>::kKeys + 16 * tt) / C, (n_keys - 1) / C);
         return k < 64 ? __builtin_amdgcn_readlane(ids_lo, k) : __builtin_amdgcn_readlane(ids_hi, k - 64);
     };
-    const int ta = NT == 1 ? 0 : TPW * (role & 1);
+    // the first tile this wave loads: K tiles go to waves 0 .. W/2 - 1, V
+    // tiles to the others, TPW consecutive tiles each
+    const int ta = NT == 1 ? 0 : TPW * (role % (W / 2));
     // memory address of this lane's piece of load i of a step
     auto src = [&](int step, int i, const int (&id)[TPW]) {
         const int j0 = role * kPer + i * 64;
@@ -785,7 +788,7 @@ void attn_kernel(AttnArgs a) {
 
 // Prefill: the workgroup's units with the causal mask per row; nothing else.
 template <int D, int C>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ __launch_bounds__(64 * prefill_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char img0[Img<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char img1[D >= 128 ? Img<D>::kBytes : 16];
@@ -794,8 +797,8 @@ void prefill_kernel(AttnArgs a) {
     const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
     const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
     for (int k = 0; k < ucount; ++k)
-        run_unit_wide<D, C, prefill_row_tiles(D), true>(a, meta(a.units) + 8 * (ufirst + k), wave,
-                                                        lane, img0, img1);
+        run_unit_wide<D, C, prefill_row_tiles(D), true, prefill_waves(D)>(
+            a, meta(a.units) + 8 * (ufirst + k), wave, lane, img0, img1);
 }
 
 // Fold every partial of one (sequence, head) with attn_reduce and divide.
@@ -960,7 +963,7 @@ template <int D, int C>
 hipError_t prefill_dc(const AttnArgs& a, hipStream_t s) {
     const unsigned grid = static_cast<unsigned>(a.n_wg);
     if (grid == 0) return hipSuccess;
-    prefill_kernel<D, C><<<dim3(grid), dim3(256), 0, s>>>(a);
+    prefill_kernel<D, C><<<dim3(grid), dim3(64 * prefill_waves(D)), 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -127,7 +127,7 @@ int make_plan(const Tree& tree, int32_t b, const int32_t* q_order, const PlanOpt
 // Prefill plan: the query rows are positions q_from[s] .. len - 1 of each of
 // the n sequences seq_ids[s] (in that order, positions ascending), and a row
 // at position p attends to its sequence's tokens 0 .. p.  Rows are cut into
-// blocks of up to 64 * prefill_row_tiles(d) depth-first rows; a block reads
+// blocks of up to 16 * prefill_waves(d) * prefill_row_tiles(d) depth-first rows; a block reads
 // the chunks common to its sequences once for all its rows and each
 // sequence's own chunks for that sequence's rows, with the causal mask
 // applied per row in the kernel.  The blob has the decode layout with no

@@ -11,6 +11,8 @@ import numpy as np
  H_OFF_SEQLEN, H_TOTAL, H_NUNITS, H_OFF_WGUNITS, H_OFF_UNITS, H_OFF_QPOS) = range(22)
 MAGIC = 0x504B5657
 ROWS_PER_UNIT = 64
+# rows of a prefill unit: 8 waves x 2 row tiles of 16 up to head_dim 128, 1 tile at 256
+PREFILL_UNIT_ROWS = {64: 256, 128: 256, 256: 128}
 
 
 def parse(blob: np.ndarray) -> dict:
@@ -204,7 +206,7 @@ def check_prefill_plan(plan: dict, seq_ids, q_from, paths: dict, lens: dict, c: 
     units_of = defaultdict(int)                         # row -> units reading it (head 0)
     for u, ch in zip(plan["units"], plan["unit_chunks"]):
         n_keys, chunk_off, n_chunks, head, row_lo, n_rows, out, key_base = [int(v) for v in u]
-        assert 1 <= n_rows <= (128 if d <= 128 else 64) and 1 <= n_chunks <= 128 and 0 <= head < heads
+        assert 1 <= n_rows <= PREFILL_UNIT_ROWS[d] and 1 <= n_chunks <= 128 and 0 <= head < heads
         assert (n_keys + c - 1) // c == n_chunks
         assert all(fills[int(x)] == c for x in ch[:-1]) and n_keys <= sum(fills[int(x)] for x in ch)
         for i in range(n_rows):

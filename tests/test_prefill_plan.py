@@ -48,7 +48,7 @@ def test_prefill_batch_plans(b, prefix, new, c):
 
 def test_shared_prefix_read_once_per_row_block():
     """64 sequences x 8 new tokens over a stored 4-chunk prefix: 512 rows in
-    blocks of 16 sequences (128 rows), so each prefix chunk is read by 4 row
+    blocks of 32 sequences (256 rows), so each prefix chunk is read by 2 row
     blocks (per head), not 64."""
     pb = W.prefill_batch(3, 64, 64, 8, h=1, d=64, c=16, with_kv=False)
     t = _tree(1, 64, 16)
@@ -59,7 +59,7 @@ def test_shared_prefix_read_once_per_row_block():
         prefix_chunks = set(int(x) for x in B.pkvt_tree_chunk_path(t, int(ids[0]))[:4])
         readers = [u for u, ch in zip(plan["units"], plan["unit_chunks"])
                    if prefix_chunks & set(int(x) for x in ch)]
-        assert len(readers) == 4 and all(int(u[5]) == 128 for u in readers)
+        assert len(readers) == 2 and all(int(u[5]) == 256 for u in readers)
     finally:
         B.pkvt_tree_destroy(t)
 
