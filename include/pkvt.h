@@ -310,15 +310,18 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* tree, const void* d_meta, const
  * pkvt_kv_scatter of the new tokens' K/V, the new tokens' queries attend
  * causally: the row at position p of sequence s sees s's tokens 0 .. p, the
  * stored prefix included.  Chunks that several batch sequences read are
- * read once per block of up to 64 rows for all of them together (the
- * chunk-first phase of Knowl 2 applied to many query rows).
+ * read once per block of up to 256 rows (128 at head_dim 256) for all of
+ * them together (the chunk-first phase of Knowl 2 applied to many query
+ * rows).
  * ---------------------------------------------------------------------- */
 
 /* Plan the prefill of n sequences: query rows are positions q_from[i] ..
  * len_i - 1 of sequence seq_ids[i], sequences in the given order, positions
  * ascending (R rows in all).  opts may be NULL; phase1_chunks caps the
- * chunks per work item (0 = 64), workgroups as for pkvt_plan, the other
- * fields are ignored.  Reports the metadata bytes (pkvt_prefill_upload) and
+ * chunks per work item (0 = 128, also the maximum), workgroups sets the
+ * grid (0 = as for pkvt_plan, two per compute unit: a prefill workgroup has
+ * 8 waves and one is resident per compute unit, so the second half starts
+ * as the first finishes), the other fields are ignored.  Reports the metadata bytes (pkvt_prefill_upload) and
  * the workspace bytes (fp32 partials) pkvt_prefill_attn needs.
  * Errors: UNKNOWN_SEQ, INVALID_ARG (n < 1, a duplicate id, q_from outside
  * [0, len)), HOST_MEMORY. */

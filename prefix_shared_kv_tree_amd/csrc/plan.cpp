@@ -754,7 +754,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
         err = "prefill_plan: chunk limit and workgroups must be >= 0";
         return PKVT_ERR_INVALID_ARG;
     }
-    const int32_t G = in_opts.workgroups > 0 ? in_opts.workgroups : kPrefillWorkgroups;
+    const int32_t G = in_opts.workgroups > 0 ? in_opts.workgroups : kDefaultWorkgroups;
     const int32_t lanes = G * kWavesPerWg;
     const int32_t S = in_opts.phase1_chunks > 0 ? std::min(in_opts.phase1_chunks, kPrefillMaxChunks)
                                                 : kPrefillMaxChunks;
