@@ -235,3 +235,27 @@ def test_prefill_units_over_64_chunks(d, c, prefix, new):
           f"units={blob_units}", flush=True)
     assert err <= TOL
     ps.close()
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_prefill_grid_size_does_not_change_results(d):
+    """One prefill workgroup is resident per compute unit; a grid larger than
+    that is dispatched as workgroups finish.  Every unit's arithmetic and the
+    merge order are fixed by the plan, not by which workgroup runs a unit, so
+    grids of 256, 512 and 1024 workgroups give bit-identical outputs (and
+    match the oracle)."""
+    _torch()
+    print(f"\n[case] prefill grid sizes d={d}", flush=True)
+    pb = W.prefill_batch(61 + d, 24, 300, [int(x) for x in np.random.default_rng(d).integers(1, 400, 24)],
+                         h=3, d=d, c=32)
+    ref = A.prefill_attention(pb.w, pb.seqs, pb.q_from, pb.q)
+    ps = _setup(pb)
+    outs = []
+    for g in (256, 512, 1024):
+        ps.replan(workgroups=g)
+        outs.append(_run(ps))
+        print(f"[case]   workgroups={g} err={float(np.abs(outs[-1] - ref).max()):.3e} "
+              f"units={ps.info['wg_units']} slots={ps.info['slots']}", flush=True)
+    ps.close()
+    assert float(np.abs(outs[0] - ref).max()) <= TOL
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
