@@ -9,8 +9,9 @@ device chunk pool; its only inputs are the seeded workload arrays.
 Modules
   attention  the attention result per sequence, written as its plain
              definition (softmax of scaled dot products, fp64), plus the
-             chunk-partitioned form of the ChunkAttention page (Knowl 2 / 3)
-             used to pin the algebra the kernels rely on.
+             partial / merge equations of the ChunkAttention page (Knowl 3) and
+             the result assembled from them over any cover of a context by
+             disjoint pieces, used to pin the algebra the kernels rely on.
   sharing    which chunks a prefix tree stores once: the plain definition
              for insertion-built trees, and a small reference model of the
              arrival / decode-append / departure rules (Knowl 1) for dynamic

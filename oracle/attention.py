@@ -2,9 +2,9 @@
 
 Sources (cited by page title and section):
   * "ChunkAttention: Efficient Self-Attention with Prefix-Aware KV Cache and
-    Two-Phase Partition" (chapterpal digest), Knowl 2 (the two-phase
-    partition algorithm) and Knowl 3 (partial_attn / attn_reduce equations
-    and the final division O = o / n).
+    Two-Phase Partition" (chapterpal digest), Knowl 3 (partial_attn /
+    attn_reduce equations and the final division O = o / n) and Knowl 1 (a
+    shared chunk is stored once).
   * "CachedAttention / AttentionStore" digest, section "Load-bearing
     equations": Attention(Q, K, V) = softmax(Q K^T / sqrt(d_K)) V, which
     fixes the 1/sqrt(d) score scale that the ChunkAttention equations leave
@@ -18,8 +18,10 @@ is the plain definition
 over every token t currently stored for u (its root-to-leaf path).  The
 two-phase partition reaches exactly this result up to rounding, because
 attn_reduce is the exact online-softmax merge.  ``attention_batch`` is that
-definition; ``partial_attn`` / ``attn_reduce`` / ``tpp_attention`` restate
-the page's partitioned form so the tests can pin that it agrees.
+definition; ``partial_attn`` / ``attn_reduce`` restate the page's two
+equations, and ``partitioned_attention`` uses them to assemble the result
+from any cover of each context by disjoint pieces, so the tests can pin that
+such a decomposition (the one the kernels rely on) agrees with it.
 """
 from __future__ import annotations
 
@@ -74,7 +76,7 @@ def attention_batch(w, layer: int = 0, scale: float = None, seqs: Sequence[int] 
 
 
 # --------------------------------------------------------------------------
-# Partitioned form (Knowl 3 equations, Knowl 2 algorithm), natural exp, fp64.
+# Partitioned form (Knowl 3 equations), natural exp, fp64.
 # --------------------------------------------------------------------------
 
 def partial_attn(Qr: np.ndarray, Kc: np.ndarray, Vc: np.ndarray):
@@ -108,64 +110,56 @@ def attn_reduce(oC, mC, nC, ou, mu, nu):
     return x * oC + y * ou, M, x * nC + y * nu
 
 
-def tpp_attention(w, chunk_labels: List[np.ndarray], c: int, layer: int = 0,
-                  scale: float = None, order: str = "path", rng=None,
-                  min_share: int = 2) -> np.ndarray:
-    """The two-phase partition of Knowl 2, in fp64, on the oracle's own chunks.
+def partitioned_attention(w, pieces: Sequence[Sequence[Tuple[int, int, int]]], layer: int = 0,
+                          scale: float = None) -> np.ndarray:
+    """Attention assembled from partials over pieces of each context, fp64.
 
-    ``chunk_labels[u][k]`` identifies chunk k of sequence u (equal labels =
-    the same stored chunk, as produced by ``oracle.sharing.chunk_labels``).
-    Phase 1 visits every chunk covered by at least ``min_share`` sequences
-    once, running partial_attn for all covering query rows together.  Phase
-    2 folds, per sequence, those partials and then the sequence's own chunks
-    through attn_reduce, and divides.  ``order`` selects the fold order
-    ("path", "reverse" or "random") -- the merge is order-independent up to
-    rounding, which the tests check.  The K/V of a shared chunk is read from
-    the first covering sequence, so a wrong sharing map would change the
-    result."""
+    Knowl 3's two equations make attention over a key set decomposable: the
+    partial (o, m, n) of any subset of the keys carries everything needed,
+    and attn_reduce of the partials of disjoint subsets is the partial of
+    their union.  So for any cover of u's keys by disjoint pieces, folding
+    the pieces' partials in any order and dividing o by n gives the plain
+    result.  ``pieces[u]`` lists u's pieces in the order they are folded;
+    a piece (src, lo, hi) stands for keys lo .. hi-1 of sequence ``src``'s
+    materialised K/V.  With src = u and any partition of [0, L_u) the result
+    equals ``attention_batch``; a piece taken from another sequence models a
+    stored chunk that the tree claims both sequences hold (Knowl 1: a shared
+    chunk is stored once), so a wrong claim changes the result."""
     b, h, d = w.q.shape
     if scale is None:
         scale = default_scale(d)
-    mats = [materialize(w, u, layer) for u in range(b)]
-    cover: Dict[int, List[Tuple[int, int]]] = {}
+    mats: Dict[int, Tuple[np.ndarray, np.ndarray]] = {}
+    out = np.empty((b, h, d), dtype=np.float64)
+    for u in range(b):
+        for hh in range(h):
+            qs = w.q[u, hh].astype(np.float64)[None, :] * scale
+            o, m, n = np.zeros(d), -math.inf, 0.0
+            for src, lo, hi in pieces[u]:
+                if src not in mats:
+                    mats[src] = materialize(w, src, layer)
+                K, V = mats[src]
+                Op, mp, np_ = partial_attn(qs, K[lo:hi, hh], V[lo:hi, hh])
+                o, m, n = attn_reduce(Op[0], mp[0], np_[0], o, m, n)
+            out[u, hh] = o / n
+    return out
+
+
+def pieces_from_labels(chunk_labels: List[np.ndarray], c: int, lens: Sequence[int]):
+    """The chunk pieces of every context under a sharing map: chunk k of u
+    is keys k*c .. min((k+1)*c, L) of the first sequence (in index order)
+    whose path holds the same label -- the one stored copy of a shared
+    chunk.  Returns ``pieces`` for ``partitioned_attention`` (path order)."""
+    holder: Dict[int, Tuple[int, int]] = {}
     for u, labs in enumerate(chunk_labels):
         for k, lab in enumerate(labs):
-            cover.setdefault(int(lab), []).append((u, k))
-    out = np.empty((b, h, d), dtype=np.float64)
-    for hh in range(h):
-        # Phase 1: chunk-first over shared chunks.
-        shared_parts: Dict[int, Dict[int, tuple]] = {}
-        for lab, users in cover.items():
-            if len(users) < min_share:
-                continue
-            u0, k0 = users[0]
-            K, V = mats[u0]
-            sl = slice(k0 * c, min((k0 + 1) * c, K.shape[0]))
-            rows = np.stack([w.q[u, hh].astype(np.float64) * scale for u, _ in users])
-            O, m, n = partial_attn(rows, K[sl, hh], V[sl, hh])
-            shared_parts[lab] = {u: (O[i], m[i], n[i]) for i, (u, _) in enumerate(users)}
-        # Phase 2: sequence-first.
-        for u in range(b):
-            K, V = mats[u]
-            qs = w.q[u, hh].astype(np.float64)[None, :] * scale
-            parts = []
-            for k, lab in enumerate(chunk_labels[u]):
-                lab = int(lab)
-                if lab in shared_parts:
-                    parts.append(shared_parts[lab][u])
-                else:
-                    sl = slice(k * c, min((k + 1) * c, K.shape[0]))
-                    O, m, n = partial_attn(qs, K[sl, hh], V[sl, hh])
-                    parts.append((O[0], m[0], n[0]))
-            if order == "reverse":
-                parts = parts[::-1]
-            elif order == "random":
-                perm = (rng or np.random.default_rng(0)).permutation(len(parts))
-                parts = [parts[i] for i in perm]
-            o, m, n = np.zeros(d), -math.inf, 0.0
-            for oC, mC, nC in parts:
-                o, m, n = attn_reduce(oC, mC, nC, o, m, n)
-            out[u, hh] = o / n
+            holder.setdefault(int(lab), (u, k))
+    out = []
+    for u, labs in enumerate(chunk_labels):
+        row = []
+        for lab in labs:
+            src, k = holder[int(lab)]
+            row.append((src, k * c, min((k + 1) * c, int(lens[src]))))
+        out.append(row)
     return out
 
 

@@ -173,7 +173,7 @@ def test_scale_enters_scores():
     assert not np.allclose(a, A.attention_one(q, K, V, 0.25))
 
 
-# ---- partitioned form (Knowl 2 / 3) ---------------------------------------
+# ---- partitioned form (Knowl 3) -------------------------------------------
 
 def test_attn_reduce_identity():
     o = np.arange(4.0)
@@ -212,27 +212,67 @@ def test_attn_reduce_two_halves():
     np.testing.assert_allclose(o, Ow[0], rtol=1e-12, atol=1e-13)
 
 
+def _random_pieces(w, rng):
+    """Every context cut at random points (not chunk boundaries), the pieces
+    listed in a random order."""
+    out = []
+    for u in range(w.b):
+        L = w.seq_len(u)
+        k = int(rng.integers(0, min(L, 6)))
+        cuts = np.unique(np.concatenate([[0, L], rng.integers(1, L, size=k) if L > 1 else []]))
+        row = [(u, int(a), int(b)) for a, b in zip(cuts[:-1], cuts[1:])]
+        out.append([row[i] for i in rng.permutation(len(row))])
+    return out
+
+
+@pytest.mark.parametrize("case", ["tiny", "rand0", "rand1", "rand2", "rand3"])
+def test_random_partition_equals_monolithic(case):
+    """Knowl 3: any cover of a context by disjoint key pieces, their partials
+    folded by attn_reduce in any order, gives the plain result."""
+    if case == "tiny":
+        w = W.make_config("tiny")
+    else:
+        w = W.random_tree(int(case[4:]) + 10, h=2, d=8, c=4, max_b=6, max_len=60)
+    ref = A.attention_batch(w)
+    for seed in range(3):
+        got = A.partitioned_attention(w, _random_pieces(w, np.random.default_rng(seed)))
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
 @pytest.mark.parametrize("order", ["path", "reverse", "random"])
 @pytest.mark.parametrize("case", ["tiny", "rand0", "rand1", "rand2", "rand3"])
-def test_tpp_equals_monolithic(case, order):
+def test_shared_chunks_read_once_equal_monolithic(case, order):
+    """Every chunk read from its one stored copy (the first holder of its
+    label under the sharing definition), folded in path, reverse or random
+    order: equals the plain result, because shared chunks really hold the
+    same tokens."""
     if case == "tiny":
         w = W.make_config("tiny")
     else:
         w = W.random_tree(int(case[4:]) + 10, h=2, d=8, c=4, max_b=6, max_len=60)
     labs = S.chunk_labels(w.all_seq_tokens(), w.c)
+    pieces = A.pieces_from_labels(labs, w.c, [w.seq_len(u) for u in range(w.b)])
+    if case == "tiny":
+        assert any(p[0] != u for u, row in enumerate(pieces) for p in row)   # the prefix is shared
+    rng = np.random.default_rng(3)
+    if order == "reverse":
+        pieces = [row[::-1] for row in pieces]
+    elif order == "random":
+        pieces = [[row[i] for i in rng.permutation(len(row))] for row in pieces]
     ref = A.attention_batch(w)
-    got = A.tpp_attention(w, labs, w.c, order=order, rng=np.random.default_rng(3))
+    got = A.partitioned_attention(w, pieces)
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
 
 
-def test_tpp_detects_wrong_sharing():
-    """The partitioned oracle reads a shared chunk's K/V once, so an
-    incorrect sharing map changes its result (the same mechanism that makes
-    a GPU tree with a wrong map fail parity)."""
+def test_wrong_sharing_changes_result():
+    """A chunk taken from a sequence that does not hold it changes the
+    result (the same mechanism that makes a GPU tree with a wrong map fail
+    parity)."""
     w = W.make_config("tiny")
     labs = S.chunk_labels(w.all_seq_tokens(), w.c)
     bad = [l.copy() for l in labs]
     bad[1][4] = bad[0][4]           # pretend seq 1's first private chunk is seq 0's
     ref = A.attention_batch(w)
-    got = A.tpp_attention(w, bad, w.c)
+    got = A.partitioned_attention(w, A.pieces_from_labels(bad, w.c, [w.seq_len(u) for u in range(w.b)]))
     assert np.abs(got[1] - ref[1]).max() > 1e-3
+    np.testing.assert_allclose(got[0], ref[0], rtol=1e-12, atol=1e-13)

@@ -102,6 +102,54 @@ def test_fragmentation_bound(seed):
         assert (allocated - n) / n <= S.fragmentation_bound(c, n) + 1e-15
 
 
+def test_sharing_ratio_hand_worked():
+    """Knowl 4: r = n_s / (n_p + n_c), worked by hand: 1024 shared tokens of
+    a 1536-token prompt with 512 generated tokens make half of the final
+    context shared; with nothing generated two thirds; a fully shared prompt
+    before decoding is all shared; nothing shared is 0."""
+    assert S.sharing_ratio(1024, 1536, 512) == 0.5
+    assert S.sharing_ratio(1024, 1536, 0) == pytest.approx(2 / 3, rel=1e-15)
+    assert S.sharing_ratio(2048, 2048, 0) == 1.0
+    assert S.sharing_ratio(0, 2048, 512) == 0.0
+    assert S.sharing_ratio(256, 512, 256) == pytest.approx(1 / 3, rel=1e-15)
+
+
+@pytest.mark.parametrize("n_s,n_q,n_c", [(64, 32, 40), (128, 0, 96), (32, 64, 128), (96, 16, 1)])
+def test_sharing_ratio_is_shared_fraction_after_decode(n_s, n_q, n_c):
+    """Knowl 4's r, measured on the reference model: b sequences whose
+    prompts (n_p = n_s + n_q tokens) share their first n_s tokens, each then
+    decoding n_c tokens of its own.  The fraction of every final context
+    that lies in chunks stored once for all sequences is r(n_s, n_p, n_c)."""
+    c, b = 16, 5
+    rng = np.random.default_rng(n_s + n_q + n_c)
+    shared = [int(x) for x in rng.integers(0, 1000, size=n_s)]
+    m = S.SharingModel(c)
+    sids = [m.insert(shared + [int(x) for x in rng.integers(1000 * (u + 1), 1000 * (u + 2), size=n_q)])
+            for u in range(b)]
+    for _ in range(n_c):
+        for sid in sids:
+            m.append(sid, int(rng.integers(0, 1 << 20)))
+    for sid in sids:
+        in_shared = sum(len(n.tokens) for n in m.seqs[sid] if len(n.refs) == b)
+        total = m.seq_len(sid)
+        assert total == n_s + n_q + n_c
+        assert in_shared / total == pytest.approx(S.sharing_ratio(n_s, n_s + n_q, n_c), rel=1e-15)
+
+
+@pytest.mark.parametrize("c", [2, 4, 16, 64])
+@pytest.mark.parametrize("k", [0, 1, 5, 37])
+def test_fragmentation_bound_is_reached(c, k):
+    """Knowl 4's bound (c - 1) / n is tight: a context of n = k c + 1 tokens
+    fills its last chunk with one token, so exactly c - 1 slots of the
+    chunks the reference model allocates for it are unused."""
+    n = k * c + 1
+    m = S.SharingModel(c)
+    sid = m.insert(list(range(n)))
+    allocated = c * len(m.seqs[sid])
+    assert allocated - n == c - 1
+    assert (allocated - n) / n == S.fragmentation_bound(c, n)
+
+
 # ---- reference model -------------------------------------------------------
 
 @pytest.mark.parametrize("seed", range(25))
