@@ -28,8 +28,8 @@
 //    and each wave computes 16 of the rows from the LDS copy.  Every stored
 //    byte of a shared chunk is thus fetched once per row block, however many
 //    rows read it.  Each workgroup runs its units first, all 4 waves in lock
-//    step.  Prefill uses the same units with a causal limit per row and up to
-//    two 16-row tiles per wave.
+//    step.  Prefill runs wider units of the same kind (run_unit_wide: eight
+//    waves, up to two 16-row tiles per wave, a causal limit per row).
 //  * Single-wave tasks (phase-2 items, and phase-1 row blocks of <= 16
 //    rows): every wave then walks its own list of tasks, keeping the next
 //    step's K/V -- or the next task's queries and first K/V -- in flight
@@ -293,10 +293,9 @@ struct Img {
 // Wave w loads pieces [w, w + 1) * kPieces / 4 of every step's image and
 // computes rows 16w .. 16w + 15 (if it has any) from the LDS copy.  The trip
 // count comes from the unit descriptor that all 4 waves read, so every wave
-// passes the same number of barriers.  kCausal (prefill): the row at
-// sequence position p sees only the keys at positions <= p, the unit's keys
-// starting at position key_base.
-template <int D, int C, bool kCausal>
+// passes the same number of barriers.  Decode only (every row sees all of
+// the unit's keys); prefill units are run_unit_wide's.
+template <int D, int C>
 __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, int lane, char* img) {
     constexpr int KS = D / 32, DT = D / 16, NT = Step<D>::kTiles;
     constexpr int kPer = Img<D>::kPieces / kWaves;   // pieces per wave per step
@@ -314,7 +313,6 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
     const int row_lo = u[4];
     const int n_rows = u[5];
     const int out = u[6];
-    const int key_base = kCausal ? u[7] : 0;
     const int role = wave;
     const bool computes = 16 * role < n_rows;
     const int n_steps = (n_keys + Step<D>::kKeys - 1) / Step<D>::kKeys;
@@ -362,11 +360,9 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 
     h8 qb[KS];
     int qrow = -1;
-    int lim = n_keys;                  // keys this lane's row sees
     if (computes) {
         const int r = 16 * role + col;
         qrow = r < n_rows ? a.rows[row_lo + r] : -1;
-        if (kCausal && r < n_rows) lim = min(n_keys, a.qpos[row_lo + r] + 1 - key_base);
         const _Float16* qp = static_cast<const _Float16*>(a.q) +
                              (static_cast<size_t>(qrow < 0 ? 0 : qrow) * H + head) * D + 8 * grp;
 #pragma unroll
@@ -399,8 +395,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
                 }
             }
             h4 pq[NT];
-            softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, kCausal ? lim : n_keys, grp,
-                                 a.scale_log2e);
+            softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, n_keys, grp, a.scale_log2e);
             // V entries past the last key are zeroed on the last step only
             auto pv = [&](auto masked) {
 #pragma unroll
@@ -423,9 +418,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
                 pv(Flag<false>{});
         }
     }
-    // a prefill unit whose rows read nothing else writes O itself (out < 0)
-    const int wout = (kCausal && out < 0) ? -1 : out + 16 * role;
-    if (computes) finish<D, DT>(a, o, m_run, l_run, qrow, wout, head, col, grp);
+    if (computes) finish<D, DT>(a, o, m_run, l_run, qrow, out + 16 * role, head, col, grp);
 }
 
 // A wide unit: like run_unit (with the causal mask for prefill), but every one
@@ -679,7 +672,7 @@ void attn_kernel(AttnArgs a) {
             if constexpr (D >= 128)
                 run_unit_wide<D, C, 1, false>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds, lds1);
             else
-                run_unit<D, C, false>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
+                run_unit<D, C>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds);
         }
     }
 
