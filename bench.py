@@ -115,9 +115,38 @@ def time_region(ds, B, ev, stream, steps, warmup, per_kernel):
     return total, wall, step_ms, attn_ms
 
 
+def _oracle_worker(args):
+    """One worker of the all-cores oracle run: the oracle on its share of the
+    sequences of layer 0 (the workload is inherited from the parent)."""
+    from oracle import attention as A
+    w, seqs = _ORACLE_JOB["w"], args
+    A.attention_batch(w, layer=0, seqs=seqs)
+    return len(seqs)
+
+
+_ORACLE_JOB = {}
+
+
+def oracle_cores():
+    """CPU threads the all-cores oracle run may use: the CPUs this process
+    may run on, at most 16 (a one-GPU share of a GPU host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def cpu_baseline(w, unique_bytes, budget_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the same layer:
-    sequences are evaluated one by one until the time budget is spent."""
+    """The fp64 oracle, as it stands, on the same layer, twice:
+      * single thread, on a bounded sample: sequences one by one until the
+        time budget is spent, scaled to the whole layer;
+      * on all the host cores this process may use (at most 16): every
+        sequence of the layer, spread over that many forked worker processes
+        (the oracle itself is unchanged; numpy runs one thread per worker),
+        best of two runs.
+    Must run before the GPU is initialised (the workers are forked)."""
+    import multiprocessing as mp
     from oracle import attention as A
     t0 = time.perf_counter()
     done = 0
@@ -127,14 +156,30 @@ def cpu_baseline(w, unique_bytes, budget_s):
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    per_layer_s = el * w.b / done
+    per_layer_1 = el * w.b / done
+    cores = oracle_cores()
+    _ORACLE_JOB["w"] = w
+    parts = [list(range(k, w.b, cores)) for k in range(cores) if k < w.b]
+    runs = []
+    with mp.get_context("fork").Pool(len(parts)) as pool:
+        for _ in range(2):
+            t1 = time.perf_counter()
+            assert sum(pool.map(_oracle_worker, parts, chunksize=1)) == w.b
+            runs.append(time.perf_counter() - t1)
+    _ORACLE_JOB.clear()
+    per_layer_n = min(runs)
     return {
-        "value": round(unique_bytes / per_layer_s / 1e9, 4),
+        "value": round(unique_bytes / per_layer_n / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": len(parts),
         "kind": "oracle",
-        "sample": f"{done} of {w.b} sequences of layer 0 ({el:.1f} s, numpy fp64 single thread); "
-                  f"scaled to one layer = {per_layer_s * 1e3:.0f} ms/layer",
+        "sample": f"all {w.b} sequences of layer 0 over {len(parts)} worker processes "
+                  f"(numpy fp64, one thread each), best of 2 runs = {per_layer_n * 1e3:.0f} ms/layer; "
+                  f"single thread: {done} of {w.b} sequences in {el:.1f} s, scaled to one layer = "
+                  f"{per_layer_1 * 1e3:.0f} ms/layer",
+        "single_thread_value": round(unique_bytes / per_layer_1 / 1e9, 4),
+        "ms_per_layer": round(per_layer_n * 1e3, 1),
+        "single_thread_ms_per_layer": round(per_layer_1 * 1e3, 1),
     }
 
 
@@ -781,6 +826,71 @@ def run_prefill(args):
                       "steps": args.prefill_steps}), flush=True)
 
 
+def config_entry(name, args, ev, stream):
+    """One more configuration at the bench's own protocol: layer 0 holds the
+    workload's K/V (checked against the oracle on sampled rows), the other
+    rotated layers are drawn on the device; TPP and the plain per-sequence
+    schedule (phase 1 off) are each timed over --config-steps steps; the
+    attention kernel alone is timed with events around it."""
+    import torch
+    from oracle import attention as A
+    from prefix_shared_kv_tree_amd import binding as B
+    from prefix_shared_kv_tree_amd import workloads as W
+    from prefix_shared_kv_tree_amd.harness import DecodeSetup
+    w = W.make_config(name, layers=1)
+    b_tok = w.h * w.d * 2 * 2
+    unique = W.unique_tokens(w) * b_tok
+    layers = max(2, math.ceil(2 * 2 ** 30 / unique))
+    ds = DecodeSetup(w, layers=layers, extra_layers_seed=5000 + W.CONFIG_NAMES.index(name))
+    info = dict(ds.info)
+    assert info["unique_tokens"] * b_tok == unique
+    out = ds.decode(0)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    rows = sorted({0, 1, w.b // 2, w.b - 2, w.b - 1})
+    ref = A.attention_batch(w, layer=0, seqs=rows)
+    parity = float(max(np.abs(got[u] - ref[u]).max() for u in rows))
+    steps, warm = args.config_steps, 10
+    t_ms, _, _, _ = time_region(ds, B, ev, stream, steps, warm, per_kernel=False)
+    _, _, _, attn_ms = time_region(ds, B, ev, stream, steps, warm, per_kernel=True)
+    us = t_ms / steps * 1e3
+    attn_us = float(np.mean(attn_ms)) * 1e3
+    _, attn_bytes = algorithmic_bytes(w, info)
+    ds.replan(0, 0, 1 << 20)
+    p_ms, _, _, _ = time_region(ds, B, ev, stream, steps, warm, per_kernel=False)
+    p_us = p_ms / steps * 1e3
+    plain_plan = dict(ds.info)
+    ds.close()
+    del ds
+    gbps = unique / (us * 1e-6) / 1e9
+    res = {
+        "workload": W.CONFIG_DESCRIPTIONS[name],
+        "layers_rotated": layers, "steps": steps,
+        "unique_kv_bytes": int(unique),
+        "tpp_us_per_layer": round(us, 2),
+        "effective_gbps": round(gbps, 1),
+        "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "attn_kernel_us": round(attn_us, 2),
+        "kernel_frac_unique_kv": round(unique / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "kernel_frac_algorithmic": round(attn_bytes / (attn_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "plain_us_per_layer": round(p_us, 2),
+        "speedup_vs_plain": round(p_us / us, 3),
+        "tpp_over_plain_time": round(us / p_us, 4),
+        "same_plan_as_plain": info["tasks"] == plain_plan["tasks"] and info["wg_units"] == plain_plan["wg_units"]
+                           and info["phase1_items"] == 0,
+        "plan": {k: info[k] for k in ("phase1_items", "phase2_items", "wg_units", "tasks", "slots",
+                                       "merge_rows")},
+        "parity_max_abs_err_sampled": parity,
+        "parity_rows": rows,
+    }
+    traffic = profile_traffic(name)
+    if traffic:
+        res["rocprof_kernel_avg_us"] = traffic.get("kernel_avg_us_trace")
+        res["traffic_bytes"] = traffic["traffic_bytes"]
+    print(json.dumps({name: res}), file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -830,6 +940,11 @@ def main():
                     help="time only this prefill workload (index), shared variant only")
     ap.add_argument("--loop-only", action="store_true",
                     help="run only the decode loop (for profiling it)")
+    ap.add_argument("--other-configs", default="c2,c4,c5",
+                    help="comma-separated configurations also timed (TPP and plain, sampled "
+                         "parity) and reported in the line's `configs` object; '' for none")
+    ap.add_argument("--config-steps", type=int, default=100,
+                    help="timed steps per variant for each of --other-configs")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args)
@@ -848,9 +963,22 @@ def main():
               "GPU's share and has no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    from prefix_shared_kv_tree_amd import workloads as W
+    bench_run = not (args.sweep or args.prefill or args.loop_only)
+    if bench_run:
+        # host-side work first: the workload draws, and the oracle's CPU
+        # baseline (its worker processes are forked before the GPU is touched)
+        probe = W.make_config(args.config, with_kv=False)
+        b_tok = probe.h * probe.d * 2 * 2
+        unique_bytes_est = W.unique_tokens(probe) * b_tok
+        layers = max(2, math.ceil(2 * 2 ** 30 / unique_bytes_est))
+        t0 = time.perf_counter()
+        w = W.make_config(args.config, layers=layers)
+        gen_s = time.perf_counter() - t0
+        cpu = None if args.no_cpu_baseline else cpu_baseline(w, unique_bytes_est, args.cpu_budget)
+
     import torch
     from prefix_shared_kv_tree_amd import binding as B
-    from prefix_shared_kv_tree_amd import workloads as W
     from prefix_shared_kv_tree_amd.harness import DecodeSetup
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -862,21 +990,16 @@ def main():
     if args.prefill:
         run_prefill(args)
         return
-
-    probe = W.make_config(args.config, with_kv=False)
-    b_tok = probe.h * probe.d * 2 * 2
-    unique_bytes_est = W.unique_tokens(probe) * b_tok
-    layers = max(2, math.ceil(2 * 2 ** 30 / unique_bytes_est))
     if args.loop_only:
+        probe = W.make_config(args.config, with_kv=False)
+        layers = max(2, math.ceil(2 * 2 ** 30 / (W.unique_tokens(probe) * probe.h * probe.d * 4)))
         print(json.dumps({"config": args.config,
                           "decode_loop": decode_loop(args, args.config, layers, None)}), flush=True)
         return
-    t0 = time.perf_counter()
-    w = W.make_config(args.config, layers=layers)
-    gen_s = time.perf_counter() - t0
     ds = DecodeSetup(w, phase1_chunks=args.phase1_chunks, phase2_chunks=args.phase2_chunks)
     info = dict(ds.info)
     unique_bytes = info["unique_tokens"] * b_tok
+    assert unique_bytes == unique_bytes_est, "tree and workload disagree on the stored tokens"
     logical_bytes = info["logical_tokens"] * b_tok
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -969,7 +1092,17 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic["traffic_bytes"] if traffic else None,
             "kernel": f"attn_kernel<{D},{w.c}>",
+            # achieved = algorithmic_bytes_per_launch / duration_us: the distinct
+            # stored KV bytes plus Q and the kernel's partial / O writes, over the
+            # mean HIP-event time of the attention kernel alone (events recorded
+            # on its stream right before and after it, K launches)
             "algorithmic_bytes_per_launch": int(attn_bytes),
+            "duration_us": round(attn_avg_us, 2),
+            "duration": "mean of K HIP-event intervals around the attention kernel alone, on its stream",
+            # the same duration with only the distinct stored KV bytes counted
+            "unique_kv_bytes": int(unique_bytes),
+            "frac_unique_kv": round(unique_bytes / (attn_avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "rocprof_avg_us": traffic.get("kernel_avg_us_trace") if traffic else None,
         },
         "workload_gen_s": round(gen_s, 1),
         # a counter-collection run calibrates on its own copy's dispatches
@@ -985,10 +1118,17 @@ def main():
         res["speedup_vs_plain"] = round(p_us / us_layer, 3)
         ds.replan(args.phase1_chunks, args.phase2_chunks, 0)
 
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, unique_bytes, args.cpu_budget)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     ds.close()
     del ds
+    if args.other_configs:
+        res["configs"] = {name: config_entry(name, args, ev, stream)
+                          for name in args.other_configs.split(",") if name}
+        probe_gbps = res["hbm_copy_probe_gbps"]
+        for entry in res["configs"].values():
+            entry["effective_over_copy_probe"] = (round(entry["effective_gbps"] / probe_gbps, 3)
+                                                  if probe_gbps else None)
     if not args.no_loop:
         res["decode_loop"] = decode_loop(args, args.config, layers, us_layer)
     if args.copy_probe_mib:

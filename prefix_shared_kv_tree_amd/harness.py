@@ -52,10 +52,14 @@ class DecodeSetup:
                  phase1_chunks: int = 0, phase2_chunks: int = 0, min_share: int = 0,
                  pool_chunks: Optional[int] = None, unit_rows: int = 0,
                  device_random_seed: Optional[int] = None, match: str = "chunks",
-                 build_groups: int = 1):
+                 build_groups: int = 1, extra_layers_seed: Optional[int] = None):
         """``device_random_seed``: instead of the workload's K/V (which may
         then be absent), fill the pools and Q with N(0,1) fp16 drawn on the
-        device (for timing sweeps that need no oracle).  ``match``: the
+        device (for timing sweeps that need no oracle).
+        ``extra_layers_seed``: ``layers`` may exceed the workload's own layer
+        count; the pools of the layers it lacks are drawn N(0,1) on the
+        device with this seed (Q and the workload's layers stay as given, so
+        those layers can still be checked against the oracle).  ``match``: the
         tree's prefix matching ("chunks" or "tokens").  ``build_groups``:
         insert the sequences in that many successive pkvt_tree_build calls
         (in order); under token matching a later call may split nodes of an
@@ -98,13 +102,13 @@ class DecodeSetup:
         self.v_pools: List = []
         stream = torch.cuda.current_stream().cuda_stream
         gen = None
-        if device_random_seed is not None:
+        if device_random_seed is not None or extra_layers_seed is not None:
             gen = torch.Generator(device=device)
-            gen.manual_seed(device_random_seed)
+            gen.manual_seed(device_random_seed if device_random_seed is not None else extra_layers_seed)
         for layer in range(self.layers):
             kp = torch.empty(pool_elems, dtype=torch.float16, device=device)
             vp = torch.empty(pool_elems, dtype=torch.float16, device=device)
-            if gen is not None:
+            if device_random_seed is not None or (extra_layers_seed is not None and layer >= w.layers):
                 kp.normal_(generator=gen)
                 vp.normal_(generator=gen)
                 self.k_pools.append(kp)
@@ -129,7 +133,7 @@ class DecodeSetup:
                     del kd, vd, sd
             self.k_pools.append(kp)
             self.v_pools.append(vp)
-        if gen is not None:
+        if device_random_seed is not None:
             self.q = torch.empty(w.q.shape, dtype=torch.float16, device=device).normal_(generator=gen)
         else:
             self.q = torch.from_numpy(np.ascontiguousarray(w.q)).to(device)

@@ -44,3 +44,16 @@ def test_algorithmic_bytes_c3():
     assert unique == W.unique_tokens(w) * 32 * 128 * 4          # 16 KiB per distinct token
     assert attn == unique + 64 * 32 * 128 * 2 + info["slots"] * 32 * 130 * 4 + \
         (64 - info["merge_rows"]) * 32 * 128 * 2
+
+
+def test_cpu_baseline_single_and_all_cores():
+    """The oracle's CPU baseline: a single-thread figure on a sample and an
+    all-cores figure over every sequence, both for the same layer."""
+    from prefix_shared_kv_tree_amd import workloads as W
+    w = W.make_config("tiny")
+    unique = W.unique_tokens(w) * w.h * w.d * 4
+    r = bench.cpu_baseline(w, unique, 0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert 1 <= r["cores"] <= min(bench.oracle_cores(), w.b)
+    assert r["value"] > 0 and r["single_thread_value"] > 0
+    assert r["ms_per_layer"] > 0

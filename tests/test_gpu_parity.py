@@ -244,43 +244,66 @@ def test_decode_append_and_lazy_upload():
 
 @pytest.mark.parametrize("b,n_s,private", [(96, 2048, 56), (16, 2048, 8), (32, 1024, 1),
                                            (32, 4096, 960), (80, 2048, 40)])
-@pytest.mark.parametrize("variant", ["tpp", "plain"])
-def test_sweep_shapes_sampled(b, n_s, private, variant):
+def test_sweep_shapes_all_rows(b, n_s, private):
     """Full-size points of the divergence and batch sweeps (h = 32, d = 128,
     c = 64; b sequences sharing n_s prompt tokens plus `private` tokens
-    each): sampled rows against the oracle."""
+    each), two-phase and plain: every output row against the oracle (b = 80
+    and 96 cut the shared rows into several blocks)."""
     _torch()
-    print(f"\n[case] sweep shape b={b} n_s={n_s} private={private} {variant}", flush=True)
     w = W.one_prefix(4000 + b + n_s + private, b, n_s, private, h=32, d=128, c=64)
-    ds = _setup(w, min_share=(1 << 20) if variant == "plain" else 0)
-    got = _run(ds)
-    rows = sorted({0, b // 3, b // 2 + 1, b - 1})
-    ref = A.attention_batch(w, seqs=rows)
-    err = _err(got[rows], ref[rows])
-    print(f"[case]   rows {rows} err={err:.3e} info={ds.info}", flush=True)
-    assert err <= TOL
-    ds.close()
+    ref = A.attention_batch(w)
+    for variant, ms in (("tpp", 0), ("plain", 1 << 20)):
+        print(f"\n[case] sweep shape b={b} n_s={n_s} private={private} {variant}", flush=True)
+        ds = _setup(w, min_share=ms)
+        err = _err(_run(ds), ref)
+        print(f"[case]   all {b} rows err={err:.3e} info={ds.info}", flush=True)
+        assert err <= TOL
+        if variant == "tpp":
+            assert ds.info["wg_units"] > 0
+        ds.close()
 
 
 @pytest.mark.parametrize("d,c", [(256, 64), (256, 16), (256, 128), (64, 64)])
 def test_head_dim_variants_long_prefix(d, c):
     """The long-shared-prompt batch (64 sequences, 4096 shared tokens,
-    ragged private suffixes) at other head dims, with h d = 4096: sampled
-    rows against the oracle, two-phase and plain."""
+    ragged private suffixes) at other head dims, with h d = 4096: every row
+    against the oracle, two-phase and plain."""
     _torch()
     h = 4096 // d
     rng = np.random.default_rng(d + c)
     suffix = [int(x) for x in rng.integers(256, 1025, size=64)]
     print(f"\n[case] head_dim variant d={d} c={c} h={h}", flush=True)
     w = W.one_prefix(5000 + d + c, 64, 4096, suffix, h=h, d=d, c=c)
-    rows = [0, 21, 42, 63]
-    ref = A.attention_batch(w, seqs=rows)
+    ref = A.attention_batch(w)
     for ms in (0, 1 << 20):
         ds = _setup(w, min_share=ms)
         got = _run(ds)
-        err = _err(got[rows], ref[rows])
-        print(f"[case]   min_share={ms} err={err:.3e} info={ds.info}", flush=True)
+        err = _err(got, ref)
+        print(f"[case]   min_share={ms} all 64 rows err={err:.3e} info={ds.info}", flush=True)
         assert err <= TOL
+        ds.close()
+
+
+# ChunkAttention page, Knowl 6: b = 32 sequences of n_p context tokens each, the
+# first n_s shared by all of them (h = 32, d = 128, c = 64, fp16).
+@pytest.mark.parametrize("n_p,n_s", [(4096, 4096), (2048, 2048), (1024, 1024), (4096, 3072),
+                                     (2048, 1024), (1024, 0)])
+def test_knowl6_cells_all_rows(n_p, n_s):
+    """Cells of the pages' microkernel grid, among them every fully shared
+    corner (n_s = n_p: each context is one shared prompt), two-phase and
+    plain: every output row against the oracle."""
+    _torch()
+    w = W.one_prefix(6000 + n_p + n_s, 32, n_s, n_p - n_s, h=32, d=128, c=64)
+    assert all(w.seq_len(u) == n_p for u in range(32))
+    ref = A.attention_batch(w)
+    for variant, ms in (("tpp", 0), ("plain", 1 << 20)):
+        print(f"\n[case] knowl6 n_p={n_p} n_s={n_s} {variant}", flush=True)
+        ds = _setup(w, min_share=ms)
+        err = _err(_run(ds), ref)
+        print(f"[case]   all 32 rows err={err:.3e} info={ds.info}", flush=True)
+        assert err <= TOL
+        if variant == "tpp" and n_s > 0:
+            assert ds.info["phase1_items"] > 0
         ds.close()
 
 
