@@ -23,7 +23,9 @@
  *     not thread-safe: use one host thread per tree at a time.
  *   - All DEVICE memory (K/V pools, Q, O, metadata, workspace, slot arrays
  *     for the scatter) is allocated and owned by the caller and passed as
- *     raw device pointers.  The library never allocates device memory.
+ *     raw device pointers.  The library never allocates device memory; its
+ *     only device storage is the fixed scratch array of
+ *     pkvt_attn_decode_noalloc, part of the loaded code object.
  *   - "stream" arguments are hipStream_t values passed as void*; NULL is the
  *     default stream.  Device work is asynchronous on that stream.
  *   - Host pointer arguments are only read/written during the call.
@@ -302,6 +304,25 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* tree, const void* d_meta, const
                                 const void* k_pool, const void* v_pool, void* out,
                                 void* workspace, size_t workspace_bytes, float scale,
                                 void* stream, void* attn_start_event, void* attn_end_event);
+
+/* pkvt_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, with the partial results in a fixed device
+ * scratch array of PKVT_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on every device it runs on until the process ends, instead of a
+ * caller workspace.  The call allocates nothing.  Arguments as
+ * pkvt_attn_decode, less the workspace; the current device must be the one
+ * that q, the pools and out live on.  The scratch is shared by every call
+ * on a device and keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that overlap on one device -- on different
+ * streams, or from several host threads -- race on it and must not be
+ * issued.  Errors: BUFFER_TOO_SMALL when the plan's partials
+ * (workspace_bytes of pkvt_plan) exceed the scratch, otherwise as
+ * pkvt_attn_decode. */
+#define PKVT_NOALLOC_SCRATCH_BYTES (64u << 20)
+pkvt_status pkvt_attn_decode_noalloc(const pkvt_tree* tree, const void* d_meta, const void* q,
+                                     const void* k_pool, const void* v_pool, void* out,
+                                     float scale, void* stream);
 
 /* ------------------------------------------------------------------------
  * Prefix-aware prefill (Knowl 1 arrival: matched prefix chunks are shared,

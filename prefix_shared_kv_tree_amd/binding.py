@@ -78,6 +78,7 @@ _SIGNATURES = {
     "pkvt_plan_upload": [_vp, _vp, _sz, _vp],
     "pkvt_attn_decode": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp],
     "pkvt_attn_decode_ex": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, C.c_float, _vp, _vp, _vp],
+    "pkvt_attn_decode_noalloc": [_vp, _vp, _vp, _vp, _vp, _vp, C.c_float, _vp],
     "pkvt_prefill_plan": [_vp, C.c_int32, _i32p, _i64p, C.POINTER(PlanOpts), C.POINTER(_sz),
                           C.POINTER(_sz)],
     "pkvt_prefill_info_get": [_vp, C.POINTER(PlanInfo)],
@@ -344,6 +345,15 @@ def pkvt_attn_decode_ex(tree: int, d_meta: int, q: int, k_pool: int, v_pool: int
     _check("pkvt_attn_decode_ex", load().pkvt_attn_decode_ex(
         tree, d_meta, q, k_pool, v_pool, out, workspace or None, workspace_bytes, float(scale),
         stream or None, attn_start_event or None, attn_end_event or None))
+
+
+PKVT_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pkvt_attn_decode_noalloc(tree: int, d_meta: int, q: int, k_pool: int, v_pool: int, out: int,
+                             scale: float, stream: int = 0) -> None:
+    _check("pkvt_attn_decode_noalloc", load().pkvt_attn_decode_noalloc(
+        tree, d_meta, q, k_pool, v_pool, out, float(scale), stream or None))
 
 
 def pkvt_kv_scatter(tree: int, k_pool: int, v_pool: int, slots: int, k_new: int, v_new: int,

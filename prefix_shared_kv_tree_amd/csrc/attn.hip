@@ -54,8 +54,16 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "kernels.h"
+
+// Fixed device scratch for callers that cannot allocate (the partials of
+// pkvt_attn_decode_noalloc): kNoAllocScratchBytes bytes on every device the
+// library runs on, held until the process ends.  In host code the name
+// `scratch` is only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, once per device (pkvt::noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[pkvt::kNoAllocScratchBytes];
 
 namespace pkvt {
 namespace {
@@ -1031,6 +1039,26 @@ hipError_t launch_copy_words(const int32_t* src, int32_t* dst, int64_t n, hipStr
     const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
     copy_words_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s>>>(src, dst, n);
     return hipGetLastError();
+}
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        // the device address of this device's copy (dev is current)
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_merge(const MergeArgs& a, int D, hipStream_t s) {

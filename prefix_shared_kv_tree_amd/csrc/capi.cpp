@@ -434,6 +434,29 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* t, const void* d_meta, const vo
     return PKVT_OK;
 }
 
+pkvt_status pkvt_attn_decode_noalloc(const pkvt_tree* t, const void* d_meta, const void* q,
+                                     const void* k_pool, const void* v_pool, void* out,
+                                     float scale, void* stream) {
+    if (!t) return fail(PKVT_ERR_INVALID_ARG, "attn_decode_noalloc: tree is NULL");
+    if (!plan_current(t))
+        return fail(PKVT_ERR_STALE_PLAN, "attn_decode_noalloc: plan is older than the tree");
+    const size_t need = static_cast<size_t>(t->plan.n_slots) * t->tree.H * (t->tree.D + 2) *
+                        sizeof(float);
+    if (need > pkvt::kNoAllocScratchBytes)
+        return fail(PKVT_ERR_BUFFER_TOO_SMALL,
+                    "attn_decode_noalloc: the plan's partials need " + std::to_string(need) +
+                        " bytes, more than the library's fixed scratch of " +
+                        std::to_string(pkvt::kNoAllocScratchBytes) +
+                        " bytes (use pkvt_attn_decode with a workspace)");
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = pkvt::noalloc_scratch(&ws);
+        if (e != hipSuccess) return hip_fail(e, "attn_decode_noalloc: scratch address");
+    }
+    return pkvt_attn_decode_ex(t, d_meta, q, k_pool, v_pool, out, ws, need, scale, stream,
+                               nullptr, nullptr);
+}
+
 pkvt_status pkvt_kv_scatter(const pkvt_tree* t, void* k_pool, void* v_pool, const int64_t* slots,
                             const void* k_new, const void* v_new, int64_t n_tokens, void* stream) {
     if (!t || n_tokens < 0) return fail(PKVT_ERR_INVALID_ARG, "kv_scatter: bad arguments");

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cstddef>
 #include <cstdint>
 
 #include "shapes.h"
@@ -69,6 +70,12 @@ constexpr int kInlineSlots = 256;
 struct InlineSlots {
     int64_t slot[kInlineSlots];
 };
+
+// Bytes of the library's fixed device scratch (pkvt_attn_decode_noalloc).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+// Device address of the current device's scratch (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_attn(const AttnArgs& a, int D, int C, hipStream_t s);
 // units only, each row masked to the keys at positions <= a.qpos[row]
