@@ -14,7 +14,10 @@ from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkvt.so")
+# PKVT_LIB selects another build of the library (the sanitizer build of the
+# host code, for CPU tests); by default the in-tree libpkvt.so.
+LIB_PATH = os.environ.get("PKVT_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                      "libpkvt.so")
 
 PKVT_OK = 0
 STATUS_NAMES = {
