@@ -616,6 +616,14 @@ PAGE_DIVERGENCE = {
     (2048, 512): (145.41, 39.85), (2048, 1024): (107.37, 36.18), (2048, 2048): (70.33, 30.17),
     (4096, 512): (101.69, 21.04), (4096, 4096): (37.05, 15.12),
 }
+# Knowl 6 (b = 32, h = 32, d = 128, c = 64, fp16, A100): µs per attention kernel for n_p
+# context tokens of which the first n_s are shared -- (ChunkAttn, PagedAttn).  Context only.
+PAGE_KNOWL6 = {
+    (1024, 0): (332.50, 356.17), (1024, 512): (198.87, 355.88), (1024, 768): (131.21, 356.02),
+    (1024, 1024): (56.00, 355.44), (2048, 0): (655.44, 702.98), (2048, 1024): (384.37, 703.35),
+    (2048, 1536): (247.14, 702.90), (2048, 2048): (110.48, 703.72), (4096, 0): (1301.78, 1400.61),
+    (4096, 2048): (747.56, 1400.99), (4096, 3072): (477.66, 1400.30), (4096, 4096): (206.22, 1399.51),
+}
 # Knowl 9 (n_s = 2048, n_c = 64): ChunkAttn 10^3 tokens/s at the two ends of b in [16, 96].
 PAGE_BATCH = {16: 155.0, 96: 224.0}
 
@@ -703,6 +711,30 @@ def run_sweep(args):
             points.append(row)
         print(json.dumps({"sweep": "tokens", "b": 64, "private": "uniform [256, 1024]", "h": 32,
                           "d": 128, "c": 64, "dtype": "f16", "data": "synthetic, device N(0,1)",
+                          "points": points}), flush=True)
+        return
+    if args.sweep == "knowl6":
+        # the pages' microkernel grid: 32 sequences of n_p context tokens, the
+        # first n_s shared by all, one decode query each
+        points = []
+        for i, (n_p, n_s) in enumerate(sorted(PAGE_KNOWL6)):
+            row = {"n_p": n_p, "n_s": n_s}
+            for variant in ("tpp", "plain"):
+                t, info, unique = sweep_time(torch, B, W, 32, n_s, n_p - n_s, 3600 + i, variant,
+                                             args.sweep_steps, 10, ev)
+                row[f"{variant}_us_per_layer"] = round(t, 2)
+                if variant == "tpp":
+                    row["unique_kv_bytes"] = int(unique)
+                    row["effective_gbps"] = round(unique / (t * 1e-6) / 1e9, 1)
+                    row["frac_hbm_peak"] = round(unique / (t * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+                    row["plan"] = {k: info[k] for k in ("phase1_items", "wg_units", "tasks", "slots")}
+            row["speedup_vs_plain"] = round(row["plain_us_per_layer"] / row["tpp_us_per_layer"], 3)
+            ca, pa = PAGE_KNOWL6[(n_p, n_s)]
+            row["page_a100_us"] = {"chunkattn": ca, "pagedattn": pa}
+            print(json.dumps(row), file=sys.stderr, flush=True)
+            points.append(row)
+        print(json.dumps({"sweep": "knowl6", "b": 32, "h": 32, "d": 128, "c": 64, "dtype": "f16",
+                          "data": "synthetic, device N(0,1)", "steps_per_point": args.sweep_steps,
                           "points": points}), flush=True)
         return
     if args.sweep == "shard":
@@ -929,9 +961,10 @@ def main():
     ap.add_argument("--loop-churn", type=int, default=16,
                     help="a row gets a new sequence every this many decode-loop steps")
     ap.add_argument("--no-loop", action="store_true")
-    ap.add_argument("--sweep", choices=["divergence", "batch", "shapes", "shard", "tokens"],
-                    help="time the decode-throughput sweeps of the pages' divergence (Knowl 8) "
-                         "or batch-size (Knowl 9) experiments instead of the benchmark")
+    ap.add_argument("--sweep", choices=["divergence", "batch", "shapes", "shard", "tokens", "knowl6"],
+                    help="time the pages' microkernel grid (Knowl 6), the decode-throughput sweeps "
+                         "of the divergence (Knowl 8) or batch-size (Knowl 9) experiments, or the "
+                         "shape / head-share / token-matching sweeps instead of the benchmark")
     ap.add_argument("--sweep-steps", type=int, default=60)
     ap.add_argument("--prefill", action="store_true",
                     help="time prefix-aware prefill attention instead of the decode benchmark")

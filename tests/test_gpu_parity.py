@@ -259,7 +259,7 @@ def test_sweep_shapes_all_rows(b, n_s, private):
         print(f"[case]   all {b} rows err={err:.3e} info={ds.info}", flush=True)
         assert err <= TOL
         if variant == "tpp":
-            assert ds.info["wg_units"] > 0
+            assert ds.info["phase1_items"] > 0
         ds.close()
 
 
