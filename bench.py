@@ -576,9 +576,11 @@ def decode_loop(args, name, layers, static_us_layer):
             "tree_and_plan_per_step": round(tree_plan / n_steps, 1),
             "append": round(us["append"] / max(cnt["append"], 1), 1),
             "plan_full": round(us["plan_full"] / max(cnt["plan_full"], 1), 1),
+            "plan_patch": round(us["plan_patch"] / max(cnt["plan_patch"], 1), 1),
             "plan_refresh": round(us["plan_refresh"] / max(cnt["plan_refresh"], 1), 1),
             "join": round(us["join"] / max(cnt["join"], 1), 1),
-            "full_replans": cnt["plan_full"], "refreshes": cnt["plan_refresh"], "joins": cnt["join"],
+            "full_replans": cnt["plan_full"], "patches": cnt["plan_patch"],
+            "refreshes": cnt["plan_refresh"], "joins": cnt["join"],
         }
 
     # parity on sampled rows (every replaced row among them) at the last step

@@ -207,6 +207,15 @@ pkvt_status pkvt_tree_moves(const pkvt_tree* tree, int64_t* src, int64_t* dst, i
  * item share a workgroup, so its chunks are fetched once per CU).  By
  * default items are cut at the mean per-wave load, so no task is longer
  * than what a perfectly balanced wave would do.
+ *
+ * Re-planning the same batch (same q_order and options) is lazy (Knowl 5):
+ * when only sequence lengths changed, only the length table is rewritten;
+ * when the only structural changes since the last plan are decode appends
+ * that opened new leaf chunks, each such chunk is added to the end of its
+ * row's last (sequence-first) work item, in room the plan keeps there, and
+ * nothing else is re-planned; any other change (an arrival, a departure, a
+ * row whose room is used up or whose path ends in shared chunks, or 256
+ * patches in a row) builds the plan afresh.
  * ---------------------------------------------------------------------- */
 typedef struct {
     int32_t phase1_chunks;  /* max chunks per phase-1 item; 0 = derived from
@@ -242,6 +251,11 @@ typedef struct {
     int32_t wg_units;       /* workgroup units: phase-1 row blocks of 17..64
                                rows whose 4 waves share every K/V load through
                                LDS                                             */
+    int32_t last_update;    /* what the last pkvt_plan call did: 0 refreshed
+                               the sequence lengths only, 1 patched the plan
+                               for decode appends that opened new leaf chunks,
+                               2 built it afresh                               */
+    int32_t patches;        /* patches since the plan was last built           */
 } pkvt_plan_info;
 
 /* Build the plan for a batch.  opts may be NULL (defaults).  Reports the

@@ -52,7 +52,7 @@ class PlanInfo(C.Structure):
                 ("unique_tokens", C.c_int64), ("logical_tokens", C.c_int64),
                 ("structure_version", C.c_int32), ("tasks", C.c_int32),
                 ("phase1_split", C.c_int32), ("phase2_split", C.c_int32),
-                ("wg_units", C.c_int32)]
+                ("wg_units", C.c_int32), ("last_update", C.c_int32), ("patches", C.c_int32)]
 
 
 _i32p = C.POINTER(C.c_int32)
@@ -272,6 +272,13 @@ def pkvt_plan_info_get(tree: int) -> dict:
     s = PlanInfo()
     _check("pkvt_plan_info_get", load().pkvt_plan_info_get(tree, C.byref(s)))
     return {k: getattr(s, k) for k, _ in PlanInfo._fields_ if k != "reserved"}
+
+
+def pkvt_plan_last_update(tree: int) -> int:
+    """What the last pkvt_plan did: 0 lengths only, 1 patched, 2 rebuilt."""
+    s = PlanInfo()
+    _check("pkvt_plan_info_get", load().pkvt_plan_info_get(tree, C.byref(s)))
+    return s.last_update
 
 
 def pkvt_plan_blob(tree: int) -> np.ndarray:

@@ -170,6 +170,8 @@ void fill_info(const pkvt::Plan& p, pkvt_plan_info* out) {
     out->phase1_split = p.split1_chunks;
     out->phase2_split = p.split2_chunks;
     out->wg_units = p.n_units;
+    out->last_update = p.last_update;
+    out->patches = p.patches;
 }
 
 }  // namespace

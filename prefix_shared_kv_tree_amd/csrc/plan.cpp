@@ -177,6 +177,7 @@ private:
 
 struct Item {
     std::vector<int32_t> chunks;
+    int32_t k0 = -1;             // path index of the first chunk (a row's own items)
     int32_t key_base = 0;
     int32_t len_row = -1;
     int32_t tail = 0;            // keys missing from the last chunk when len_row < 0
@@ -294,6 +295,56 @@ static void write_seqlen(const Tree& t, Plan& plan) {
     plan.logical_tokens = logical;
 }
 
+// Follow the decode appends since the plan was built (the tree was changed
+// by nothing else): each row whose sequence opened new leaf chunks gets them
+// at the end of its last work item, in the room reserved after that item's
+// chunk ids.  Only the item's chunk count and ids change: the new chunks are
+// private (phase 2) and every other node keeps its coverage, so the depth-first
+// order, the items, the partial slots and the merge lists stay valid.  The
+// balance of the task lists drifts by at most kAppendSlack steps per task.
+// False (and nothing changed) when some row cannot be patched: its path ends
+// in phase-1 chunks, its room is used up, or its old last chunk is partial.
+static bool patch_appends(const Tree& t, Plan& plan) {
+    std::vector<int32_t> rows;
+    for (const auto& g : t.grown()) {
+        if (g.first <= plan.struct_version) continue;
+        const auto it = plan.pos_of_seq.find(g.second);
+        if (it != plan.pos_of_seq.end()) rows.push_back(it->second);
+    }
+    std::sort(rows.begin(), rows.end());
+    rows.erase(std::unique(rows.begin(), rows.end()), rows.end());
+    std::vector<int32_t>& blob = plan.blob;
+    const int32_t wbase = blob[kOffWaves], cbase = blob[kOffChunks];
+    for (const int32_t p : rows) {                           // check every row first
+        const int32_t w = plan.last_wave[p];
+        if (w < 0) return false;
+        const std::vector<int32_t>& path = t.find_seq(plan.dfs_seq[p])->path;
+        const int32_t n = static_cast<int32_t>(path.size());
+        const int32_t k0 = plan.last_k0[p];
+        const int32_t old_n = blob[wbase + 8 * w + 1];
+        if (n - k0 > plan.wave_cap[w] || n - k0 <= old_n) return false;
+        for (int32_t k = k0 + old_n - 1; k < n; ++k) {
+            const Node& x = t.node(path[k]);
+            if (k + 1 < n && x.fill != t.C) return false;         // key k must lie in chunk k / C
+            if (k >= k0 + old_n && x.refs != 1) return false;     // new chunks are private
+        }
+    }
+    for (const int32_t p : rows) {
+        const int32_t w = plan.last_wave[p];
+        const std::vector<int32_t>& path = t.find_seq(plan.dfs_seq[p])->path;
+        const int32_t n = static_cast<int32_t>(path.size());
+        const int32_t k0 = plan.last_k0[p];
+        int32_t* wd = &blob[wbase + 8 * w];
+        for (int32_t k = k0 + wd[1]; k < n; ++k) blob[cbase + wd[0] + (k - k0)] = path[k];
+        wd[1] = n - k0;
+    }
+    plan.serial += 1;
+    blob[kSerial] = static_cast<int32_t>(plan.serial & 0x7fffffff);
+    plan.struct_version = t.structure_version();
+    plan.patches += 1;
+    return true;
+}
+
 int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& in_opts,
               Plan& plan, std::string& err) {
     if (b < 1 || !q_order) {
@@ -335,10 +386,20 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     }
 
     // ---- same structure as the current plan: refresh lengths only ------------
-    if (plan.valid && plan.struct_version == t.structure_version() && plan.b == b &&
-        plan.opts == opts && std::equal(q_order, q_order + b, plan.q_order.begin())) {
+    const bool same_batch = plan.valid && plan.b == b && plan.opts == opts &&
+                            std::equal(q_order, q_order + b, plan.q_order.begin());
+    if (same_batch && plan.struct_version == t.structure_version()) {
         write_seqlen(t, plan);
         plan.len_version = t.length_version();
+        plan.last_update = 0;
+        return PKVT_OK;
+    }
+    // ---- only appends that opened leaf chunks since: patch the last items -----
+    if (same_batch && t.reshape_version() <= plan.struct_version && plan.patches < kMaxPatches &&
+        patch_appends(t, plan)) {
+        write_seqlen(t, plan);
+        plan.len_version = t.length_version();
+        plan.last_update = 1;
         return PKVT_OK;
     }
 
@@ -482,6 +543,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
                 const int32_t a = r0 + at[q];
                 const int32_t e = r0 + at[q + 1];
                 it.chunks.assign(path.begin() + a, path.begin() + e);
+                it.k0 = a;
                 it.key_base = static_cast<int32_t>(pos + static_cast<int64_t>(at[q]) * t.C);
                 it.len_row = (e == n) ? p : -1;
                 if (e < n) it.tail = t.C - t.node(path[e - 1]).fill;
@@ -627,8 +689,19 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     const int32_t n_waves = static_cast<int32_t>(waves.size());
     const int32_t n_units = static_cast<int32_t>(units.size());
     const int32_t n_tasks = static_cast<int32_t>(lane_tasks.size());
+    // a row's last item keeps room for kAppendSlack more chunk ids (patch_appends)
+    std::vector<int32_t> wave_cap(n_waves);
+    std::vector<int32_t> last_wave(b, -1), last_k0(b, -1);
+    for (int32_t w = 0; w < n_waves; ++w) {
+        const int32_t n = static_cast<int32_t>(wave_chunks[w]->size());
+        wave_cap[w] = waves[w].len_row >= 0 ? std::max(n, std::min(kMaxItemChunks, n + kAppendSlack)) : n;
+    }
+    for (const Item& it : items2)
+        if (it.len_row >= 0) last_k0[it.len_row] = it.k0;
+    for (int32_t w = 0; w < n_waves; ++w)
+        if (waves[w].len_row >= 0) last_wave[waves[w].len_row] = w;
     int32_t total_chunks = 0;
-    for (auto* l : wave_chunks) total_chunks += static_cast<int32_t>(l->size());
+    for (int32_t w = 0; w < n_waves; ++w) total_chunks += wave_cap[w];
     for (const Unit& u : units) total_chunks += static_cast<int32_t>(u.it->chunks.size());
     std::vector<int32_t> merge_rows;
     for (int32_t p = 0; p < b; ++p)
@@ -669,6 +742,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
             WaveDesc d = waves[w];
             d.chunk_off = coff;
             for (int32_t id : *wave_chunks[w]) blob[blob[kOffChunks] + coff++] = id;
+            coff += wave_cap[w] - static_cast<int32_t>(wave_chunks[w]->size());
             std::copy(reinterpret_cast<const int32_t*>(&d),
                       reinterpret_cast<const int32_t*>(&d) + 8, &blob[blob[kOffWaves] + w * 8]);
         }
@@ -740,6 +814,13 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     plan.unique_tokens = unique;
     plan.dfs_seq.resize(b);
     for (int32_t p = 0; p < b; ++p) plan.dfs_seq[p] = q_order[dfs_row[p]];
+    plan.last_wave = std::move(last_wave);
+    plan.last_k0 = std::move(last_k0);
+    plan.wave_cap = std::move(wave_cap);
+    plan.pos_of_seq.clear();
+    for (int32_t p = 0; p < b; ++p) plan.pos_of_seq[plan.dfs_seq[p]] = p;
+    plan.patches = 0;
+    plan.last_update = 2;
     write_seqlen(t, plan);
     return PKVT_OK;
 }

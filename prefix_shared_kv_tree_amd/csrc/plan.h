@@ -23,6 +23,7 @@
 
 #include <cstdint>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "shapes.h"
@@ -76,6 +77,8 @@ constexpr int32_t kDefaultWorkgroups = 512;  // 256 CUs x 2 resident workgroups
 constexpr int32_t kMaxItemChunks = 64;       // chunks per work item (one per wave lane)
 constexpr int32_t kUnitStepCost = 2;         // quarter steps per wave of a unit step (4 = a task step)
 constexpr int32_t kYoungSpeedPct = 60;       // speed of a compute unit's younger workgroup, % of the older
+constexpr int32_t kAppendSlack = 2;          // chunk ids reserved after a row's last item for appends
+constexpr int32_t kMaxPatches = 256;         // incremental patches before a plan is rebuilt anyway
 
 struct PlanOpts {
     int32_t phase1_chunks = 0;   // 0 = derived from the balanced per-lane load
@@ -116,6 +119,15 @@ struct Plan {
     int64_t unique_tokens = 0, logical_tokens = 0;
     std::vector<int32_t> dfs_seq;     // depth-first position -> sequence id (tests)
     PlanScratch scratch;
+    // Incremental patching: a decode append that opens a new leaf chunk adds
+    // that chunk to the end of its row's last work item, in room reserved
+    // after the item's chunk ids, instead of rebuilding the plan.
+    std::vector<int32_t> last_wave;   // depth-first position -> wave of its last item, -1 if none
+    std::vector<int32_t> last_k0;     // ... and the path index of that item's first chunk
+    std::vector<int32_t> wave_cap;    // chunk ids reserved per wave
+    std::unordered_map<int32_t, int32_t> pos_of_seq;   // sequence id -> depth-first position
+    int32_t patches = 0;              // patches since the plan was last built
+    int32_t last_update = 0;          // last make_plan: 0 lengths only, 1 patched, 2 rebuilt
 
     int32_t off(HeaderField f) const { return blob[f]; }
 };

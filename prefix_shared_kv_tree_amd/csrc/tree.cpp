@@ -172,7 +172,7 @@ int Tree::build(int32_t n_seqs, const int32_t* tokens, const int64_t* offsets,
         added.push_back(sid);
         seq_ids[s] = sid;
     }
-    if (n_seqs > 0) ++struct_version_;
+    if (n_seqs > 0) reshaped();
     return PKVT_OK;
 }
 
@@ -237,7 +237,15 @@ int Tree::append(int32_t n, const int32_t* seq_ids, const int32_t* tokens, int64
         s.len++;
     }
     if (n > 0) ++len_version_;
-    if (structural) ++struct_version_;
+    if (structural) {
+        ++struct_version_;
+        if (grown_.size() + log.size() > kMaxGrown) {
+            reshaped();                                 // too many to patch: plan afresh
+        } else {
+            for (const Step& st : log)
+                if (st.created) grown_.emplace_back(struct_version_, st.sid);
+        }
+    }
     return PKVT_OK;
 }
 
@@ -362,7 +370,7 @@ int Tree::build_tokens(int32_t n_seqs, const int32_t* tokens, const int64_t* off
         for (int32_t k = 0; k < nodes_[kv.first].fill; ++k)
             if (kv.second[k] >= 0) moves_.emplace_back(kv.second[k], static_cast<int64_t>(kv.first) * C + k);
     std::sort(moves_.begin(), moves_.end());
-    if (n_seqs > 0) ++struct_version_;
+    if (n_seqs > 0) reshaped();
     return PKVT_OK;
 }
 
@@ -378,7 +386,7 @@ int Tree::remove(int32_t seq_id, std::string& err) {
         Node& x = nodes_[*p];
         if (--x.refs == 0) free_node(*p);               // leaf first: children already gone
     }
-    ++struct_version_;
+    reshaped();
     return PKVT_OK;
 }
 

@@ -81,6 +81,15 @@ public:
 
     // Bumped on every change of which chunks form which paths.
     int64_t structure_version() const { return struct_version_; }
+    // The structure version of the last change other than decode appends
+    // that opened a new leaf chunk at the end of a sequence (arrival,
+    // departure): a plan at or after it can follow the appends since by
+    // extending the sequences' last work items (grown()).
+    int64_t reshape_version() const { return reshape_version_; }
+    // (structure version, sequence id) of every append that opened a new
+    // leaf chunk since reshape_version(), in order.
+    const std::vector<std::pair<int64_t, int32_t>>& grown() const { return grown_; }
+    static constexpr size_t kMaxGrown = 1 << 16;
     // Bumped on every decode append (sequence lengths change).
     int64_t length_version() const { return len_version_; }
 
@@ -92,7 +101,16 @@ private:
     int64_t next_created_ = 0;
     int64_t struct_version_ = 0;
     int64_t len_version_ = 0;
+    int64_t reshape_version_ = 0;
+    std::vector<std::pair<int64_t, int32_t>> grown_;
     std::vector<std::pair<int64_t, int64_t>> moves_;
+
+    // a structural change that is not an append opening a leaf chunk
+    void reshaped() {
+        ++struct_version_;
+        reshape_version_ = struct_version_;
+        grown_.clear();
+    }
 
     int build_tokens(int32_t n_seqs, const int32_t* tokens, const int64_t* offsets,
                      int32_t* seq_ids, int64_t* slots, std::string& err);

@@ -184,21 +184,22 @@ class HostDecoder:
 
     Per step: departures and arrivals of the step's joins (``pkvt_tree_remove``
     then ``pkvt_tree_build``), one ``pkvt_tree_append`` for the whole batch,
-    and ``pkvt_plan`` for the rows' live sequences.  The plan is rebuilt only
-    when the tree's structure changed (a leaf chunk filled and a new one was
-    allocated, or a sequence arrived or left); otherwise only the length
-    table is refreshed (ChunkAttention page, Knowl 5, lazy context copy).
-    Needs no GPU.  Host time per call is accumulated in ``us`` (microseconds)
-    and ``count``."""
+    and ``pkvt_plan`` for the rows' live sequences.  The library decides how
+    much to redo (ChunkAttention page, Knowl 5, lazy context copy): only the
+    length table when no chunk was opened; a patch of the rows' last items
+    when appends opened new leaf chunks; a full rebuild after an arrival or
+    departure.  Needs no GPU.  Host time per call is accumulated in ``us``
+    (microseconds) and ``count`` under "plan_refresh", "plan_patch" and
+    "plan_full"."""
 
     def __init__(self, tree: int, trace, seq_ids, **plan_kw):
         self.tree = tree
         self.tr = trace
         self.rows = np.array(seq_ids, dtype=np.int32)        # row -> live sequence id
         self.plan_kw = plan_kw
-        self.us = {"join": 0.0, "append": 0.0, "plan_full": 0.0, "plan_refresh": 0.0}
-        self.count = {"join": 0, "append": 0, "plan_full": 0, "plan_refresh": 0}
-        self.structural = True
+        self.us = {"join": 0.0, "append": 0.0, "plan_full": 0.0, "plan_patch": 0.0,
+                   "plan_refresh": 0.0}
+        self.count = {k: 0 for k in self.us}
 
     def _time(self, key, t0):
         import time
@@ -219,7 +220,6 @@ class HostDecoder:
             moves = B.pkvt_tree_moves(self.tree)
             self.rows[j.row] = ids[0]
             self._time("join", t0)
-            self.structural = True
             out.append((j, slots, moves))
         return out
 
@@ -229,9 +229,6 @@ class HostDecoder:
         t0 = time.perf_counter_ns()
         slots = B.pkvt_tree_append(self.tree, self.rows, self.tr.tokens[t])
         self._time("append", t0)
-        # a token at offset 0 of its chunk opened a new leaf chunk
-        if np.any(slots % self.tr.base.c == 0):
-            self.structural = True
         return slots
 
     def plan(self):
@@ -239,8 +236,10 @@ class HostDecoder:
         import time
         t0 = time.perf_counter_ns()
         mb, wb = B.pkvt_plan(self.tree, self.rows, **self.plan_kw)
-        self._time("plan_full" if self.structural else "plan_refresh", t0)
-        self.structural = False
+        el = time.perf_counter_ns() - t0
+        kind = ("plan_refresh", "plan_patch", "plan_full")[B.pkvt_plan_last_update(self.tree)]
+        self.us[kind] += el / 1e3
+        self.count[kind] += 1
         return mb, wb
 
 

@@ -70,6 +70,7 @@ def _check_tree(hd, wt):
     ("tiny", 60, 5, 1),
     ("c4", 70, 9, 23),
     ("c3", 70, 8, 23),
+    ("c3", 90, 45, 1),
 ])
 def test_host_decoder_follows_trace(name, steps, churn, check_every):
     w = W.make_config(name, with_kv=False)
@@ -105,8 +106,13 @@ def test_host_decoder_follows_trace(name, steps, churn, check_every):
                 PV.check_plan(plan, hd.rows, {int(s): p for s, p in zip(hd.rows, paths)},
                               {int(s): wt.seq_len(r) for r, s in enumerate(hd.rows)}, w.c,
                               heads=w.h)
-        assert hd.count["plan_full"] - full0 == structural_steps
+        assert hd.count["plan_full"] + hd.count["plan_patch"] - full0 == structural_steps
         assert hd.count["plan_refresh"] == steps - structural_steps
+        # appends that open leaf chunks are patched in; full rebuilds follow
+        # arrivals (or a row whose reserved room ran out)
+        if name != "tiny":
+            assert hd.count["plan_patch"] > 0
+            assert hd.count["plan_full"] - full0 <= len(tr.joins) + steps // w.c + 1
         assert hd.count["join"] == len(tr.joins)
         # every row leaves: the pool is whole again
         for s in hd.rows:
