@@ -933,6 +933,11 @@ def main():
     ap.add_argument("--config", default="c3", choices=["tiny", "c2", "c3", "c4", "c5", "phase1"])
     ap.add_argument("--phase1-chunks", type=int, default=0)
     ap.add_argument("--phase2-chunks", type=int, default=0)
+    ap.add_argument("--unit-rows", type=int, default=0,
+                    help="smallest phase-1 row block run as a workgroup unit (0 = default; "
+                         "above 64 runs every phase-1 row group as single-wave tasks)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer pools rotated (0 = max(2, ceil(2 GiB / unique KV bytes)))")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plain", action="store_true")
@@ -1007,6 +1012,8 @@ def main():
         b_tok = probe.h * probe.d * 2 * 2
         unique_bytes_est = W.unique_tokens(probe) * b_tok
         layers = max(2, math.ceil(2 * 2 ** 30 / unique_bytes_est))
+        if args.layers:
+            layers = args.layers            # diagnostic: fewer or more layer pools
         t0 = time.perf_counter()
         w = W.make_config(args.config, layers=layers)
         gen_s = time.perf_counter() - t0
@@ -1031,7 +1038,8 @@ def main():
         print(json.dumps({"config": args.config,
                           "decode_loop": decode_loop(args, args.config, layers, None)}), flush=True)
         return
-    ds = DecodeSetup(w, phase1_chunks=args.phase1_chunks, phase2_chunks=args.phase2_chunks)
+    ds = DecodeSetup(w, phase1_chunks=args.phase1_chunks, phase2_chunks=args.phase2_chunks,
+                     unit_rows=args.unit_rows)
     info = dict(ds.info)
     unique_bytes = info["unique_tokens"] * b_tok
     assert unique_bytes == unique_bytes_est, "tree and workload disagree on the stored tokens"
@@ -1049,7 +1057,7 @@ def main():
         B.pkvt_plan(ds.tree, ds.seq_ids, args.phase1_chunks + (k % 2) * 0, args.phase2_chunks,
                     2 + (k % 2))                     # alternate options to force a rebuild
         plan_full_us.append((time.perf_counter() - t0) * 1e6)
-    ds.replan(args.phase1_chunks, args.phase2_chunks, 0)
+    ds.replan(args.phase1_chunks, args.phase2_chunks, 0, unit_rows=args.unit_rows)
 
     # quick parity guard on a few sequences of layer 0
     from oracle import attention as A
@@ -1151,7 +1159,7 @@ def main():
         p_us = p_ms / args.steps * 1e3
         res["plain_us_per_layer"] = round(p_us, 2)
         res["speedup_vs_plain"] = round(p_us / us_layer, 3)
-        ds.replan(args.phase1_chunks, args.phase2_chunks, 0)
+        ds.replan(args.phase1_chunks, args.phase2_chunks, 0, unit_rows=args.unit_rows)
 
     if cpu is not None:
         res["cpu_baseline"] = cpu
