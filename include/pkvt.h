@@ -256,6 +256,14 @@ typedef struct {
                                for decode appends that opened new leaf chunks,
                                2 built it afresh                               */
     int32_t patches;        /* patches since the plan was last built           */
+    int32_t kernel;         /* 0: the two-phase kernel (workgroup units and
+                               single-wave tasks, 2 workgroups of 4 waves per
+                               compute unit); 1: the units-only kernel, chosen
+                               when every row's context lies in chunks shared
+                               by at least unit_rows rows and head_dim >= 128
+                               (one workgroup of 8 waves per compute unit:
+                               two groups of 4 waves take alternate steps of
+                               each unit, so two steps are in flight)          */
 } pkvt_plan_info;
 
 /* Build the plan for a batch.  opts may be NULL (defaults).  Reports the

@@ -52,7 +52,8 @@ class PlanInfo(C.Structure):
                 ("unique_tokens", C.c_int64), ("logical_tokens", C.c_int64),
                 ("structure_version", C.c_int32), ("tasks", C.c_int32),
                 ("phase1_split", C.c_int32), ("phase2_split", C.c_int32),
-                ("wg_units", C.c_int32), ("last_update", C.c_int32), ("patches", C.c_int32)]
+                ("wg_units", C.c_int32), ("last_update", C.c_int32), ("patches", C.c_int32),
+                ("kernel", C.c_int32)]
 
 
 _i32p = C.POINTER(C.c_int32)

@@ -152,9 +152,10 @@ __device__ __forceinline__ void qk(f4 (&s)[NT], const h8 (&kr)[NT][KS], const h8
 // 16tt + 4grp + i.  Returns P^T in fp16, pq[tt] = keys 16tt + 4grp .. +3 of
 // row col (the B-operand layout of the P V product), and rescales o to the
 // new running max.
-// kSkip (compute-bound prefill units): the key mask and the rescale of o
-// are skipped, wave-wide, on steps where no lane needs them (no lane's keys
-// end inside the step; no lane's running max moved).
+// kSkip (workgroup units, whose steps are bound by the instructions a wave
+// issues): the key mask and the rescale of o are skipped, wave-wide, on
+// steps where no lane needs them (no lane's keys end inside the step; no
+// lane's running max moved).
 // With a positive scale (the attention scale always is) the scores stay
 // unscaled: their max is scaled once and each weight is exp2 of one fused
 // multiply-add, s * scale - m.  Other scales scale the scores first.  The
@@ -439,9 +440,19 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 // images used in turn: the loads of step s + 1 fly while step s is computed,
 // with one barrier per step and no staging registers.  At head_dim 64 a V
 // load spans two padded 4-key groups, so the register path is kept.
-template <int D, int C, int RT, bool kCausal, int W = kWaves>
+//
+// P = 2 (decode units of the units-only kernel, head_dim >= 128): the
+// workgroup has 2 W waves in two phases of W; phase ph computes the unit's
+// steps ph, ph + 2, ph + 4, ... from its own pair of images (img0/img1 for
+// phase 0, img2/img3 for phase 1), so two steps are in flight and each SIMD
+// holds one wave of each phase, which hides the latency of one wave's step.
+// Both phases pass the same barriers (one per pair of steps).  At the end
+// phase 1 hands its running state (o, m, n) to phase 0 through LDS, which
+// folds it in with attn_reduce before writing the unit's partials.
+template <int D, int C, int RT, bool kCausal, int W = kWaves, int P = 1>
 __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wave, int lane,
-                                              char* img0, char* img1) {
+                                              char* img0, char* img1, char* img2 = nullptr,
+                                              char* img3 = nullptr) {
     constexpr int KS = D / 32, DT = D / 16, NT = Step<D>::kTiles;
     constexpr int kPer = Img<D>::kPieces / W;
     constexpr int NL = kPer / 64;
@@ -464,7 +475,9 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     const int n_rows = u[5];
     const int out = u[6];
     const int key_base = kCausal ? u[7] : 0;
-    const int role = wave;
+    static_assert(P == 1 || (P == 2 && RT == 1 && !kCausal), "two phases: decode units only");
+    const int role = P == 1 ? wave : wave % W;
+    const int phase = P == 1 ? 0 : wave / W;
     const bool computes = 16 * RT * role < n_rows;
     const int n_steps = (n_keys + Step<D>::kKeys - 1) / Step<D>::kKeys;
     const size_t slice = static_cast<size_t>(C) * D * 2;
@@ -478,17 +491,26 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     // the first tile this wave loads: K tiles go to waves 0 .. W/2 - 1, V
     // tiles to the others, TPW consecutive tiles each
     const int ta = NT == 1 ? 0 : TPW * (role % (W / 2));
-    // memory address of this lane's piece of load i of a step
+    // memory address of this lane's piece of load i of a step: a wave-uniform
+    // base (pool, chunk, key tile) plus the lane's offset inside the tile,
+    // which does not change from step to step and is computed once
+    uint32_t loff[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int j0 = role * kPer + i * 64;
+        const int rem = (j0 < KP ? j0 : j0 - KP) % (2 * D) + lane;
+        loff[i] = j0 < KP ? static_cast<uint32_t>(((rem >> 4) * C + (rem & 15)) * 16)
+                          : static_cast<uint32_t>(rem * 16);
+    }
     auto src = [&](int step, int i, const int (&id)[TPW]) {
         const int j0 = role * kPer + i * 64;
         const bool is_k = j0 < KP;
         const int jj = is_k ? j0 : j0 - KP;
         const int ts = tile_start<D>(step, jj / (2 * D), n_keys);
-        const int rem = jj % (2 * D) + lane;
         const size_t cbytes = static_cast<size_t>(id[i / (NL / TPW)]) * cstride;
-        const char* kp = kbase + cbytes + (static_cast<size_t>(rem >> 4) * C + ts % C + (rem & 15)) * 16;
-        const char* vp = vbase + cbytes + static_cast<size_t>((ts % C) / 4) * (D * 8) + rem * 16;
-        return reinterpret_cast<const h8*>(is_k ? kp : vp);
+        const char* base = is_k ? kbase + cbytes + static_cast<size_t>(ts % C) * 16
+                                : vbase + cbytes + static_cast<size_t>((ts % C) / 4) * (D * 8);
+        return reinterpret_cast<const h8*>(base + loff[i]);
     };
     // LDS byte offset of the piece a lane of load i writes (lane offset excluded
     // when lane_part is false)
@@ -503,18 +525,34 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     };
 
     h8 stg[kDirect ? 1 : NL];
+    // a wave loads either K or V pieces (all of its pieces are of one kind)
+    const bool kwave = role * kPer < KP;
+    int ldso[NL];                                 // LDS offset of load i (lane 0)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) ldso[i] = wave_uniform(dst(i, false));
     auto stage = [&](int step, char* img) {
-        int id[TPW];
+        if constexpr (kDirect) {
+            // per tile: one wave-uniform base (pool, chunk, key offset), then
+            // its loads at the lanes' fixed offsets
 #pragma unroll
-        for (int k = 0; k < TPW; ++k) id[k] = chunk_of(step, ta + k);
+            for (int k = 0; k < TPW; ++k) {
+                const int tt = ta + k;
+                const int ts = tile_start<D>(step, tt, n_keys);
+                const size_t cb = static_cast<size_t>(chunk_of(step, tt)) * cstride;
+                const char* base = kwave ? kbase + cb + static_cast<size_t>(ts % C) * 16
+                                         : vbase + cb + static_cast<size_t>((ts % C) / 4) * (D * 8);
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            if constexpr (kDirect)
-                __builtin_amdgcn_global_load_lds(src(step, i, id),
-                                                 (__attribute__((address_space(3))) void*)(img + dst(i, false)),
-                                                 16, 0, 0);
-            else
-                stg[i] = __builtin_nontemporal_load(src(step, i, id));
+                for (int i = k * (NL / TPW); i < (k + 1) * (NL / TPW); ++i)
+                    __builtin_amdgcn_global_load_lds(
+                        reinterpret_cast<const h8*>(base + loff[i]),
+                        (__attribute__((address_space(3))) void*)(img + ldso[i]), 16, 0, 0);
+            }
+        } else {
+            int id[TPW];
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) id[k] = chunk_of(step, ta + k);
+#pragma unroll
+            for (int i = 0; i < NL; ++i) stg[i] = __builtin_nontemporal_load(src(step, i, id));
         }
     };
     auto commit = [&](char* img) {
@@ -546,7 +584,49 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         l_run[rt] = 0.f;
     }
 
+    // One row tile per wave (decode units): every K fragment of the step is
+    // read before the first product and every V fragment before the softmax,
+    // so that the step waits for LDS twice instead of once per fragment pair
+    // (a decode unit's step is bound by its waves' latency, not by registers).
+    auto compute1 = [&](const char* img, int step) {
+        h8 kf[NT][KS];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[tt][ks] = *reinterpret_cast<const h8*>(img + ((tt * (D / 8) + 4 * ks + grp) * 16 + col) * 16);
+        f4 s[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+            s[tt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[tt][ks], qb[0][ks], s[tt], 0, 0, 0);
+        }
+        h4 vf[DT][NT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                vf[dt][tt] = *reinterpret_cast<const h4*>(img + Img<D>::kBytesK + (tt * 4 + grp) * Img<D>::kGroupV +
+                                                          (16 * dt + col) * 8);
+        h4 pq[NT];
+        softmax_step<NT, DT, true>(s, pq, o[0], m_run[0], l_run[0], step, lim[0], grp, a.scale_log2e);
+        if ((step + 1) * Step<D>::kKeys > n_keys) {           // V past the last key: zero
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    vf[dt][tt] = mask_v(vf[dt][tt], step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[0][dt] = pv_tile<NT>(o[0][dt], vf[dt], pq);
+    };
     auto compute = [&](const char* img, int step) {
+        if constexpr (RT == 1) {
+            compute1(img, step);
+            return;
+        }
         f4 s[RT][NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
@@ -564,8 +644,8 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         h4 pq[RT][NT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-            softmax_step<NT, DT, kCausal>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt], step, lim[rt],
-                                          grp, a.scale_log2e);
+            softmax_step<NT, DT, true>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt], step, lim[rt],
+                                       grp, a.scale_log2e);
         // V entries past the last key are zeroed on the last step only
         auto pv = [&](auto masked) {
 #pragma unroll
@@ -589,7 +669,52 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
             pv(Flag<false>{});
     };
 
-    if constexpr (kDirect) {
+    if constexpr (P == 2) {
+        static_assert(kDirect, "two phases need loads straight into LDS");
+        // iteration i: phase ph computes step 2i + ph from image (i % 2) of its
+        // pair while step 2i + 2 + ph loads into the other image of the pair
+        char* mine0 = phase ? img2 : img0;
+        char* mine1 = phase ? img3 : img1;
+        const int n_iter = (n_steps + 1) / 2;
+        if (phase < n_steps) stage(phase, mine0);
+        for (int it = 0; it < n_iter; ++it) {
+            const int step = 2 * it + phase;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's loads (see below)
+            __syncthreads();
+            char* cur = (it & 1) ? mine1 : mine0;
+            char* nxt = (it & 1) ? mine0 : mine1;
+            if (step + 2 < n_steps) stage(step + 2, nxt);
+            if (step < n_steps && computes) compute(cur, step);
+        }
+        __syncthreads();                     // every image has been read
+        // phase 1's (o, m, n) to phase 0: o as [role][dt][lane] f4, then (m, n)
+        constexpr int kOBytes = W * DT * 64 * 16;
+        static_assert(kOBytes + W * 64 * 8 <= 4 * Img<D>::kBytes, "state exchange fits the images");
+        f4* xo = reinterpret_cast<f4*>(img0);
+        float* xml = reinterpret_cast<float*>(img0 + kOBytes);
+        if (phase == 1 && computes) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) xo[(role * DT + dt) * 64 + lane] = o[0][dt];
+            xml[(role * 64 + lane) * 2] = m_run[0];
+            xml[(role * 64 + lane) * 2 + 1] = l_run[0];
+        }
+        __syncthreads();
+        if (phase == 0 && computes) {
+            const float mb = xml[(role * 64 + lane) * 2];
+            const float lb = xml[(role * 64 + lane) * 2 + 1];
+            const float mx = fmaxf(m_run[0], mb);     // finite: phase 0 has step 0
+            const float wa = fast_exp2(m_run[0] - mx);
+            const float wb = fast_exp2(mb - mx);      // 0 when phase 1 had no step
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[0][dt] = wa * o[0][dt] + wb * xo[(role * DT + dt) * 64 + lane];
+            l_run[0] = wa * l_run[0] + wb * lb;
+            m_run[0] = mx;
+            finish<D, DT>(a, o[0], m_run[0], l_run[0], qrow[0], out < 0 ? -1 : out + 16 * role, head,
+                          col, grp);
+        }
+        __syncthreads();                     // the next unit reuses the images
+        return;
+    } else if constexpr (kDirect) {
         // step s is computed from image s % 2 while step s + 1 loads into the other
         auto body = [&](char* cur, char* nxt, int step) {
             // The loads into LDS count as vector-memory operations: wait for this
@@ -802,6 +927,25 @@ void prefill_kernel(AttnArgs a) {
             a, meta(a.units) + 8 * (ufirst + k), wave, lane, img0, img1);
 }
 
+// Decode plans whose work is all workgroup units (every batch row's context
+// lies in chunks shared by at least unit_rows rows, head_dim >= 128): one
+// workgroup of 8 waves per compute unit runs its units in two phases of 4
+// waves (run_unit_wide, P = 2) from four LDS images.
+template <int D, int C>
+__global__ __launch_bounds__(64 * 2 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void unit_kernel(AttnArgs a) {
+    static_assert(D >= 128, "two-phase units load straight into LDS");
+    __shared__ __attribute__((aligned(16))) char lds[4 * Img<D>::kBytes];
+    const int wave = wave_uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
+    const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
+    for (int k = 0; k < ucount; ++k)
+        run_unit_wide<D, C, 1, false, kWaves, 2>(a, meta(a.units) + 8 * (ufirst + k), wave, lane, lds,
+                                                 lds + Img<D>::kBytes, lds + 2 * Img<D>::kBytes,
+                                                 lds + 3 * Img<D>::kBytes);
+}
+
 // Fold every partial of one (sequence, head) with attn_reduce and divide.
 // One wave per (sequence, head): the lanes first read the partials' (m, n)
 // in parallel and agree on the common max M; then every partial's o row is
@@ -961,6 +1105,18 @@ hipError_t attn_dc(const AttnArgs& a, hipStream_t s) {
 }
 
 template <int D, int C>
+hipError_t units_dc(const AttnArgs& a, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(a.n_wg);
+    if (grid == 0) return hipSuccess;
+    if constexpr (D >= 128) {
+        unit_kernel<D, C><<<dim3(grid), dim3(64 * 2 * kWaves), 0, s>>>(a);
+        return hipGetLastError();
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <int D, int C>
 hipError_t prefill_dc(const AttnArgs& a, hipStream_t s) {
     const unsigned grid = static_cast<unsigned>(a.n_wg);
     if (grid == 0) return hipSuccess;
@@ -1014,6 +1170,10 @@ hipError_t move_dc(const MoveArgs& a, hipStream_t s) {
 
 hipError_t launch_attn(const AttnArgs& a, int D, int C, hipStream_t s) {
     PKVT_DISPATCH(attn_dc, D, C, a, s)
+}
+
+hipError_t launch_units(const AttnArgs& a, int D, int C, hipStream_t s) {
+    PKVT_DISPATCH(units_dc, D, C, a, s)
 }
 
 hipError_t launch_prefill(const AttnArgs& a, int D, int C, hipStream_t s) {

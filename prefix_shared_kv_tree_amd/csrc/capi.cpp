@@ -172,6 +172,7 @@ void fill_info(const pkvt::Plan& p, pkvt_plan_info* out) {
     out->wg_units = p.n_units;
     out->last_update = p.last_update;
     out->patches = p.patches;
+    out->kernel = p.kernel;
 }
 
 }  // namespace
@@ -415,7 +416,7 @@ pkvt_status pkvt_attn_decode_ex(const pkvt_tree* t, const void* d_meta, const vo
     if (attn_start_event &&
         (e = hipEventRecord(static_cast<hipEvent_t>(attn_start_event), s)) != hipSuccess)
         return hip_fail(e, "attn_decode: event record");
-    e = pkvt::launch_attn(a, D, C, s);
+    e = p.kernel == 1 ? pkvt::launch_units(a, D, C, s) : pkvt::launch_attn(a, D, C, s);
     if (e != hipSuccess) return hip_fail(e, "attn_decode: attention kernel");
     if (attn_end_event && (e = hipEventRecord(static_cast<hipEvent_t>(attn_end_event), s)) != hipSuccess)
         return hip_fail(e, "attn_decode: event record");

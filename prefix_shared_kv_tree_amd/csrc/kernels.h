@@ -78,6 +78,8 @@ constexpr int kMaxDevices = 64;
 hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_attn(const AttnArgs& a, int D, int C, hipStream_t s);
+// units-only decode plans (head_dim >= 128): 8-wave workgroups, one per CU
+hipError_t launch_units(const AttnArgs& a, int D, int C, hipStream_t s);
 // units only, each row masked to the keys at positions <= a.qpos[row]
 hipError_t launch_prefill(const AttnArgs& a, int D, int C, hipStream_t s);
 // slots come from is.slot instead of a.slots (a.n_tokens <= kInlineSlots)

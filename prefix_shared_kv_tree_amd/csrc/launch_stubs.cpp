@@ -8,6 +8,7 @@
 namespace pkvt {
 
 hipError_t launch_attn(const AttnArgs&, int, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_units(const AttnArgs&, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_prefill(const AttnArgs&, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_scatter_inline(const ScatterArgs&, const InlineSlots&, int, int, hipStream_t) {
     return hipErrorNoDevice;

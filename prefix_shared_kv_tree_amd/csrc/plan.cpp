@@ -191,7 +191,8 @@ struct Item {
 // compute unit (g >= G/2) runs at kYoungSpeedPct % speed.  Ties go to the
 // older class, then to the lower workgroup index.
 void assign_units(const std::vector<int64_t>& cost, int32_t G,
-                  std::vector<std::vector<int32_t>>& wg_units, std::vector<int64_t>& wg_load) {
+                  std::vector<std::vector<int32_t>>& wg_units, std::vector<int64_t>& wg_load,
+                  int32_t young_pct = kYoungSpeedPct) {
     wg_units.assign(G, {});
     wg_load.assign(G, 0);
     std::vector<int32_t> order(cost.size());
@@ -208,7 +209,7 @@ void assign_units(const std::vector<int64_t>& cost, int32_t G,
         int64_t best = 0;
         for (int c = 0; c < 2; ++c) {
             if (q[c].empty()) continue;
-            const int64_t fin = (q[c].min_load() + cost[ui]) * 100 / (c ? kYoungSpeedPct : 100);
+            const int64_t fin = (q[c].min_load() + cost[ui]) * 100 / (c ? young_pct : 100);
             if (cls < 0 || fin < best) {
                 cls = c;
                 best = fin;
@@ -446,6 +447,21 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     for (size_t s = 0; s < segs.size(); ++s)
         for (int32_t x : segs[s]) seg_keys[s] += t.node(x).fill;
 
+    // ---- units-only plans -----------------------------------------------------------
+    // When every row's whole context is shared by at least unit_rows rows (no
+    // sequence-first work and no single-wave phase-1 groups) and head_dim >=
+    // 128, the plan runs on the units-only kernel: one workgroup of 8 waves
+    // per compute unit (G / 2 of them), each unit computed by two phases of 4
+    // waves that take alternate steps.  Items are then cut so that there are
+    // about as many units as workgroups (subject to the partial-cost floor).
+    bool units_only = t.D >= 128 && G >= 2 && !segs.empty();
+    for (int32_t p = 0; p < b && units_only; ++p)
+        units_only = k0[p] == static_cast<int32_t>(seqs[dfs_row[p]]->path.size());
+    for (size_t s = 0; s < segs.size() && units_only; ++s)
+        for (const int32_t rb : row_blocks(seg_range[s].j - seg_range[s].i, opts.unit_rows))
+            units_only = units_only && rb >= opts.unit_rows;
+    const int32_t Gk = units_only ? G / 2 : G;        // workgroups of the kernel that runs the plan
+
     // ---- item size ----------------------------------------------------------------
     // T = the mean per-wave load in 64-key steps with nothing cut (a unit
     // step counted at its cost relative to a single-wave step).  Phase-1
@@ -491,6 +507,16 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     // the kernel holds a task's chunk ids one per lane of a 64-lane wave
     s1 = std::min(s1, kMaxItemChunks);
     s2 = std::min(s2, kMaxItemChunks);
+    // units-only: unit steps spread evenly over the Gk workgroups
+    int32_t s1_units_only = kMaxItemChunks;
+    if (units_only) {
+        int64_t unit_steps = 0;
+        for (size_t s = 0; s < segs.size(); ++s)
+            unit_steps += steps_of(seg_keys[s]) *
+                          static_cast<int64_t>(row_blocks(seg_range[s].j - seg_range[s].i, opts.unit_rows).size());
+        unit_steps *= t.H;
+        s1_units_only = std::min(kMaxItemChunks, steps_to_chunks((unit_steps + Gk - 1) / Gk, t.C));
+    }
 
     // ---- 3. items ------------------------------------------------------------------
     std::vector<Item> items1;
@@ -512,7 +538,7 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         int32_t limit = s1;
         if (opts.phase1_chunks == 0) {
             const int64_t rows = seg_range[s].j - seg_range[s].i;
-            if (rows >= opts.unit_rows) limit = s1_unit;
+            if (rows >= opts.unit_rows) limit = units_only ? s1_units_only : s1_unit;
             const int64_t need = (8 * rows * (t.D + 2) * 4 + 4LL * t.C * t.D - 1) / (4LL * t.C * t.D);
             limit = static_cast<int32_t>(std::min<int64_t>(kMaxItemChunks, std::max<int64_t>(limit, need)));
         }
@@ -635,8 +661,10 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
             std::vector<int64_t> cost(units.size());
             for (size_t i = 0; i < units.size(); ++i) cost[i] = units[i].cost;
             std::vector<int64_t> wg_load;
-            assign_units(cost, G, wg_units, wg_load);
-            for (int32_t g = 0; g < G; ++g)
+            // units-only: one workgroup per compute unit, all at the same speed
+            assign_units(cost, Gk, wg_units, wg_load, units_only ? 100 : kYoungSpeedPct);
+            wg_units.resize(G);
+            for (int32_t g = 0; g < Gk; ++g)
                 for (int32_t k = 0; k < kWavesPerWg; ++k) load[g * kWavesPerWg + k] = wg_load[g];
         }
         // single-wave tasks x heads, longest first; equal costs keep the
@@ -780,7 +808,8 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     blob[kMagic] = kPlanMagic;
     blob[kB] = b;
     blob[kNWaves] = n_waves;
-    blob[kNWg] = G;
+    blob[kNWg] = Gk;
+    blob[kKernel] = units_only ? 1 : 0;
     blob[kNTasks] = n_tasks;
     blob[kNUnits] = n_units;
     blob[kNSlots] = n_slots;
@@ -803,7 +832,8 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
     plan.phase1_items = static_cast<int32_t>(items1.size());
     plan.phase2_items = static_cast<int32_t>(items2.size());
     plan.n_waves = n_waves;
-    plan.n_wg = G;
+    plan.n_wg = Gk;
+    plan.kernel = units_only ? 1 : 0;
     plan.n_tasks = n_tasks;
     plan.n_units = n_units;
     plan.n_slots = n_slots;

@@ -66,7 +66,8 @@ static_assert(sizeof(UnitDesc) == 32, "UnitDesc is 8 int32");
 enum HeaderField {
     kMagic = 0, kSerial, kB, kNWaves, kNWg, kNTasks, kNSlots, kNMerge,
     kOffLists, kOffTasks, kOffWaves, kOffChunks, kOffRows, kOffMerge, kOffMptr, kOffMslots,
-    kOffSeqlen, kTotalWords, kNUnits, kOffWgUnits, kOffUnits, kOffQpos, kHeaderWords = 24
+    kOffSeqlen, kTotalWords, kNUnits, kOffWgUnits, kOffUnits, kOffQpos, kKernel,
+    kHeaderWords = 24
 };
 constexpr int32_t kPlanMagic = 0x504b5657;   // "PKVW": lane lists + workgroup units
 constexpr int32_t kRowsPerUnit = 64;         // query rows of one workgroup-unit block
@@ -113,6 +114,7 @@ struct Plan {
     std::vector<int32_t> blob;
     // summary
     int32_t phase1_items = 0, phase2_items = 0, n_waves = 0, n_wg = 0, n_tasks = 0, n_units = 0;
+    int32_t kernel = 0;               // 0: attn_kernel; 1: unit_kernel (units-only decode plans)
     int32_t n_slots = 0, n_merge = 0;
     int32_t split1_chunks = 0, split2_chunks = 0;   // the item sizes actually used
     int32_t shared_chunks = 0;
