@@ -189,6 +189,14 @@ KERNEL_SRCS = [os.path.join(ROOT, "prefix_shared_kv_tree_amd", "csrc", f)
                for f in ("attn.hip", "kernels.h", "shapes.h", "plan.cpp", "plan.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 ATTN_KERNEL = "attn_kernel"
+UNIT_KERNEL = "unit_kernel"
+
+
+def kernel_of(info):
+    """Name of the kernel that runs a decode plan: the units-only kernel for
+    plans whose rows are all shared (plan info "kernel" = 1), else the
+    two-phase attention kernel."""
+    return UNIT_KERNEL if info.get("kernel") == 1 else ATTN_KERNEL
 
 
 def kernel_source_sha256():
@@ -223,8 +231,11 @@ def profile_traffic(config):
     """HBM bytes per attention launch from the committed counter summary of
     this workload, or None when there is none or the kernel source changed
     since the counters were taken."""
-    path = os.path.join(PROFILES, f"{ATTN_KERNEL}_{config}_pmc.md")
-    if not os.path.exists(path):
+    for name in (ATTN_KERNEL, UNIT_KERNEL):
+        path = os.path.join(PROFILES, f"{name}_{config}_pmc.md")
+        if os.path.exists(path):
+            break
+    else:
         return None
     text = open(path).read()
     start = text.find("```json pmc-summary")
@@ -258,9 +269,10 @@ def summarize_pmc(args):
     B.pkvt_plan(t, ids)
     info = B.pkvt_plan_info_get(t)
     B.pkvt_tree_destroy(t)
+    kname = kernel_of(info)
     unique, attn_bytes = algorithmic_bytes(w, info)
-    fetch, n_fetch = _counter_means(args.fetch_csv, ATTN_KERNEL)
-    write, n_write = _counter_means(args.write_csv, ATTN_KERNEL)
+    fetch, n_fetch = _counter_means(args.fetch_csv, kname)
+    write, n_write = _counter_means(args.write_csv, kname)
     copy_bytes = args.copy_mib * 2 ** 20
     cf, ncf = _counter_means(args.fetch_csv, "neg_kernel")
     cw, ncw = _counter_means(args.write_csv, "neg_kernel")
@@ -274,7 +286,7 @@ def summarize_pmc(args):
     write_b = write["WRITE_SIZE"] * 1024 * f_write
     rec = {
         "workload": args.config,
-        "kernel": f"{ATTN_KERNEL}<{w.d},{w.c}>",
+        "kernel": f"{kname}<{w.d},{w.c}>",
         "kernel_source_sha256": kernel_source_sha256(),
         "dispatches": {"fetch": n_fetch.get("FETCH_SIZE", 0), "write": n_write.get("WRITE_SIZE", 0)},
         "fetch_kib_raw": round(fetch["FETCH_SIZE"], 1),
@@ -291,12 +303,12 @@ def summarize_pmc(args):
     if args.trace_csv:
         import csv as _csv
         for r in _csv.DictReader(open(args.trace_csv)):
-            if ATTN_KERNEL in r["Name"]:
+            if kname in r["Name"]:
                 kernel_ns = float(r["AverageNs"])
                 rec["kernel_avg_us_trace"] = round(kernel_ns / 1e3, 2)
                 rec["traffic_gbps_at_trace_avg"] = round(rec["traffic_bytes"] / kernel_ns, 1)
     if args.mfma_csv:
-        m, _ = _counter_means(args.mfma_csv, ATTN_KERNEL)
+        m, _ = _counter_means(args.mfma_csv, kname)
         rec["mfma_counters"] = {k: round(v, 1) for k, v in m.items()}
         if "SQ_INSTS_VALU_MFMA_MOPS_F16" in m:
             # the counter counts f16 MFMA math operations divided by 512
@@ -348,14 +360,21 @@ def summarize_trace(args):
     """Turn a rocprofv3 --kernel-trace --stats CSV (and the bench JSON line
     printed by the same run) into the committed kernel-trace summary."""
     import csv as _csv
+    from prefix_shared_kv_tree_amd import binding as B
     from prefix_shared_kv_tree_amd import workloads as W
+    w = W.make_config(args.config, with_kv=False)
+    t = B.pkvt_tree_create(w.h, w.d, w.c, 1 << 20)
+    ids, _ = B.pkvt_tree_build(t, w.all_seq_tokens())
+    B.pkvt_plan(t, ids)
+    kname = kernel_of(B.pkvt_plan_info_get(t))
+    B.pkvt_tree_destroy(t)
     rows = list(_csv.DictReader(open(args.trace_csv)))
     bench = None
     if args.bench_log:
         for line in open(args.bench_log):
             if line.startswith('{"metric"'):
                 bench = json.loads(line)
-    out = [f"# {ATTN_KERNEL} -- kernel trace, workload {args.config}", "",
+    out = [f"# {kname} -- kernel trace, workload {args.config}", "",
            f"Workload: {W.CONFIG_DESCRIPTIONS[args.config]}.", "",
            "Commands (repository root as $R):", "", "```"] + list(args.command) + [
            "```", "",
@@ -366,14 +385,14 @@ def summarize_trace(args):
         name = name if len(name) <= 70 else name[:67] + "..."
         out.append(f"| `{name}` | {r['Calls']} | {r['TotalDurationNs']} | {float(r['AverageNs']):.0f} | "
                    f"{r['Percentage']} | {r['MinNs']} | {r['MaxNs']} | {float(r['StdDev']):.0f} |")
-    attn = [r for r in rows if ATTN_KERNEL in r["Name"]][0]
+    attn = [r for r in rows if kname in r["Name"]][0]
     avg = float(attn["AverageNs"]) / 1e3
     if bench:
         out += ["", f"Same run, bench.py's own HIP-event figures: us_per_layer = {bench['us_per_layer']}, "
                 f"attention kernel (events recorded right before and after it on its stream) = "
                 f"{bench['attn_kernel_us']} us, roofline achieved = {bench['roofline']['achieved']} GB/s "
                 f"of {bench['roofline']['peak']} GB/s.",
-                f"rocprofv3 average for {ATTN_KERNEL}: {avg:.2f} us; the event figure is within "
+                f"rocprofv3 average for {kname}: {avg:.2f} us; the event figure is within "
                 f"{abs(bench['attn_kernel_us'] - avg) / avg * 100:.1f} % of it."]
     print("\n".join(out + [""]))
 
@@ -912,6 +931,7 @@ def config_entry(name, args, ev, stream):
         "tpp_over_plain_time": round(us / p_us, 4),
         "same_plan_as_plain": info["tasks"] == plain_plan["tasks"] and info["wg_units"] == plain_plan["wg_units"]
                            and info["phase1_items"] == 0,
+        "kernel": kernel_of(info),
         "plan": {k: info[k] for k in ("phase1_items", "phase2_items", "wg_units", "tasks", "slots",
                                        "merge_rows")},
         "parity_max_abs_err_sampled": parity,
@@ -1134,7 +1154,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic["traffic_bytes"] if traffic else None,
-            "kernel": f"attn_kernel<{D},{w.c}>",
+            "kernel": f"{kernel_of(info)}<{D},{w.c}>",
             # achieved = algorithmic_bytes_per_launch / duration_us: the distinct
             # stored KV bytes plus Q and the kernel's partial / O writes, over the
             # mean HIP-event time of the attention kernel alone (events recorded
@@ -1146,6 +1166,10 @@ def main():
             "unique_kv_bytes": int(unique_bytes),
             "frac_unique_kv": round(unique_bytes / (attn_avg_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "rocprof_avg_us": traffic.get("kernel_avg_us_trace") if traffic else None,
+            # frac over the committed rocprofv3 kernel average instead of the events
+            "frac_at_rocprof_avg": (round(attn_bytes / (traffic["kernel_avg_us_trace"] * 1e-6) / 1e9
+                                          / HBM_PEAK_GBPS, 4)
+                                    if traffic and traffic.get("kernel_avg_us_trace") else None),
         },
         "workload_gen_s": round(gen_s, 1),
         # a counter-collection run calibrates on its own copy's dispatches
