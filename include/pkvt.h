@@ -71,7 +71,14 @@ typedef struct pkvt_tree pkvt_tree;
  * chunk, head j's slice starts at j*c*d and is laid out for the gfx950
  * matrix cores, not as a plain [c][d] matrix:
  *   K slice: [d/8][c][8]  -- element (token t, dim x) at ((x/8)*c + t)*8 + x%8
- *   V slice: [c/4][d][4]  -- element (token t, dim x) at ((t/4)*d + x)*4 + t%4
+ *   V slice: blocks of F tokens one after the other, F = 32 (16 when
+ *            head_dim is 256 or c is 16); a block is [d/16][F/8][16][8]:
+ *            element (token t, dim x), with w = t%F, at
+ *              (t-w)*d + (((x/16)*(F/8) + g)*16 + x%16)*8 + e
+ *            where for F = 32: g = (w%16)/4, e = (w/16)*4 + w%4 (tokens
+ *            4g..4g+3 and 16+4g..16+4g+3 share one 8-element run, the
+ *            operand order of the matrix cores), and for F = 16: g = w/8,
+ *            e = w%8
  * Callers never compute these offsets: pkvt_kv_scatter writes tokens given
  * in natural [token][head][dim] order.  pkvt_pool_bytes gives the size of
  * ONE pool (K or V) for one layer.

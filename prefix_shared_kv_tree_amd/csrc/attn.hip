@@ -39,12 +39,15 @@
 // 15 of the 16 MFMA columns idle; that costs nothing measurable, because a
 // decode step does ~1 FLOP per byte while the matrix cores sustain ~300, and
 // it keeps both phases on the same streaming loop.  The pool layouts are
-// chosen so that the A-operand fragments are whole 16-byte (K) and 8-byte (V)
-// pieces and 16 consecutive lanes read 256 (K) or 128 (V) consecutive bytes:
+// chosen so that the A-operand fragments are whole 16-byte pieces and 16
+// consecutive lanes read 256 consecutive bytes:
 //   K slice [d/8][c][8]: the 8 dims a lane needs for one key are contiguous,
 //                        and consecutive keys are 16 bytes apart;
-//   V slice [c/4][d][4]: 4 consecutive keys of one dim are contiguous, and
-//                        consecutive dims are 8 bytes apart.
+//   V slice, per 32-key block (16 at head_dim 256 or chunk 16):
+//                        [d/16][4 groups][16][8]: 8 keys of one dim are
+//                        contiguous, consecutive dims 16 bytes apart, and
+//                        the keys of a group are those of one lane group of
+//                        the P V instruction (VLay below).
 // The online softmax (max, exp2, rescale) runs in fp32 on the S^T fragments;
 // P is rounded to fp16 for the PV product and n sums those rounded weights.
 // Scores are scaled by scale*log2(e) in fp32 (inside the exponent's FMA) so
@@ -54,6 +57,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 #include <mutex>
 
 #include "kernels.h"
@@ -74,7 +78,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;          // waves per workgroup
-constexpr int kVPad = 128;         // LDS padding after each 4-key group of a V image
 
 // Keys per step of the streaming loop: 4 tiles of 16 keys up to head_dim
 // 128; one tile at head_dim 256, where a step of K and V in registers next
@@ -134,6 +137,55 @@ template <int D, int C>
 __device__ __forceinline__ int tile_id(int ids, int step, int tt, int n_valid) {
     return __builtin_amdgcn_readlane(ids, min((step * Step<D>::kKeys + 16 * tt) / C, (n_valid - 1) / C));
 }
+
+// V pool order.  A (chunk, head) slice of V is a run of fragments, 32 keys
+// each (paired) or 16, stored one after the other.  Inside a fragment the
+// keys are split into 8-key groups (4 or 2), and the fragment is
+// [D/16 dim tiles][group][16 dims][8 keys]: a 16-byte piece holds 8 keys of
+// one dim, and the pieces that one P V instruction takes for one dim tile
+// (every group, 16 dims) are one contiguous run of 1 KiB (512 B unpaired).
+// Paired (steps of 4 tiles, chunks of at least 32 keys): group g of a block
+// holds keys 4g .. 4g+3 of its first 16-key tile and then keys 4g .. 4g+3
+// of its second -- the 8 keys whose weights lane group g holds for the
+// 32-key P V instruction -- so that operand is one 16-byte load and needs
+// no register shuffles.  Otherwise (head_dim 256, whose steps are one tile;
+// chunks of 16, where a block would span two chunks) a fragment is one
+// 16-key tile in key order, and P V goes tile by tile through the 16-key
+// instruction, whose operand is half a piece.
+template <int D, int C>
+struct VLay {
+    static constexpr int NT = Step<D>::kTiles;
+    static constexpr bool kPaired = NT > 1 && C >= 32;
+    static constexpr int kFrags = kPaired ? NT / 2 : NT;      // per 16-dim tile and step
+    static constexpr int kFragKeys = kPaired ? 32 : 16;
+    static constexpr int kGroups = kFragKeys / 8;             // 8-key groups per fragment
+    using Frag = std::conditional_t<kPaired, h8, h4>;
+    // element offset (halves) of key t, dim x in a slice
+    __host__ __device__ static constexpr int elem(int t, int x) {
+        const int w = t % kFragKeys;
+        const int g = kPaired ? (w & 15) >> 2 : w >> 3;
+        const int e = kPaired ? (w >> 4) * 4 + (w & 3) : w & 7;
+        return (t - w) * D + (((x >> 4) * kGroups + g) * 16 + (x & 15)) * 8 + e;
+    }
+    // Where the V of key tile tt of a step is read from, as a key: the V of
+    // keys p .. p+15 (p a multiple of 16) is the contiguous 32 D bytes from
+    // p * 2 D -- a whole fragment, or the first or second half of a paired
+    // one.  Fragments are clamped like tile_start, to the last one that
+    // holds a valid key.
+    __device__ static int tile_src(int step, int tt, int n_valid) {
+        if constexpr (kPaired) {
+            const int key = step * Step<D>::kKeys + 32 * (tt >> 1);
+            const int last = (n_valid - 1) & ~31;
+            return (key < last ? key : last) + 16 * (tt & 1);
+        } else {
+            return tile_start<D>(step, tt, n_valid);
+        }
+    }
+    // a lane's part of a fragment: its 8-position group within the fragment,
+    // and the byte offset inside the 16-byte piece
+    __device__ static int lane_group(int grp) { return kPaired ? grp : grp >> 1; }
+    __device__ static int lane_byte(int grp) { return kPaired ? 0 : (grp & 1) * 8; }
+};
 
 // S^T = K Q^T for the keys of a step: tile tt = keys 16tt .. 16tt+15.
 template <int NT, int KS>
@@ -216,42 +268,64 @@ __device__ __forceinline__ h4 mask_v(h4 v, int key, int n_valid) {
     return __builtin_bit_cast(h4, __builtin_bit_cast(unsigned long long, v) & mk);
 }
 
-// O^T += V^T P^T for one 16-dim tile: v[tt] holds V of dim 16dt + col for
-// the keys of tile tt that the lane's P covers (16tt + 4grp .. +3).  Pairs of
-// tiles go through the 32-key instruction (the key order inside a pair is
-// permuted alike in both operands); a single tile through the 16-key one.
-template <int NT>
-__device__ __forceinline__ f4 pv_tile(f4 o, const h4 (&v)[NT], const h4 (&pq)[NT]) {
-    if constexpr (NT == 1) {
-        o = __builtin_amdgcn_mfma_f32_16x16x16f16(v[0], pq[0], o, 0, 0, 0);
-    } else {
+// A paired V piece: positions 0..3 are keys key_a .. key_a+3, positions 4..7
+// are keys key_a+16 .. key_a+19.
+__device__ __forceinline__ h8 mask_v(h8 v, int key_a, int n_valid) {
+    const h4 lo = mask_v(__builtin_shufflevector(v, v, 0, 1, 2, 3), key_a, n_valid);
+    const h4 hi = mask_v(__builtin_shufflevector(v, v, 4, 5, 6, 7), key_a + 16, n_valid);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Zero the V entries of the lane's part of fragment f of a step (first key
+// key0) that lie past n_valid.
+template <int D, int C>
+__device__ __forceinline__ typename VLay<D, C>::Frag mask_frag(typename VLay<D, C>::Frag v, int key0,
+                                                               int f, int grp, int n_valid) {
+    if constexpr (VLay<D, C>::kPaired)
+        return mask_v(v, key0 + 32 * f + 4 * grp, n_valid);
+    else
+        return mask_v(v, key0 + 16 * f + 4 * grp, n_valid);
+}
+
+// O^T += V^T P^T for one 16-dim tile: v[f] is the lane's part of V fragment
+// f for dim 16dt + col, pq[tt] the lane's weights for keys 16tt + 4grp ..
+// +3.  Paired fragments go through the 32-key instruction (the weights of a
+// block's two tiles side by side, in the order of the V piece), single
+// tiles through the 16-key one.
+template <int D, int C>
+__device__ __forceinline__ f4 pv_frags(f4 o, const typename VLay<D, C>::Frag (&v)[VLay<D, C>::kFrags],
+                                       const h4 (&pq)[Step<D>::kTiles]) {
 #pragma unroll
-        for (int hs = 0; hs < NT / 2; ++hs) {
-            const h8 va = __builtin_shufflevector(v[2 * hs], v[2 * hs + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-            const h8 pb = __builtin_shufflevector(pq[2 * hs], pq[2 * hs + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, o, 0, 0, 0);
+    for (int f = 0; f < VLay<D, C>::kFrags; ++f) {
+        if constexpr (VLay<D, C>::kPaired) {
+            const h8 pb = __builtin_shufflevector(pq[2 * f], pq[2 * f + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(v[f], pb, o, 0, 0, 0);
+        } else {
+            o = __builtin_amdgcn_mfma_f32_16x16x16f16(v[f], pq[f], o, 0, 0, 0);
         }
     }
     return o;
 }
 
 // softmax_step, then the PV product with a whole step of V in registers.
-template <int NT, int DT>
-__device__ __forceinline__ void softmax_pv(f4 (&s)[NT], h4 (&vr)[DT][NT], f4 (&o)[DT],
-                                           float& m_run, float& l_run, int step, int n_valid,
-                                           int grp, float scale_log2e) {
+template <int D, int C>
+using VStep = typename VLay<D, C>::Frag[D / 16][VLay<D, C>::kFrags];   // [dim tile][fragment]
+
+template <int D, int C, int NT = Step<D>::kTiles, int DT = D / 16>
+__device__ __forceinline__ void softmax_pv(f4 (&s)[NT], VStep<D, C>& vr, f4 (&o)[DT], float& m_run,
+                                           float& l_run, int step, int n_valid, int grp, float scale_log2e) {
     h4 pq[NT];
     softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, n_valid, grp, scale_log2e);
     const int key0 = step * 16 * NT;
     if (key0 + 16 * NT > n_valid) {
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+        for (int f = 0; f < VLay<D, C>::kFrags; ++f)
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-                vr[dt][tt] = mask_v(vr[dt][tt], key0 + 16 * tt + 4 * grp, n_valid);
+                vr[dt][f] = mask_frag<D, C>(vr[dt][f], key0, f, grp, n_valid);
     }
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = pv_tile<NT>(o[dt], vr[dt], pq);
+    for (int dt = 0; dt < DT; ++dt) o[dt] = pv_frags<D, C>(o[dt], vr[dt], pq);
 }
 
 // End of a task for query row col (lane group grp holds dims 16dt + 4grp ..):
@@ -288,15 +362,44 @@ __device__ __forceinline__ void finish(const AttnArgs& a, const f4 (&o)[DT], flo
 }
 
 // Bytes of a workgroup unit's LDS image of one step: K as [tile][d/8][16 keys][8],
-// then V as [tile][4-key group][d][4] with kVPad bytes after every group.
+// then the V fragments of the step in pool order.  An operand read of V (one
+// dim tile of a fragment, every lane) is a contiguous 1 KiB (512 B), free of
+// bank conflicts without padding.
 template <int D>
 struct Img {
     static constexpr int kBytesK = Step<D>::kKeys * D * 2;
-    static constexpr int kGroupV = D * 8 + kVPad;
-    static constexpr int kBytes = kBytesK + (Step<D>::kKeys / 4) * kGroupV;
+    static constexpr int kBytes = 2 * kBytesK;
     static constexpr int kPiecesK = kBytesK / 16;         // 16-byte pieces of K (2D per tile)
     static constexpr int kPieces = 2 * kPiecesK;          // ... of K and V together
 };
+
+// LDS of the two-phase unit kernel: four images, also holding at the end
+// one phase's running state (o as f4 per dim tile and lane, then m and n)
+// for every wave of a phase.
+template <int D>
+constexpr int unit_lds_bytes() {
+    const int x = kWaves * (D / 16) * 64 * 16 + kWaves * 64 * 8;
+    return 4 * Img<D>::kBytes > x ? 4 * Img<D>::kBytes : x;
+}
+
+// LDS offset of V piece jv of a step's image.  The pieces of key tile tt
+// are 2 D tt .. 2 D tt + 2 D - 1, in the order they sit in memory from the
+// tile's source (VLay::tile_src).
+template <int D>
+__device__ __forceinline__ int v_piece_dst(int jv) {
+    return Img<D>::kBytesK + jv * 16;
+}
+// byte offset, inside a fragment, of the lane's part for dims 16dt + col
+template <int D, int C>
+__device__ __forceinline__ int v_frag_lane(int dt, int col, int grp) {
+    using L = VLay<D, C>;
+    return ((dt * L::kGroups + L::lane_group(grp)) * 16 + col) * 16 + L::lane_byte(grp);
+}
+// LDS offset of the lane's part of V fragment f for dims 16dt + col
+template <int D, int C>
+__device__ __forceinline__ int v_frag_lds(int f, int dt, int col, int grp) {
+    return Img<D>::kBytesK + f * (VLay<D, C>::kFragKeys * D * 2) + v_frag_lane<D, C>(dt, col, grp);
+}
 
 // One workgroup unit: query rows [row_lo, row_lo + n_rows) of one head.
 // Wave w loads pieces [w, w + 1) * kPieces / 4 of every step's image and
@@ -332,7 +435,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 
     h8 stg[NL];
     // piece j of the image: K pieces [0, KP) as (tile, d/8 piece, key), then
-    // V pieces [KP, 2 KP) as (tile, byte offset / 16 in the tile's V block)
+    // V pieces [KP, 2 KP) as (group, dim)
     // A wave's pieces cover TPW tiles from ta on (of K for waves 0-1, of V
     // for waves 2-3); load i falls in tile ta + i / (NL / TPW).  With one
     // tile per step every wave loads a part of tile 0.
@@ -347,10 +450,11 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
             const bool is_k = j0 < KP;
             const int jj = is_k ? j0 : j0 - KP;
             const int ts = tile_start<D>(step, jj / (2 * D), n_keys);
+            const int tv = VLay<D, C>::tile_src(step, jj / (2 * D), n_keys);
             const int rem = jj % (2 * D) + lane;
             const size_t cbytes = static_cast<size_t>(id[i / (NL / TPW)]) * cstride;
             const char* kp = kbase + cbytes + (static_cast<size_t>(rem >> 4) * C + ts % C + (rem & 15)) * 16;
-            const char* vp = vbase + cbytes + static_cast<size_t>((ts % C) / 4) * (D * 8) + rem * 16;
+            const char* vp = vbase + cbytes + static_cast<size_t>(tv % C) * (D * 2) + rem * 16;
             stg[i] = __builtin_nontemporal_load(reinterpret_cast<const h8*>(is_k ? kp : vp));
         }
     };
@@ -358,12 +462,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int j = role * kPer + i * 64 + lane;
-            const int jv = j - KP;
-            const int tt = jv / (2 * D);
-            const int rem = jv % (2 * D);
-            const int voff = Img<D>::kBytesK + (tt * 4 + rem / (D / 2)) * Img<D>::kGroupV +
-                             (rem % (D / 2)) * 16;
-            *reinterpret_cast<h8*>(img + (j < KP ? j * 16 : voff)) = stg[i];
+            *reinterpret_cast<h8*>(img + (j < KP ? j * 16 : v_piece_dst<D>(j - KP))) = stg[i];
         }
     };
 
@@ -407,18 +506,17 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
             softmax_step<NT, DT>(s, pq, o, m_run, l_run, step, n_keys, grp, a.scale_log2e);
             // V entries past the last key are zeroed on the last step only
             auto pv = [&](auto masked) {
+                using L = VLay<D, C>;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
-                    h4 v[NT];
+                    typename L::Frag v[L::kFrags];
 #pragma unroll
-                    for (int tt = 0; tt < NT; ++tt) {
-                        v[tt] = *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
-                                                             (tt * 4 + grp) * Img<D>::kGroupV +
-                                                             (16 * dt + col) * 8);
+                    for (int f = 0; f < L::kFrags; ++f) {
+                        v[f] = *reinterpret_cast<const typename L::Frag*>(img + v_frag_lds<D, C>(f, dt, col, grp));
                         if constexpr (decltype(masked)::value)
-                            v[tt] = mask_v(v[tt], step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+                            v[f] = mask_frag<D, C>(v[f], step * Step<D>::kKeys, f, grp, n_keys);
                     }
-                    o[dt] = pv_tile<NT>(o[dt], v, pq);
+                    o[dt] = pv_frags<D, C>(o[dt], v, pq);
                 }
             };
             if ((step + 1) * Step<D>::kKeys > n_keys)
@@ -461,7 +559,7 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     constexpr bool kDirect = D >= 128;
     static_assert(kPer % 64 == 0 && (2 * D) % 64 == 0 && (kPer % (2 * D) == 0 || NT == 1) &&
                   NL % TPW == 0 && (NT == 1 || (W / 2) * TPW == NT), "piece split");
-    static_assert(!kDirect || (D / 2) % 64 == 0, "a direct load must stay inside one V group");
+    static_assert(D % 64 == 0, "a load's 64 pieces must stay inside one V group");
     const int col = lane & 15;
     const int grp = lane >> 4;
     const int H = a.H;
@@ -506,22 +604,18 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         const int j0 = role * kPer + i * 64;
         const bool is_k = j0 < KP;
         const int jj = is_k ? j0 : j0 - KP;
-        const int ts = tile_start<D>(step, jj / (2 * D), n_keys);
+        const int tk = tile_start<D>(step, jj / (2 * D), n_keys);
+        const int tv = VLay<D, C>::tile_src(step, jj / (2 * D), n_keys);
         const size_t cbytes = static_cast<size_t>(id[i / (NL / TPW)]) * cstride;
-        const char* base = is_k ? kbase + cbytes + static_cast<size_t>(ts % C) * 16
-                                : vbase + cbytes + static_cast<size_t>((ts % C) / 4) * (D * 8);
+        const char* base = (is_k ? kbase : vbase) + cbytes +
+                           (is_k ? static_cast<size_t>(tk % C) * 16 : static_cast<size_t>(tv % C) * (D * 2));
         return reinterpret_cast<const h8*>(base + loff[i]);
     };
     // LDS byte offset of the piece a lane of load i writes (lane offset excluded
     // when lane_part is false)
     auto dst = [&](int i, bool lane_part) {
         const int j = role * kPer + i * 64 + (lane_part ? lane : 0);
-        const int jv = j - KP;
-        const int tt = jv / (2 * D);
-        const int rem = jv % (2 * D);
-        const int voff = Img<D>::kBytesK + (tt * 4 + rem / (D / 2)) * Img<D>::kGroupV +
-                         (rem % (D / 2)) * 16;
-        return j < KP ? j * 16 : voff;
+        return j < KP ? j * 16 : v_piece_dst<D>(j - KP);
     };
 
     h8 stg[kDirect ? 1 : NL];
@@ -537,10 +631,10 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
 #pragma unroll
             for (int k = 0; k < TPW; ++k) {
                 const int tt = ta + k;
-                const int ts = tile_start<D>(step, tt, n_keys);
+                const int ts = kwave ? tile_start<D>(step, tt, n_keys) : VLay<D, C>::tile_src(step, tt, n_keys);
                 const size_t cb = static_cast<size_t>(chunk_of(step, tt)) * cstride;
                 const char* base = kwave ? kbase + cb + static_cast<size_t>(ts % C) * 16
-                                         : vbase + cb + static_cast<size_t>((ts % C) / 4) * (D * 8);
+                                         : vbase + cb + static_cast<size_t>(ts % C) * (D * 2);
 #pragma unroll
                 for (int i = k * (NL / TPW); i < (k + 1) * (NL / TPW); ++i)
                     __builtin_amdgcn_global_load_lds(
@@ -603,24 +697,24 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
             for (int ks = 0; ks < KS; ++ks)
                 s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[tt][ks], qb[0][ks], s[tt], 0, 0, 0);
         }
-        h4 vf[DT][NT];
+        using L = VLay<D, C>;
+        typename L::Frag vf[DT][L::kFrags];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-                vf[dt][tt] = *reinterpret_cast<const h4*>(img + Img<D>::kBytesK + (tt * 4 + grp) * Img<D>::kGroupV +
-                                                          (16 * dt + col) * 8);
+            for (int f = 0; f < L::kFrags; ++f)
+                vf[dt][f] = *reinterpret_cast<const typename L::Frag*>(img + v_frag_lds<D, C>(f, dt, col, grp));
         h4 pq[NT];
         softmax_step<NT, DT, true>(s, pq, o[0], m_run[0], l_run[0], step, lim[0], grp, a.scale_log2e);
         if ((step + 1) * Step<D>::kKeys > n_keys) {           // V past the last key: zero
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt)
-                    vf[dt][tt] = mask_v(vf[dt][tt], step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+                for (int f = 0; f < L::kFrags; ++f)
+                    vf[dt][f] = mask_frag<D, C>(vf[dt][f], step * Step<D>::kKeys, f, grp, n_keys);
         }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[0][dt] = pv_tile<NT>(o[0][dt], vf[dt], pq);
+        for (int dt = 0; dt < DT; ++dt) o[0][dt] = pv_frags<D, C>(o[0][dt], vf[dt], pq);
     };
     auto compute = [&](const char* img, int step) {
         if constexpr (RT == 1) {
@@ -648,19 +742,18 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
                                        grp, a.scale_log2e);
         // V entries past the last key are zeroed on the last step only
         auto pv = [&](auto masked) {
+            using L = VLay<D, C>;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                h4 v[NT];
+                typename L::Frag v[L::kFrags];
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    v[tt] = *reinterpret_cast<const h4*>(img + Img<D>::kBytesK +
-                                                         (tt * 4 + grp) * Img<D>::kGroupV +
-                                                         (16 * dt + col) * 8);
+                for (int f = 0; f < L::kFrags; ++f) {
+                    v[f] = *reinterpret_cast<const typename L::Frag*>(img + v_frag_lds<D, C>(f, dt, col, grp));
                     if constexpr (decltype(masked)::value)
-                        v[tt] = mask_v(v[tt], step * Step<D>::kKeys + 16 * tt + 4 * grp, n_keys);
+                        v[f] = mask_frag<D, C>(v[f], step * Step<D>::kKeys, f, grp, n_keys);
                 }
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) o[rt][dt] = pv_tile<NT>(o[rt][dt], v, pq[rt]);
+                for (int rt = 0; rt < RT; ++rt) o[rt][dt] = pv_frags<D, C>(o[rt][dt], v, pq[rt]);
             }
         };
         if ((step + 1) * Step<D>::kKeys > n_keys)
@@ -689,7 +782,7 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         __syncthreads();                     // every image has been read
         // phase 1's (o, m, n) to phase 0: o as [role][dt][lane] f4, then (m, n)
         constexpr int kOBytes = W * DT * 64 * 16;
-        static_assert(kOBytes + W * 64 * 8 <= 4 * Img<D>::kBytes, "state exchange fits the images");
+        static_assert(W == kWaves && kOBytes + W * 64 * 8 <= unit_lds_bytes<D>(), "state exchange fits");
         f4* xo = reinterpret_cast<f4*>(img0);
         float* xml = reinterpret_cast<float*>(img0 + kOBytes);
         if (phase == 1 && computes) {
@@ -821,7 +914,8 @@ void attn_kernel(AttnArgs a) {
 
     h8 qb[KS];            // Q^T (B operand): row col, dims 32*ks + 8*grp .. +7
     h8 kr[NT][KS];        // K of one step: tile t = keys 16t .. 16t+15
-    h4 vr[DT][NT];        // V of one step: [dim tile][key tile], 4 keys per lane
+    using VL = VLay<D, C>;
+    typename VL::Frag vr[DT][VL::kFrags];   // V of one step: [dim tile][fragment]
 
     auto query_row = [&](const Task& t) { return col < t.n_rows ? a.rows[t.row_lo + col] : -1; };
     auto load_q = [&](const Task& t, int qrow) {
@@ -834,7 +928,7 @@ void attn_kernel(AttnArgs a) {
     // Byte offsets: a uniform part (chunk slice, key tile, k-step / dim tile)
     // plus one per-lane constant, so every load is SGPR base + VGPR offset.
     const uint32_t k_lane = static_cast<uint32_t>(col + grp * C) * 16u;   // key col, dims 8*grp..
-    const uint32_t v_lane = static_cast<uint32_t>(grp * D + col) * 8u;    // keys 4*grp.., dim col
+    const uint32_t v_lane = static_cast<uint32_t>(v_frag_lane<D, C>(0, col, grp));   // the lane's keys, dim col
     auto slice_of = [&](const _Float16* pool, int chunk, int head) {
         return reinterpret_cast<const char*>(pool + (static_cast<size_t>(chunk) * H + head) * slice);
     };
@@ -850,15 +944,22 @@ void attn_kernel(AttnArgs a) {
         }
     };
     auto load_v = [&](const Task& t, int step) {
+        constexpr int TPF = NT / VL::kFrags;       // key tiles per fragment
+        const char* base[VL::kFrags];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            const int key = tile_start<D>(step, tt, t.n_valid);
-            const char* base = slice_of(vpool, tile_id<D, C>(t.ids, step, tt, t.n_valid), t.head) +
-                               ((key % C) / 4) * (D * 8);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                vr[dt][tt] = __builtin_nontemporal_load(reinterpret_cast<const h4*>(base + dt * 128 + v_lane));
+        for (int f = 0; f < VL::kFrags; ++f) {
+            const int key = VL::tile_src(step, TPF * f, t.n_valid);
+            base[f] = slice_of(vpool, tile_id<D, C>(t.ids, step, TPF * f, t.n_valid), t.head) + (key % C) * (D * 2);
         }
+        // dim tile by dim tile across the fragments: the P V product of a dim
+        // tile waits only for its own loads (measured faster than fragment by
+        // fragment when every wave streams one long context)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int f = 0; f < VL::kFrags; ++f)
+                vr[dt][f] = __builtin_nontemporal_load(
+                    reinterpret_cast<const typename VL::Frag*>(base[f] + dt * (VL::kGroups * 256) + v_lane));
     };
 
     Task cur = fetch_task<D, C>(a, first);
@@ -888,7 +989,7 @@ void attn_kernel(AttnArgs a) {
         for (int step = 0; step + 1 < n_steps; ++step) {
             qk<NT, KS>(s, kr, qb);
             load_k(cur, step + 1);
-            softmax_pv<NT, DT>(s, vr, o, m_run, l_run, step, cur.n_valid, grp, a.scale_log2e);
+            softmax_pv<D, C>(s, vr, o, m_run, l_run, step, cur.n_valid, grp, a.scale_log2e);
             load_v(cur, step + 1);
         }
         // last step: the next task's queries and K/V follow instead
@@ -897,7 +998,7 @@ void attn_kernel(AttnArgs a) {
             load_q(nxt, nxt_qrow);
             load_k(nxt, 0);
         }
-        softmax_pv<NT, DT>(s, vr, o, m_run, l_run, n_steps - 1, cur.n_valid, grp, a.scale_log2e);
+        softmax_pv<D, C>(s, vr, o, m_run, l_run, n_steps - 1, cur.n_valid, grp, a.scale_log2e);
         finish<D, DT>(a, o, m_run, l_run, cur_qrow, cur.out, cur.head, col, grp);
         if (!has_next) break;
         load_v(nxt, 0);
@@ -935,7 +1036,7 @@ template <int D, int C>
 __global__ __launch_bounds__(64 * 2 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void unit_kernel(AttnArgs a) {
     static_assert(D >= 128, "two-phase units load straight into LDS");
-    __shared__ __attribute__((aligned(16))) char lds[4 * Img<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) char lds[unit_lds_bytes<D>()];
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
@@ -1040,10 +1141,9 @@ __device__ __forceinline__ void scatter_piece(const ScatterArgs& a, int64_t gid,
     *reinterpret_cast<h8*>(static_cast<_Float16*>(a.kpool) + sbase +
                            (static_cast<size_t>(piece) * C + t) * 8) = kv;
     const h8 vv = *reinterpret_cast<const h8*>(static_cast<const _Float16*>(a.vnew) + src);
-    _Float16* vb = static_cast<_Float16*>(a.vpool) + sbase +
-                   (static_cast<size_t>(t / 4) * D + piece * 8) * 4 + (t % 4);
+    _Float16* vb = static_cast<_Float16*>(a.vpool) + sbase + VLay<D, C>::elem(t, piece * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vb[e * 4] = vv[e];
+    for (int e = 0; e < 8; ++e) vb[e * 8] = vv[e];
 }
 
 template <int D, int C>
@@ -1065,7 +1165,7 @@ __global__ __launch_bounds__(256) void scatter_inline_kernel(ScatterArgs a, Inli
 
 // Move tokens' K/V between pool slots (the split of a node under token
 // matching).  One thread per (move, head, 8 dims): a 16-byte K piece and the
-// same 8 dims of V, which sit 4 halves apart in the [c/4][d][4] layout.
+// same 8 dims of V, which sit 8 halves apart in the V layout.
 template <int D, int C>
 __global__ __launch_bounds__(256) void move_kernel(MoveArgs a) {
     constexpr int P = D / 8;
@@ -1083,10 +1183,10 @@ __global__ __launch_bounds__(256) void move_kernel(MoveArgs a) {
     *reinterpret_cast<h8*>(kp + tb + (static_cast<size_t>(piece) * C + tt) * 8) =
         *reinterpret_cast<const h8*>(kp + fb + (static_cast<size_t>(piece) * C + ft) * 8);
     _Float16* vp = static_cast<_Float16*>(a.vpool);
-    const _Float16* vf = vp + fb + (static_cast<size_t>(ft / 4) * D + piece * 8) * 4 + (ft % 4);
-    _Float16* vt = vp + tb + (static_cast<size_t>(tt / 4) * D + piece * 8) * 4 + (tt % 4);
+    const _Float16* vf = vp + fb + VLay<D, C>::elem(ft, piece * 8);
+    _Float16* vt = vp + tb + VLay<D, C>::elem(tt, piece * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vt[e * 4] = vf[e * 4];
+    for (int e = 0; e < 8; ++e) vt[e * 8] = vf[e * 8];
 }
 
 __global__ __launch_bounds__(256) void copy_words_kernel(const int32_t* __restrict__ src,

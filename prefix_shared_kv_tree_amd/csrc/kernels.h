@@ -22,7 +22,7 @@ struct AttnArgs {
     const int32_t* seqlen;    // [b] tokens per depth-first position
     const void* q;            // fp16 [b][H][D]
     const void* kpool;        // fp16 [N][H][D/8][C][8]
-    const void* vpool;        // fp16 [N][H][C/4][D][4]
+    const void* vpool;        // fp16 [N][H] slices of C x D in the V order of VLay
     void* out;                // fp16 [b][H][D]
     float* part_o;            // [n_slots][H][D]
     float* part_ml;           // [n_slots][H][2]  (m in log2 units, n)

@@ -120,17 +120,23 @@ def test_token_and_chunk_matching_agree():
 
 def _token_kv(torch, pool, slot, h, d, c, kind):
     """One token's [h, d] K or V read back through the documented pool
-    layout (K slice [d/8][c][8], V slice [c/4][d][4])."""
+    layout: K slice [d/8][c][8]; V slice a run of blocks of F tokens (32, or
+    16 when d is 256 or c is 16), each [d/16][F/8 groups][16][8]."""
     chunk, t = divmod(int(slot), c)
     base = chunk * h * c * d
     x = torch.arange(d, device=pool.device)
+    paired = d <= 128 and c >= 32
+    F = 32 if paired else 16
+    w = t % F
+    g = (w % 16) // 4 if paired else w // 8
+    e = (w // 16) * 4 + w % 4 if paired else w % 8
     out = []
     for j in range(h):
         b = base + j * c * d
         if kind == "k":
             idx = b + ((x // 8) * c + t) * 8 + x % 8
         else:
-            idx = b + ((t // 4) * d + x) * 4 + t % 4
+            idx = b + (t - w) * d + (((x // 16) * (F // 8) + g) * 16 + x % 16) * 8 + e
         out.append(pool[idx])
     return torch.stack(out)
 
