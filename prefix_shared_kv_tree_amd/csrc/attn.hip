@@ -101,6 +101,24 @@ struct Flag {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
+// left in every lane: two register swaps between rows (gfx950 permlane
+// swaps, plain VALU work) instead of two round trips through the LDS
+// crossbar.  A swap of x with itself puts x of lane l^32 (then l^16) beside
+// x of lane l.
+__device__ __forceinline__ float rows_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // The plan metadata is read-only for the whole launch.  Reading it through
 // the constant address space lets the compiler use scalar loads: task fields
 // and chunk ids then live in SGPRs, and fetching the next chunk id never
@@ -237,8 +255,7 @@ __device__ __forceinline__ void softmax_step(f4 (&s)[NT], h4 (&pq)[NT], f4 (&o)[
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx * sc);   // finite: every step has a valid key
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
@@ -334,8 +351,7 @@ __device__ __forceinline__ void softmax_pv(f4 (&s)[NT], VStep<D, C>& vr, f4 (&o)
 template <int D, int DT>
 __device__ __forceinline__ void finish(const AttnArgs& a, const f4 (&o)[DT], float m_run,
                                        float l_run, int qrow, int out, int head, int col, int grp) {
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = rows_sum(l_run);
     if (qrow < 0) return;
     const int H = a.H;
     if (out < 0) {
@@ -574,8 +590,8 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     const int out = u[6];
     const int key_base = kCausal ? u[7] : 0;
     static_assert(P == 1 || (P == 2 && RT == 1 && !kCausal), "two phases: decode units only");
-    const int role = P == 1 ? wave : wave % W;
-    const int phase = P == 1 ? 0 : wave / W;
+    const int role = P == 2 ? wave % W : wave;
+    const int phase = P == 2 ? wave / W : 0;
     const bool computes = 16 * RT * role < n_rows;
     const int n_steps = (n_keys + Step<D>::kKeys - 1) / Step<D>::kKeys;
     const size_t slice = static_cast<size_t>(C) * D * 2;
@@ -716,12 +732,8 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[0][dt] = pv_frags<D, C>(o[0][dt], vf[dt], pq);
     };
-    auto compute = [&](const char* img, int step) {
-        if constexpr (RT == 1) {
-            compute1(img, step);
-            return;
-        }
-        f4 s[RT][NT];
+    // S^T of a step for every row tile
+    auto qk_rt = [&](const char* img, f4 (&s)[RT][NT]) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) {
 #pragma unroll
@@ -735,12 +747,17 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
                     s[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qb[rt][ks], s[rt][tt], 0, 0, 0);
             }
         }
-        h4 pq[RT][NT];
+    };
+    // the softmax of a step whose S^T is s: its weights P^T in pq
+    auto softmax_rt = [&](int step, f4 (&s)[RT][NT], h4 (&pq)[RT][NT]) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
             softmax_step<NT, DT, true>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt], step, lim[rt],
                                        grp, a.scale_log2e);
-        // V entries past the last key are zeroed on the last step only
+    };
+    // O^T += V^T P^T for a step; V entries past the last key are zeroed on
+    // the last step only
+    auto pv_rt = [&](const char* img, int step, const h4 (&pq)[RT][NT]) {
         auto pv = [&](auto masked) {
             using L = VLay<D, C>;
 #pragma unroll
@@ -760,6 +777,17 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
             pv(Flag<true>{});
         else
             pv(Flag<false>{});
+    };
+    auto compute = [&](const char* img, int step) {
+        if constexpr (RT == 1) {
+            compute1(img, step);
+        } else {
+            f4 s[RT][NT];
+            h4 pq[RT][NT];
+            qk_rt(img, s);
+            softmax_rt(step, s, pq);
+            pv_rt(img, step, pq);
+        }
     };
 
     if constexpr (P == 2) {
