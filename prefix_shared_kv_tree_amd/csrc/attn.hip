@@ -29,7 +29,9 @@
 //    byte of a shared chunk is thus fetched once per row block, however many
 //    rows read it.  Each workgroup runs its units first, all 4 waves in lock
 //    step.  Prefill runs wider units of the same kind (run_unit_wide: eight
-//    waves, up to two 16-row tiles per wave, a causal limit per row).
+//    waves, up to two 16-row tiles per wave, a causal limit per row; at
+//    head_dim 128 the two waves of each SIMD take turns, one issuing matrix
+//    products while the other runs its softmax).
 //  * Single-wave tasks (phase-2 items, and phase-1 row blocks of <= 16
 //    rows): every wave then walks its own list of tasks, keeping the next
 //    step's K/V -- or the next task's queries and first K/V -- in flight
@@ -92,6 +94,11 @@ struct Step {
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// The SIMD of its compute unit that the calling wave runs on: field SIMD_ID
+// (bits 5:4) of the HW_ID hardware register (register 4), read with
+// s_getreg_b32 (operand: register id | offset << 6 | (size - 1) << 11).
+__device__ __forceinline__ int simd_id() { return __builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11)); }
+
 // A compile-time flag passed to generic lambdas (two instantiations of a
 // loop body chosen by a wave-uniform branch).
 template <bool B>
@@ -100,6 +107,10 @@ struct Flag {
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lazy running max of the prefill softmax (softmax_step): moved only when a
+// row's step max exceeds it by more than this many log2 units.
+constexpr int kLazyLog2 = 8;
 
 // Max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
 // left in every lane: two register swaps between rows (gfx950 permlane
@@ -231,7 +242,15 @@ __device__ __forceinline__ void qk(f4 (&s)[NT], const h8 (&kr)[NT][KS], const h8
 // multiply-add, s * scale - m.  Other scales scale the scores first.  The
 // running sum adds the fp16 weights that the P V product uses, two at a
 // time with a packed dot product against (1, 1).
-template <int NT, int DT, bool kSkip = false>
+//
+// kLazy > 0 (prefill units): the running max m is moved only when a row's
+// step max exceeds it by more than kLazy (log2 units), so the weights of
+// the other steps are exp2 of at most kLazy (<= 2^kLazy, exact in fp16's
+// range) and o and n keep their scale: (o, m, n) still means
+// o = sum 2^(s - m) v, n = sum 2^(s - m) for the m it holds, the form that
+// attn_reduce and the final o / n take.  Late in a long context a new
+// maximum rarely moves by that much, so the rescale of o mostly drops out.
+template <int NT, int DT, bool kSkip = false, int kLazy = 0>
 __device__ __forceinline__ void softmax_step(f4 (&s)[NT], h4 (&pq)[NT], f4 (&o)[DT], float& m_run,
                                              float& l_run, int step, int n_valid, int grp,
                                              float scale_log2e) {
@@ -256,8 +275,21 @@ __device__ __forceinline__ void softmax_step(f4 (&s)[NT], h4 (&pq)[NT], f4 (&o)[
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
     mx = rows_max(mx);
-    const float m_new = fmaxf(m_run, mx * sc);   // finite: every step has a valid key
-    const float alpha = fast_exp2(m_run - m_new);
+    float m_new, alpha;
+    bool rescale;
+    if constexpr (kLazy > 0) {
+        // A row's first step always moves m (-inf before); a step whose keys
+        // are all masked for the row (mx = -inf) never does.
+        const float m_step = mx * sc;
+        const bool grow = m_step > m_run + static_cast<float>(kLazy);
+        m_new = grow ? m_step : m_run;
+        alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+        rescale = __any(grow);
+    } else {
+        m_new = fmaxf(m_run, mx * sc);            // finite: every step has a valid key
+        alpha = fast_exp2(m_run - m_new);
+        rescale = !kSkip || __any(alpha != 1.0f);
+    }
     m_run = m_new;
     float lsum = 0.f;
     const h2 one = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
@@ -270,7 +302,7 @@ __device__ __forceinline__ void softmax_step(f4 (&s)[NT], h4 (&pq)[NT], f4 (&o)[
         lsum = __builtin_amdgcn_fdot2(__builtin_shufflevector(pq[tt], pq[tt], 2, 3), one, lsum, false);
     }
     l_run = l_run * alpha + lsum;
-    if (!kSkip || __any(alpha != 1.0f)) {
+    if (rescale) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
     }
@@ -563,10 +595,22 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, cint* u, int wave, i
 // Both phases pass the same barriers (one per pair of steps).  At the end
 // phase 1 hands its running state (o, m, n) to phase 0 through LDS, which
 // folds it in with attn_reduce before writing the unit's partials.
+//
+// P = 3 (prefill units at head_dim 128, W = 8): a ping-pong schedule over
+// three images.  Each SIMD holds one wave of each kind: a leading wave
+// (lead) issues the matrix products of a step -- P V of step i - 1, then
+// Q K^T of step i -- while its partner runs the softmax of step i, and the
+// other way round in the next half of the step.  Two barriers per step
+// separate the halves; the matrix cores of a SIMD then work during the
+// partner's exponentials instead of both waves of a SIMD issuing the same
+// kind of work at the same time.  The image of step i is read from the
+// half before the leading waves' Q K^T of step i to the half of their
+// P V of step i, so the loads of step i + 2 go into the third image, one
+// step ahead.  The softmax moves the running max lazily (kLazy).
 template <int D, int C, int RT, bool kCausal, int W = kWaves, int P = 1>
 __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wave, int lane,
                                               char* img0, char* img1, char* img2 = nullptr,
-                                              char* img3 = nullptr) {
+                                              char* img3 = nullptr, bool lead = true) {
     constexpr int KS = D / 32, DT = D / 16, NT = Step<D>::kTiles;
     constexpr int kPer = Img<D>::kPieces / W;
     constexpr int NL = kPer / 64;
@@ -589,7 +633,8 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     const int n_rows = u[5];
     const int out = u[6];
     const int key_base = kCausal ? u[7] : 0;
-    static_assert(P == 1 || (P == 2 && RT == 1 && !kCausal), "two phases: decode units only");
+    static_assert(P == 1 || (P == 2 && RT == 1 && !kCausal) || (P == 3 && kCausal && D == 128),
+                  "two phases: decode units only; ping-pong: prefill at head_dim 128");
     const int role = P == 2 ? wave % W : wave;
     const int phase = P == 2 ? wave / W : 0;
     const bool computes = 16 * RT * role < n_rows;
@@ -693,6 +738,16 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         m_run[rt] = -INFINITY;
         l_run[rt] = 0.f;
     }
+    if constexpr (P == 3) {
+        // ping-pong: the queries wait in this wave's part of the Q area of LDS
+        // (img3), in operand order -- a contiguous 1 KiB per (row tile,
+        // k-step) -- instead of 32 registers
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                *reinterpret_cast<h8*>(img3 + ((role * RT + rt) * KS + ks) * 1024 + lane * 16) = qb[rt][ks];
+    }
 
     // One row tile per wave (decode units): every K fragment of the step is
     // read before the first product and every V fragment before the softmax,
@@ -751,9 +806,12 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     // the softmax of a step whose S^T is s: its weights P^T in pq
     auto softmax_rt = [&](int step, f4 (&s)[RT][NT], h4 (&pq)[RT][NT]) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-            softmax_step<NT, DT, true>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt], step, lim[rt],
-                                       grp, a.scale_log2e);
+        for (int rt = 0; rt < RT; ++rt) {
+            softmax_step<NT, DT, true, P == 3 ? kLazyLog2 : 0>(s[rt], pq[rt], o[rt], m_run[rt], l_run[rt],
+                                                               step, lim[rt], grp, a.scale_log2e);
+            // ping-pong: one row tile at a time (fewer registers in flight)
+            if constexpr (P == 3) __builtin_amdgcn_sched_barrier(0);
+        }
     };
     // O^T += V^T P^T for a step; V entries past the last key are zeroed on
     // the last step only
@@ -835,6 +893,230 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         }
         __syncthreads();                     // the next unit reuses the images
         return;
+    } else if constexpr (P == 3) {
+        static_assert(kDirect && RT > 1 && NL == 4, "ping-pong: loads straight into LDS, two row tiles");
+        // What a wave carries across a barrier is either S^T of a step or its
+        // weights P^T; both live in sp (P^T as the bits of sp[rt][tt].xy), so
+        // the two kinds of wave need one set of registers.
+        f4 sp[RT][NT];
+        // One matrix block: O^T += V^T P^T for a step (P^T from sp), then -- if
+        // kQK -- S^T = K Q^T of the next step into sp, k-step by k-step (the
+        // queries' fragments of a k-step come from the Q area once and meet
+        // every key tile).  A lone wave per SIMD issues these, so the reads
+        // of the next group of fragments are issued before the products of
+        // the current one (one ds_read_b128 per ~30 cycles per wave), in an
+        // order pinned by scheduling groups.  kMask zeroes V past the unit's
+        // last key (its last step, which is also the one without kQK).
+        using VL = VLay<D, C>;
+        using VF = typename VL::Frag;
+        constexpr int NF = VL::kFrags;
+        constexpr int kDsRead = 0x100, kMfma = 0x008;
+        auto vread = [&](VF (&v)[NF], const char* img, int dt) {
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+                v[f] = *reinterpret_cast<const VF*>(img + v_frag_lds<D, C>(f, dt, col, grp));
+        };
+        auto qkread = [&](h8 (&q)[RT], h8 (&k)[NT], const char* img, int ks) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                q[rt] = *reinterpret_cast<const h8*>(img3 + ((role * RT + rt) * KS + ks) * 1024 + lane * 16);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+                k[tt] = *reinterpret_cast<const h8*>(img + ((tt * (D / 8) + 4 * ks + grp) * 16 + col) * 16);
+        };
+        auto qkmma = [&](const h8 (&q)[RT], const h8 (&k)[NT]) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    sp[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k[tt], q[rt], sp[rt][tt], 0, 0, 0);
+        };
+        auto zero_sp = [&]() {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) sp[rt][tt] = f4{0.f, 0.f, 0.f, 0.f};
+        };
+        // Q K^T alone (the first step of a unit), pipelined the same way
+        auto qk_pp = [&](const char* img) {
+            h8 qa[RT], ka[NT], qb2[RT], kb[NT];
+            zero_sp();
+            qkread(qa, ka, img, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, RT + NT, 0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS) {
+                    if (ks & 1)
+                        qkread(qa, ka, img, ks + 1);
+                    else
+                        qkread(qb2, kb, img, ks + 1);
+                    __builtin_amdgcn_sched_group_barrier(kDsRead, RT + NT, 0);
+                }
+                if (ks & 1)
+                    qkmma(qb2, kb);
+                else
+                    qkmma(qa, ka);
+                __builtin_amdgcn_sched_group_barrier(kMfma, RT * NT, 0);
+            }
+        };
+        auto block = [&](auto mask, auto with_qk, const char* pv_img, int pv_step, const char* qk_img) {
+            constexpr bool kMask = decltype(mask)::value, kQK = decltype(with_qk)::value;
+            h4 pq[RT][NT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+                    pq[rt][tt] = __builtin_bit_cast(
+                        h4, __builtin_shufflevector(sp[rt][tt], sp[rt][tt], 0, 1));
+            VF va[NF], vb[NF];
+            h8 qa[RT], ka[NT], qb2[RT], kb[NT];
+            vread(va, pv_img, 0);
+            __builtin_amdgcn_sched_group_barrier(kDsRead, NF, 0);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                if (dt + 1 < DT) {
+                    if (dt & 1)
+                        vread(va, pv_img, dt + 1);
+                    else
+                        vread(vb, pv_img, dt + 1);
+                    __builtin_amdgcn_sched_group_barrier(kDsRead, NF, 0);
+                } else if constexpr (kQK) {
+                    qkread(qa, ka, qk_img, 0);
+                    __builtin_amdgcn_sched_group_barrier(kDsRead, RT + NT, 0);
+                }
+                VF (&v)[NF] = (dt & 1) ? vb : va;
+                if constexpr (kMask) {
+#pragma unroll
+                    for (int f = 0; f < NF; ++f)
+                        v[f] = mask_frag<D, C>(v[f], pv_step * Step<D>::kKeys, f, grp, n_keys);
+                }
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) o[rt][dt] = pv_frags<D, C>(o[rt][dt], v, pq[rt]);
+                __builtin_amdgcn_sched_group_barrier(kMfma, RT * NF, 0);
+            }
+            zero_sp();
+            if constexpr (kQK) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + 1 < KS) {
+                        if (ks & 1)
+                            qkread(qa, ka, qk_img, ks + 1);
+                        else
+                            qkread(qb2, kb, qk_img, ks + 1);
+                        __builtin_amdgcn_sched_group_barrier(kDsRead, RT + NT, 0);
+                    }
+                    if (ks & 1)
+                        qkmma(qb2, kb);
+                    else
+                        qkmma(qa, ka);
+                    __builtin_amdgcn_sched_group_barrier(kMfma, RT * NT, 0);
+                }
+            }
+        };
+        auto softmax_pp = [&](int step) {
+            h4 pq[RT][NT];
+            softmax_rt(step, sp, pq);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    const auto w = __builtin_bit_cast(float __attribute__((ext_vector_type(2))), pq[rt][tt]);
+                    sp[rt][tt][0] = w[0];
+                    sp[rt][tt][1] = w[1];
+                }
+        };
+        // Step i (i + 1 < n_steps) is: wait for this wave's loads of step
+        // i + 1, a workgroup barrier (step i + 1 is complete, step i - 1 is
+        // read), the second half (lead: softmax of i; partner: P V of i and
+        // Q K^T of i + 1), a plain barrier, and the first half of step i + 1
+        // (lead: P V of i and Q K^T of i + 1; partner: softmax of i + 1).
+        // Every wave loads its part of step i + 2 into the image of step
+        // i - 1 at the start of its softmax half: a lead right after the
+        // workgroup barrier, a partner after the plain one, not in front of
+        // its matrix block (a wave that issues loads stalls while the compute
+        // unit's earlier loads drain; spreading them over the half, or one
+        // wave of a pair issuing both parts, measured slower).  The
+        // plain barrier only keeps the two kinds of wave in step: the next
+        // half reads the same images, and the loads in flight go to the
+        // third (__syncthreads() would wait for them: its release fence
+        // covers writes to LDS).  Each kind of wave runs its own loop, the
+        // steps unrolled by three so that every image is known at compile
+        // time (the compiler then waits for loads into LDS only where an
+        // image is read), and the last step is peeled off.
+        auto half2 = [&](int i, char* ld) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (ld && i + 2 < n_steps) stage(i + 2, ld);
+        };
+        auto mid = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto steps = [&](auto body) {
+            int i = 0;
+            for (; i + 3 < n_steps; i += 3) {
+                body(i, img0, img1, img2);
+                body(i + 1, img1, img2, img0);
+                body(i + 2, img2, img0, img1);
+            }
+            if (i + 1 < n_steps) body(i, img0, img1, img2);
+            if (i + 2 < n_steps) body(i + 1, img1, img2, img0);
+            return (n_steps - 1) % 3;            // the image of the last step
+        };
+        // Steps 0 and 1 load, and every wave waits for its loads: step 0 is
+        // complete when all have passed the plain barrier that follows (the
+        // images were free at the end of the last unit).  Then the partner
+        // computes S^T of step 0 ahead.
+        auto prologue = [&]() {
+            stage(0, img0);
+            if (n_steps > 1) stage(1, img1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            mid();
+        };
+        int last;
+        if (!computes) {
+            prologue();
+            mid();
+            last = steps([&](int i, char*, char*, char* ld) {
+                half2(i, ld);
+                mid();
+            });
+            half2(n_steps - 1, nullptr);
+            mid();
+        } else if (lead) {
+            prologue();
+            mid();
+            qk_pp(img0);
+            last = steps([&](int i, char* cur, char* nxt, char* ld) {
+                half2(i, ld);
+                softmax_pp(i);
+                mid();
+                block(Flag<false>{}, Flag<true>{}, cur, i, nxt);
+            });
+            char* cur = last == 0 ? img0 : last == 1 ? img1 : img2;
+            half2(n_steps - 1, nullptr);
+            softmax_pp(n_steps - 1);
+            mid();
+            block(Flag<true>{}, Flag<false>{}, cur, n_steps - 1, nullptr);
+        } else {
+            prologue();
+            qk_pp(img0);
+            mid();
+            softmax_pp(0);
+            last = steps([&](int i, char* cur, char* nxt, char* ld) {
+                half2(i, nullptr);
+                block(Flag<false>{}, Flag<true>{}, cur, i, nxt);
+                mid();
+                if (i + 2 < n_steps) stage(i + 2, ld);
+                softmax_pp(i + 1);
+            });
+            char* cur = last == 0 ? img0 : last == 1 ? img1 : img2;
+            half2(n_steps - 1, nullptr);
+            block(Flag<true>{}, Flag<false>{}, cur, n_steps - 1, nullptr);
+            mid();
+        }
+        __syncthreads();                     // the next unit reuses the images
     } else if constexpr (kDirect) {
         // step s is computed from image s % 2 while step s + 1 loads into the other
         auto body = [&](char* cur, char* nxt, int step) {
@@ -1045,15 +1327,37 @@ void attn_kernel(AttnArgs a) {
 template <int D, int C>
 __global__ __launch_bounds__(64 * prefill_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(AttnArgs a) {
+    constexpr bool kPingPong = D == 128;
     __shared__ __attribute__((aligned(16))) char img0[Img<D>::kBytes];
     __shared__ __attribute__((aligned(16))) char img1[D >= 128 ? Img<D>::kBytes : 16];
+    __shared__ __attribute__((aligned(16))) char img2[kPingPong ? Img<D>::kBytes : 16];
+    // the units' queries (ping-pong): 16 rows x D halves per row tile of every wave
+    __shared__ __attribute__((aligned(16)))
+    char qlds[kPingPong ? prefill_waves(D) * prefill_row_tiles(D) * 16 * D * 2 : 16];
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
     const int ucount = meta(a.wg_units)[2 * blockIdx.x + 1];
-    for (int k = 0; k < ucount; ++k)
-        run_unit_wide<D, C, prefill_row_tiles(D), true, prefill_waves(D)>(
-            a, meta(a.units) + 8 * (ufirst + k), wave, lane, img0, img1);
+    if constexpr (kPingPong) {
+        // Pair the waves by the SIMD they run on: of the waves of this
+        // workgroup on a SIMD, in index order, every other one leads.  (The
+        // SIMD numbers pass through the Q area before any query does.)
+        int* simd_of = reinterpret_cast<int*>(qlds);
+        const int simd = wave_uniform(simd_id());
+        if (lane == 0) simd_of[wave] = simd;
+        __syncthreads();
+        int below = 0;
+        for (int w = 0; w < wave; ++w) below += simd_of[w] == simd;
+        const bool lead = (below & 1) == 0;
+        __syncthreads();
+        for (int k = 0; k < ucount; ++k)
+            run_unit_wide<D, C, prefill_row_tiles(D), true, prefill_waves(D), 3>(
+                a, meta(a.units) + 8 * (ufirst + k), wave, lane, img0, img1, img2, qlds, lead);
+    } else {
+        for (int k = 0; k < ucount; ++k)
+            run_unit_wide<D, C, prefill_row_tiles(D), true, prefill_waves(D)>(
+                a, meta(a.units) + 8 * (ufirst + k), wave, lane, img0, img1);
+    }
 }
 
 // Decode plans whose work is all workgroup units (every batch row's context
