@@ -1043,9 +1043,14 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         // steps unrolled by three so that every image is known at compile
         // time (the compiler then waits for loads into LDS only where an
         // image is read), and the last step is peeled off.
+        // (Both barriers are fenced with sched_barrier: a barrier orders
+        // memory operations, and the compiler would otherwise move the last
+        // matrix instructions of a block into the next half.)
         auto half2 = [&](int i, char* ld) {
+            __builtin_amdgcn_sched_barrier(0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
             if (ld && i + 2 < n_steps) stage(i + 2, ld);
         };
         auto mid = [&]() {
