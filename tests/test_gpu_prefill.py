@@ -54,6 +54,26 @@ def test_prefill_batch_all_rows(b, prefix, new, d, c):
         ps.close()
 
 
+@pytest.mark.parametrize("prefix,new,c", [
+    (0, 1, 64), (0, 64, 64), (64, 64, 64), (128, 64, 64), (192, 64, 64), (256, 64, 64),
+    (300, 255, 64), (60, 200, 64), (0, 256, 64), (1, 511, 64), (100, 33, 32), (40, 129, 128),
+    (17, 300, 16)])
+def test_prefill_schedule_edges(prefix, new, c):
+    """Head_dim 128 runs the ping-pong schedule: one sequence whose units have
+    1 to 9 steps of 64 keys (the steps are unrolled by three and the last one
+    is peeled) and 1 to 256 rows (waves without rows only load and wait),
+    every row against the oracle."""
+    _torch()
+    print(f"\n[case] prefill schedule edges prefix={prefix} new={new} c={c}", flush=True)
+    pb = W.prefill_batch(900 + prefix + new, 1, prefix, new, h=2, d=128, c=c)
+    ref = A.prefill_attention(pb.w, pb.seqs, pb.q_from, pb.q)
+    ps = _setup(pb)
+    err = float(np.abs(_run(ps) - ref).max())
+    print(f"[case]   err={err:.3e} info={ps.info}", flush=True)
+    assert err <= TOL
+    ps.close()
+
+
 @pytest.mark.parametrize("b,prefix,new,d,c", [
     (12, 1000, [int(x) for x in np.random.default_rng(1).integers(1, 200, 12)], 128, 64),
     (7, 40, [3, 90, 17, 1, 64, 33, 5], 64, 16), (5, 130, [70, 1, 129, 3, 40], 256, 64)])
