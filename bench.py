@@ -509,6 +509,24 @@ def summarize_prefill(args):
                 f"{timed_ns / 1e3:.1f} |",
                 f"| useful fraction of the dense f16 peak over the timed launches | "
                 f"{useful / timed_ns / 1e3 / MFMA_F16_PEAK_TFLOPS * 100:.1f} % |"]
+    if args.fetch_csv and args.write_csv:
+        # HBM traffic per launch, scaled by the calibration copy of the same runs
+        # (as for the decode kernels), against the distinct K/V bytes
+        fetch, nf = _counter_means(args.fetch_csv, kname)
+        write, nw = _counter_means(args.write_csv, kname)
+        cf, _ = _counter_means(args.fetch_csv, "neg_kernel")
+        cw, _ = _counter_means(args.write_csv, "neg_kernel")
+        copy_bytes = args.copy_mib * 2 ** 20
+        fetch_b = fetch["FETCH_SIZE"] * 1024 * copy_bytes / (cf["FETCH_SIZE"] * 1024)
+        write_b = write["WRITE_SIZE"] * 1024 * copy_bytes / (cw["WRITE_SIZE"] * 1024)
+        kv = bench_row["distinct_kv_bytes"]
+        out += [f"| HBM bytes read per launch (FETCH_SIZE, mean of {nf.get('FETCH_SIZE', 0)} dispatches, "
+                f"copy-calibrated) | {fetch_b:,.0f} |",
+                f"| HBM bytes written per launch (WRITE_SIZE, mean of {nw.get('WRITE_SIZE', 0)}) | "
+                f"{write_b:,.0f} |",
+                f"| distinct K/V bytes of the batch | {kv:,.0f} |",
+                f"| bytes read / distinct K/V bytes | {fetch_b / kv:.2f} |",
+                f"| Q read + O written (algorithmic) | {bench_row['q_o_bytes']:,.0f} |"]
     out += [
             f"| MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x {SIMDS})) | {busy * 100:.1f} % |",
             "", f"Same run, bench.py: {bench_row['shared_us_per_layer']} us per layer "
@@ -883,6 +901,8 @@ def run_prefill(args):
             row[f"{variant}_tflops"] = round(fl / (us * 1e-6) / 1e12, 1)
             if variant == "shared":
                 row["rows"] = pb.n_rows
+                row["distinct_kv_bytes"] = W.unique_tokens(pb.w) * pb.w.h * pb.w.d * 2 * 2
+                row["q_o_bytes"] = 2 * pb.n_rows * pb.w.h * pb.w.d * 2
                 row["useful_gflop"] = round(fl / 1e9, 2)
                 row["frac_mfma_f16_peak"] = round(fl / (us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
                 row["plan"] = {k: ps.info[k] for k in ("wg_units", "slots", "phase1_items")}
@@ -892,6 +912,8 @@ def run_prefill(args):
             row["speedup_vs_unshared"] = round(row["unshared_us_per_layer"] / row["shared_us_per_layer"], 3)
         print(json.dumps(row), file=sys.stderr, flush=True)
         out.append(row)
+    if args.copy_probe_mib:
+        copy_probe(torch, args.copy_probe_mib)     # calibrates FETCH_SIZE / WRITE_SIZE
     print(json.dumps({"prefill": out, "dtype": "f16", "data": "synthetic, device N(0,1)",
                       "steps": args.prefill_steps}), flush=True)
 

@@ -190,11 +190,14 @@ struct Item {
 // workgroup that would finish it first, where the younger workgroup of a
 // compute unit (g >= G/2) runs at kYoungSpeedPct % speed.  Ties go to the
 // older class, then to the lower workgroup index.
+// add: keep the lists and loads already in wg_units / wg_load and append to them.
 void assign_units(const std::vector<int64_t>& cost, int32_t G,
                   std::vector<std::vector<int32_t>>& wg_units, std::vector<int64_t>& wg_load,
-                  int32_t young_pct = kYoungSpeedPct) {
-    wg_units.assign(G, {});
-    wg_load.assign(G, 0);
+                  int32_t young_pct = kYoungSpeedPct, bool add = false) {
+    if (!add || static_cast<int32_t>(wg_units.size()) != G) {
+        wg_units.assign(G, {});
+        wg_load.assign(G, 0);
+    }
     std::vector<int32_t> order(cost.size());
     for (size_t i = 0; i < order.size(); ++i) order[i] = static_cast<int32_t>(i);
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t c) { return cost[a] > cost[c]; });
@@ -1088,13 +1091,36 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
     // Workgroups are spread round-robin over the 8 accelerator dies (XCDs),
     // each with its own L2.  With heads a multiple of 8, the units of head h
     // go to workgroups g = h (mod 8), so the blocks that re-read a head's K/V
-    // find it in one die's L2.
+    // find it in one die's L2.  A die serves several heads; when the chunks
+    // that many of its blocks re-read (read by at least a quarter of the
+    // blocks: the shared prefixes) do not fit its L2 for all of those heads
+    // together, the die's workgroups take their units head by
+    // head instead (each head's units balanced over all of them, longest
+    // first, on top of the loads already given), so that at any time the die
+    // mostly reads one head's shared chunks; the second round of workgroups
+    // (the younger half, which start as the first finish) take the heads in
+    // reverse order, starting with the one still in L2.  Otherwise every
+    // workgroup's units are balanced together, whatever their head.
     std::vector<std::vector<int32_t>> wg_units(G);
     {
         constexpr int32_t kDies = 8;
+        constexpr int64_t kDieL2Bytes = int64_t{4} << 20;
         const bool by_die = H % kDies == 0 && G % (2 * kDies) == 0;
         const int32_t groups = by_die ? kDies : 1;
-        for (int32_t x = 0; x < groups; ++x) {
+        const int32_t per = G / groups;
+        std::unordered_map<int32_t, int32_t> readers;          // chunk -> blocks reading it
+        for (const PUnit& u : blocks) {
+            int32_t p = static_cast<int32_t>(std::upper_bound(path_off.begin(), path_off.end(), u.chunk_off) -
+                                             path_off.begin()) - 1;
+            const std::vector<int32_t>& path = seqs[dfs_seq[p]]->path;
+            for (int32_t k = 0; k < u.n_chunks; ++k) readers[path[u.chunk_off - path_off[p] + k]]++;
+        }
+        const int32_t many = std::max<int32_t>(2, static_cast<int32_t>(blocks.size() / 4));
+        int64_t reread_chunks = 0;
+        for (const auto& kv : readers) reread_chunks += kv.second >= many;
+        const int64_t reread_bytes = reread_chunks * C * t.D * 4 * (H / groups);   // K and V, fp16
+        const bool head_by_head = by_die && reread_bytes > kDieL2Bytes;
+        for (int32_t x = 0; x < groups && !head_by_head; ++x) {
             std::vector<int64_t> cost;
             std::vector<int32_t> ids;
             for (size_t bi = 0; bi < blocks.size(); ++bi)
@@ -1104,9 +1130,38 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
                 }
             std::vector<std::vector<int32_t>> wu;
             std::vector<int64_t> wl;
-            assign_units(cost, G / groups, wu, wl);
-            for (int32_t i = 0; i < G / groups; ++i)
+            assign_units(cost, per, wu, wl);
+            for (int32_t i = 0; i < per; ++i)
                 for (int32_t k : wu[i]) wg_units[i * groups + x].push_back(ids[k]);
+        }
+        for (int32_t x = 0; x < groups && head_by_head; ++x) {
+            std::vector<std::vector<int32_t>> wu;
+            std::vector<int64_t> wl;
+            std::vector<std::vector<int32_t>> ids_of(per);    // unit ids per workgroup, head by head
+            std::vector<std::vector<int32_t>> head_of(per);
+            for (int32_t h = x; h < H; h += groups) {
+                std::vector<int64_t> cost;
+                for (size_t bi = 0; bi < blocks.size(); ++bi) cost.push_back(blocks[bi].cost);
+                std::vector<size_t> before(per);
+                for (int32_t i = 0; i < static_cast<int32_t>(wu.size()); ++i) before[i] = wu[i].size();
+                assign_units(cost, per, wu, wl, kYoungSpeedPct, /*add=*/true);
+                for (int32_t i = 0; i < per; ++i)
+                    for (size_t k = before[i]; k < wu[i].size(); ++k) {
+                        ids_of[i].push_back(static_cast<int32_t>(wu[i][k] * H + h));
+                        head_of[i].push_back(h);
+                    }
+            }
+            for (int32_t i = 0; i < per; ++i) {
+                std::vector<int32_t>& dst = wg_units[i * groups + x];
+                if (i < per / 2) {
+                    dst = ids_of[i];
+                } else {                                   // younger: heads in reverse order
+                    const int32_t last_h = H - groups + x;
+                    for (int32_t h = last_h; h >= x; h -= groups)
+                        for (size_t k = 0; k < ids_of[i].size(); ++k)
+                            if (head_of[i][k] == h) dst.push_back(ids_of[i][k]);
+                }
+            }
         }
     }
     std::vector<int32_t> merge_rows;
