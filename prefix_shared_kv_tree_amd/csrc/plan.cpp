@@ -187,8 +187,10 @@ struct Item {
 };
 
 // Workgroup units, longest first (equal costs in index order), each to the
-// workgroup that would finish it first, where the younger workgroup of a
-// compute unit (g >= G/2) runs at kYoungSpeedPct % speed.  Ties go to the
+// workgroup that would finish it first, where the younger workgroups
+// (g >= G/2) run at young_pct % of the older ones' speed: the younger of the
+// two workgroups that share a compute unit in decode, the second round of
+// prefill workgroups (whose share of the load it then sets).  Ties go to the
 // older class, then to the lower workgroup index.
 // add: keep the lists and loads already in wg_units / wg_load and append to them.
 void assign_units(const std::vector<int64_t>& cost, int32_t G,
@@ -1130,7 +1132,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
                 }
             std::vector<std::vector<int32_t>> wu;
             std::vector<int64_t> wl;
-            assign_units(cost, per, wu, wl);
+            assign_units(cost, per, wu, wl, kPrefillSecondRoundPct);
             for (int32_t i = 0; i < per; ++i)
                 for (int32_t k : wu[i]) wg_units[i * groups + x].push_back(ids[k]);
         }
@@ -1144,7 +1146,7 @@ int make_prefill_plan(const Tree& t, int32_t n, const int32_t* seq_ids, const in
                 for (size_t bi = 0; bi < blocks.size(); ++bi) cost.push_back(blocks[bi].cost);
                 std::vector<size_t> before(per);
                 for (int32_t i = 0; i < static_cast<int32_t>(wu.size()); ++i) before[i] = wu[i].size();
-                assign_units(cost, per, wu, wl, kYoungSpeedPct, /*add=*/true);
+                assign_units(cost, per, wu, wl, kPrefillSecondRoundPct, /*add=*/true);
                 for (int32_t i = 0; i < per; ++i)
                     for (size_t k = before[i]; k < wu[i].size(); ++k) {
                         ids_of[i].push_back(static_cast<int32_t>(wu[i][k] * H + h));

@@ -77,7 +77,10 @@ constexpr int32_t kKeysPerStep = 64;
 constexpr int32_t kDefaultWorkgroups = 512;  // 256 CUs x 2 resident workgroups
 constexpr int32_t kMaxItemChunks = 64;       // chunks per work item (one per wave lane)
 constexpr int32_t kUnitStepCost = 2;         // quarter steps per wave of a unit step (4 = a task step)
-constexpr int32_t kYoungSpeedPct = 60;       // speed of a compute unit's younger workgroup, % of the older
+constexpr int32_t kYoungSpeedPct = 70;       // speed of a compute unit's younger workgroup, % of the older
+// Prefill workgroups (one resident per compute unit) run in two rounds, the
+// second starting as the first finish: the second round's load, % of the first's.
+constexpr int32_t kPrefillSecondRoundPct = 60;
 constexpr int32_t kAppendSlack = 2;          // chunk ids reserved after a row's last item for appends
 constexpr int32_t kMaxPatches = 256;         // incremental patches before a plan is rebuilt anyway
 
