@@ -877,10 +877,11 @@ def run_prefill(args):
     if args.prefill_case is not None:
         cases = [cases[args.prefill_case]]
     out = []
+    d = args.prefill_head_dim
     for name, b, prefix, new in cases:
-        row = {"workload": name, "b": b, "prefix": prefix, "h": 32, "d": 128, "c": 64}
+        row = {"workload": name, "b": b, "prefix": prefix, "h": 32, "d": d, "c": 64}
         for variant in ("shared",) if args.prefill_case is not None else ("shared", "unshared"):
-            pb = W.prefill_batch(4242, b, prefix, new, h=32, d=128, c=64, with_kv=False)
+            pb = W.prefill_batch(4242, b, prefix, new, h=32, d=d, c=64, with_kv=False)
             if variant == "unshared":
                 pb = W.prefill_unshared(pb)
             ps = PrefillSetup(pb, layers=2, device_random_seed=4242)
@@ -1037,6 +1038,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=10,
                     help="untimed prefill launches first (the first few run up to 20 %% slower)")
+    ap.add_argument("--prefill-head-dim", type=int, default=128, choices=[64, 128, 256],
+                    help="head_dim of the --prefill batches")
     ap.add_argument("--prefill-case", type=int, default=None,
                     help="time only this prefill workload (index), shared variant only")
     ap.add_argument("--loop-only", action="store_true",
