@@ -722,17 +722,29 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     int lim[RT];
     f4 o[RT][DT];
     float m_run[RT], l_run[RT];
+    // Every lane reads a row entry (lanes past the unit's rows read its last
+    // one and discard it), so that the reads of all row tiles go out together
+    // instead of one tile's waiting for the previous tile's branch.
+    int qpos_raw[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int ri = row_lo + min(16 * (RT * role + rt) + col, n_rows - 1);
+        qrow[rt] = a.rows[ri];
+        qpos_raw[rt] = kCausal ? a.qpos[ri] : 0;
+    }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int r = 16 * (RT * role + rt) + col;
-        qrow[rt] = computes && r < n_rows ? a.rows[row_lo + r] : -1;
-        lim[rt] = kCausal && computes && r < n_rows ? min(n_keys, a.qpos[row_lo + r] + 1 - key_base)
-                                                    : n_keys;
-        const _Float16* qp = static_cast<const _Float16*>(a.q) +
-                             (static_cast<size_t>(qrow[rt] < 0 ? 0 : qrow[rt]) * H + head) * D + 8 * grp;
+        const bool valid = computes && r < n_rows;
+        qrow[rt] = valid ? qrow[rt] : -1;
+        lim[rt] = kCausal && valid ? min(n_keys, qpos_raw[rt] + 1 - key_base) : n_keys;
+        if constexpr (P != 3) {
+            const _Float16* qp = static_cast<const _Float16*>(a.q) +
+                                 (static_cast<size_t>(qrow[rt] < 0 ? 0 : qrow[rt]) * H + head) * D + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qb[rt][ks] = qrow[rt] >= 0 ? *reinterpret_cast<const h8*>(qp + 32 * ks) : h8{};
+            for (int ks = 0; ks < KS; ++ks)
+                qb[rt][ks] = qrow[rt] >= 0 ? *reinterpret_cast<const h8*>(qp + 32 * ks) : h8{};
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[rt][dt] = f4{0.f, 0.f, 0.f, 0.f};
         m_run[rt] = -INFINITY;
@@ -741,7 +753,21 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     if constexpr (P == 3) {
         // ping-pong: the queries wait in this wave's part of the Q area of LDS
         // (img3), in operand order -- a contiguous 1 KiB per (row tile,
-        // k-step) -- instead of 32 registers
+        // k-step) -- instead of 32 registers.  The rows of every tile are
+        // read first, then all queries, and the unit's first two steps of K/V
+        // are issued while the queries are in flight (the images and the Q
+        // area were free at the end of the last unit): two memory round trips
+        // before the first product instead of one per dependent read.
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const _Float16* qp = static_cast<const _Float16*>(a.q) +
+                                 (static_cast<size_t>(qrow[rt] < 0 ? 0 : qrow[rt]) * H + head) * D + 8 * grp;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qb[rt][ks] = qrow[rt] >= 0 ? *reinterpret_cast<const h8*>(qp + 32 * ks) : h8{};
+        }
+        stage(0, img0);
+        if (n_steps > 1) stage(1, img1);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1069,13 +1095,11 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
             if (i + 2 < n_steps) body(i + 1, img1, img2, img0);
             return (n_steps - 1) % 3;            // the image of the last step
         };
-        // Steps 0 and 1 load, and every wave waits for its loads: step 0 is
-        // complete when all have passed the plain barrier that follows (the
-        // images were free at the end of the last unit).  Then the partner
-        // computes S^T of step 0 ahead.
+        // Every wave waits for its loads of steps 0 and 1 (issued with the
+        // queries above): step 0 and the Q area are complete when all have
+        // passed the plain barrier that follows.  Then the partner computes
+        // S^T of step 0 ahead.
         auto prologue = [&]() {
-            stage(0, img0);
-            if (n_steps > 1) stage(1, img1);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             mid();
         };
