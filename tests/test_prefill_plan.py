@@ -157,3 +157,37 @@ def test_heads_follow_dies():
                 assert int(plan["units"][k][3]) % 8 == g % 8
     finally:
         B.pkvt_tree_destroy(t)
+
+
+def test_long_shared_prefix_takes_units_head_by_head():
+    """When the chunks that many units re-read exceed a die's L2 for the die's
+    heads (here a 4160-token prefix: 65 chunks x 64 KiB of K/V for its four
+    heads, read by every unit), every workgroup of a die takes its units head
+    by head: the older half of the die's workgroups in ascending head order
+    (each with a share of every head of the die), the younger half (which
+    start as the first finish) in descending order.  A short prefix keeps one
+    head per workgroup here.  (Which rows and keys the units cover is checked
+    by the other tests of this file and, on the GPU, by the prefill parity
+    tests; this one looks at the order only.)"""
+    for prefix, by_head in ((4160, True), (512, False)):
+        pb = W.prefill_batch(11, 8, prefix, 256, h=32, d=64, c=64, with_kv=False)
+        t = _tree(32, 64, 64)
+        try:
+            B.pkvt_tree_build(t, [pb.w.segments[s].tokens for s in pb.residents])
+            ids, _ = B.pkvt_tree_build(t, [pb.w.seq_tokens(u) for u in pb.seqs])
+            B.pkvt_prefill_plan(t, ids, pb.q_from, workgroups=64)
+            plan = PV.parse(B.pkvt_prefill_blob(t))
+            assert len(plan["units"]) == 8 * 32                # one unit per (sequence, head)
+            per = 64 // 8
+            for g, (first, cnt) in enumerate(plan["wg_units"]):
+                heads = [int(plan["units"][k][3]) for k in range(first, first + cnt)]
+                assert all(h % 8 == g % 8 for h in heads)
+                if by_head:
+                    older = g // 8 < per // 2
+                    assert heads == (sorted(heads) if older else sorted(heads, reverse=True))
+                    if older:
+                        assert sorted(set(heads)) == [g % 8 + 8 * j for j in range(4)]
+                else:
+                    assert len(set(heads)) == 1
+        finally:
+            B.pkvt_tree_destroy(t)
