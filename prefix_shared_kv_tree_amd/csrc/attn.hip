@@ -1146,6 +1146,31 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
             mid();
         }
         __syncthreads();                     // the next unit reuses the images
+    } else if constexpr (kDirect && kCausal && D == 256) {
+        // Prefill at head_dim 256, whose steps are 16 keys: two steps per
+        // workgroup barrier, computed from one pair of images (img0, img1 or
+        // img2, img3) while the next two load into the other pair.
+        auto stage2 = [&](int s, char* a0, char* a1) {
+            if (s < n_steps) stage(s, a0);
+            if (s + 1 < n_steps) stage(s + 1, a1);
+        };
+        auto body2 = [&](char* c0, char* c1, char* n0, char* n1, int s) {
+            // this wave's loads of steps s, s + 1 are in, then every wave's;
+            // nobody reads steps s - 2, s - 1 any more
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            stage2(s + 2, n0, n1);
+            if (computes) {
+                compute(c0, s);
+                if (s + 1 < n_steps) compute(c1, s + 1);
+            }
+        };
+        stage2(0, img0, img1);
+        for (int s = 0; s < n_steps; s += 4) {
+            body2(img0, img1, img2, img3, s);
+            if (s + 2 < n_steps) body2(img2, img3, img0, img1, s + 2);
+        }
+        __syncthreads();                     // the next unit reuses the images
     } else if constexpr (kDirect) {
         // step s is computed from image s % 2 while step s + 1 loads into the other
         auto body = [&](char* cur, char* nxt, int step) {
@@ -1164,14 +1189,23 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         }
         __syncthreads();                     // the next unit reuses the images
     } else {
+        // loads staged in registers (head_dim < 128): step s goes from the
+        // registers into image s % 2 and is computed there while step s + 1
+        // loads into the registers.  One barrier per step: a wave that writes
+        // image s % 2 has passed step s - 1's barrier, which every wave
+        // reached only after computing step s - 2 from that image.
+        auto body = [&](char* cur, int step) {
+            commit(cur);
+            __syncthreads();
+            if (step + 1 < n_steps) stage(step + 1, cur);
+            if (computes) compute(cur, step);
+        };
         stage(0, img0);
-        for (int step = 0; step < n_steps; ++step) {
-            __syncthreads();
-            commit(img0);
-            __syncthreads();
-            if (step + 1 < n_steps) stage(step + 1, img0);
-            if (computes) compute(img0, step);
+        for (int step = 0; step < n_steps; step += 2) {
+            body(img0, step);
+            if (step + 1 < n_steps) body(img1, step + 1);
         }
+        __syncthreads();                     // the next unit reuses the images
     }
     if (computes) {
 #pragma unroll
@@ -1357,12 +1391,14 @@ template <int D, int C>
 __global__ __launch_bounds__(64 * prefill_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(AttnArgs a) {
     constexpr bool kPingPong = D == 128;
+    constexpr bool kTwoStep = D == 256;          // two 16-key steps per barrier, four images
     __shared__ __attribute__((aligned(16))) char img0[Img<D>::kBytes];
-    __shared__ __attribute__((aligned(16))) char img1[D >= 128 ? Img<D>::kBytes : 16];
-    __shared__ __attribute__((aligned(16))) char img2[kPingPong ? Img<D>::kBytes : 16];
-    // the units' queries (ping-pong): 16 rows x D halves per row tile of every wave
+    __shared__ __attribute__((aligned(16))) char img1[Img<D>::kBytes];
+    __shared__ __attribute__((aligned(16))) char img2[kPingPong || kTwoStep ? Img<D>::kBytes : 16];
+    // the units' queries (ping-pong): 16 rows x D halves per row tile of every
+    // wave; the fourth image at head_dim 256
     __shared__ __attribute__((aligned(16)))
-    char qlds[kPingPong ? prefill_waves(D) * prefill_row_tiles(D) * 16 * D * 2 : 16];
+    char qlds[kPingPong ? prefill_waves(D) * prefill_row_tiles(D) * 16 * D * 2 : kTwoStep ? Img<D>::kBytes : 16];
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
@@ -1385,7 +1421,7 @@ void prefill_kernel(AttnArgs a) {
     } else {
         for (int k = 0; k < ucount; ++k)
             run_unit_wide<D, C, prefill_row_tiles(D), true, prefill_waves(D)>(
-                a, meta(a.units) + 8 * (ufirst + k), wave, lane, img0, img1);
+                a, meta(a.units) + 8 * (ufirst + k), wave, lane, img0, img1, img2, qlds);
     }
 }
 
