@@ -1147,28 +1147,34 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         }
         __syncthreads();                     // the next unit reuses the images
     } else if constexpr (kDirect && kCausal && D == 256) {
-        // Prefill at head_dim 256, whose steps are 16 keys: two steps per
-        // workgroup barrier, computed from one pair of images (img0, img1 or
-        // img2, img3) while the next two load into the other pair.
-        auto stage2 = [&](int s, char* a0, char* a1) {
-            if (s < n_steps) stage(s, a0);
-            if (s + 1 < n_steps) stage(s + 1, a1);
+        // Prefill at head_dim 256, whose steps are 16 keys: four steps per
+        // workgroup barrier.  Each of the four images holds two steps (one
+        // at its start, one Img<D>::kBytes in); steps s .. s + 3 are computed
+        // from one pair of images (img0, img1 or img2, img3) while s + 4 ..
+        // s + 7 load into the other pair.
+        constexpr int kB = Img<D>::kBytes;
+        auto at = [&](char* a, char* b, int j) { return (j < 2 ? a : b) + (j & 1) * kB; };
+        auto stage4 = [&](int s, char* a, char* b) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (s + j < n_steps) stage(s + j, at(a, b, j));
         };
-        auto body2 = [&](char* c0, char* c1, char* n0, char* n1, int s) {
-            // this wave's loads of steps s, s + 1 are in, then every wave's;
-            // nobody reads steps s - 2, s - 1 any more
+        auto body4 = [&](char* ca, char* cb, char* na, char* nb, int s) {
+            // this wave's loads of steps s .. s + 3 are in, then every
+            // wave's; nobody reads steps s - 4 .. s - 1 any more
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            stage2(s + 2, n0, n1);
+            stage4(s + 4, na, nb);
             if (computes) {
-                compute(c0, s);
-                if (s + 1 < n_steps) compute(c1, s + 1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (s + j < n_steps) compute(at(ca, cb, j), s + j);
             }
         };
-        stage2(0, img0, img1);
-        for (int s = 0; s < n_steps; s += 4) {
-            body2(img0, img1, img2, img3, s);
-            if (s + 2 < n_steps) body2(img2, img3, img0, img1, s + 2);
+        stage4(0, img0, img1);
+        for (int s = 0; s < n_steps; s += 8) {
+            body4(img0, img1, img2, img3, s);
+            if (s + 4 < n_steps) body4(img2, img3, img0, img1, s + 4);
         }
         __syncthreads();                     // the next unit reuses the images
     } else if constexpr (kDirect) {
@@ -1391,14 +1397,16 @@ template <int D, int C>
 __global__ __launch_bounds__(64 * prefill_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(AttnArgs a) {
     constexpr bool kPingPong = D == 128;
-    constexpr bool kTwoStep = D == 256;          // two 16-key steps per barrier, four images
-    __shared__ __attribute__((aligned(16))) char img0[Img<D>::kBytes];
-    __shared__ __attribute__((aligned(16))) char img1[Img<D>::kBytes];
-    __shared__ __attribute__((aligned(16))) char img2[kPingPong || kTwoStep ? Img<D>::kBytes : 16];
+    // head_dim 256: four 16-key steps per barrier, from four images of two steps each
+    constexpr bool kFourStep = D == 256;
+    constexpr int kImg = (kFourStep ? 2 : 1) * Img<D>::kBytes;
+    __shared__ __attribute__((aligned(16))) char img0[kImg];
+    __shared__ __attribute__((aligned(16))) char img1[kImg];
+    __shared__ __attribute__((aligned(16))) char img2[kPingPong || kFourStep ? kImg : 16];
     // the units' queries (ping-pong): 16 rows x D halves per row tile of every
     // wave; the fourth image at head_dim 256
     __shared__ __attribute__((aligned(16)))
-    char qlds[kPingPong ? prefill_waves(D) * prefill_row_tiles(D) * 16 * D * 2 : kTwoStep ? Img<D>::kBytes : 16];
+    char qlds[kPingPong ? prefill_waves(D) * prefill_row_tiles(D) * 16 * D * 2 : kFourStep ? kImg : 16];
     const int wave = wave_uniform(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int ufirst = meta(a.wg_units)[2 * blockIdx.x];
