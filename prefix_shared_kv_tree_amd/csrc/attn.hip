@@ -685,6 +685,23 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     int ldso[NL];                                 // LDS offset of load i (lane 0)
 #pragma unroll
     for (int i = 0; i < NL; ++i) ldso[i] = wave_uniform(dst(i, false));
+    // loads staged in registers, for a given set of staging registers
+    // (head_dim < 128 takes two steps per barrier, one set per step)
+    auto stage_regs = [&](int step, h8 (&st)[kDirect ? 1 : NL]) {
+        if constexpr (!kDirect) {
+            int id[TPW];
+#pragma unroll
+            for (int k = 0; k < TPW; ++k) id[k] = chunk_of(step, ta + k);
+#pragma unroll
+            for (int i = 0; i < NL; ++i) st[i] = __builtin_nontemporal_load(src(step, i, id));
+        }
+    };
+    auto commit_regs = [&](char* img, const h8 (&st)[kDirect ? 1 : NL]) {
+        if constexpr (!kDirect) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) *reinterpret_cast<h8*>(img + dst(i, true)) = st[i];
+        }
+    };
     auto stage = [&](int step, char* img) {
         if constexpr (kDirect) {
             // per tile: one wave-uniform base (pool, chunk, key offset), then
@@ -703,17 +720,7 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
                         (__attribute__((address_space(3))) void*)(img + ldso[i]), 16, 0, 0);
             }
         } else {
-            int id[TPW];
-#pragma unroll
-            for (int k = 0; k < TPW; ++k) id[k] = chunk_of(step, ta + k);
-#pragma unroll
-            for (int i = 0; i < NL; ++i) stg[i] = __builtin_nontemporal_load(src(step, i, id));
-        }
-    };
-    auto commit = [&](char* img) {
-        if constexpr (!kDirect) {
-#pragma unroll
-            for (int i = 0; i < NL; ++i) *reinterpret_cast<h8*>(img + dst(i, true)) = stg[i];
+            stage_regs(step, stg);
         }
     };
 
@@ -724,13 +731,14 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
     float m_run[RT], l_run[RT];
     // Every lane reads a row entry (lanes past the unit's rows read its last
     // one and discard it), so that the reads of all row tiles go out together
-    // instead of one tile's waiting for the previous tile's branch.
+    // instead of one tile's waiting for the previous tile's branch.  (A unit
+    // always has rows; one without would read none.)
     int qpos_raw[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int ri = row_lo + min(16 * (RT * role + rt) + col, n_rows - 1);
-        qrow[rt] = a.rows[ri];
-        qpos_raw[rt] = kCausal ? a.qpos[ri] : 0;
+        qrow[rt] = n_rows > 0 ? a.rows[ri] : -1;
+        qpos_raw[rt] = kCausal && n_rows > 0 ? a.qpos[ri] : 0;
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -1195,21 +1203,30 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         }
         __syncthreads();                     // the next unit reuses the images
     } else {
-        // loads staged in registers (head_dim < 128): step s goes from the
-        // registers into image s % 2 and is computed there while step s + 1
-        // loads into the registers.  One barrier per step: a wave that writes
-        // image s % 2 has passed step s - 1's barrier, which every wave
-        // reached only after computing step s - 2 from that image.
-        auto body = [&](char* cur, int step) {
-            commit(cur);
+        // loads staged in registers (head_dim < 128): two steps per barrier.
+        // Steps s, s + 1 go from their registers into one image pair (img0,
+        // or img1; each holds two steps, the second Img<D>::kBytes in) and
+        // are computed there while s + 2, s + 3 load into the registers.  A
+        // wave that writes a pair has passed the previous barrier, which every
+        // wave reached only after computing the steps it held before.
+        constexpr int kB = Img<D>::kBytes;
+        h8 stg_b[kDirect ? 1 : NL];
+        auto body2 = [&](char* img, int s) {
+            commit_regs(img, stg);
+            if (s + 1 < n_steps) commit_regs(img + kB, stg_b);
             __syncthreads();
-            if (step + 1 < n_steps) stage(step + 1, cur);
-            if (computes) compute(cur, step);
+            if (s + 2 < n_steps) stage_regs(s + 2, stg);
+            if (s + 3 < n_steps) stage_regs(s + 3, stg_b);
+            if (computes) {
+                compute(img, s);
+                if (s + 1 < n_steps) compute(img + kB, s + 1);
+            }
         };
-        stage(0, img0);
-        for (int step = 0; step < n_steps; step += 2) {
-            body(img0, step);
-            if (step + 1 < n_steps) body(img1, step + 1);
+        stage_regs(0, stg);
+        if (n_steps > 1) stage_regs(1, stg_b);
+        for (int s = 0; s < n_steps; s += 4) {
+            body2(img0, s);
+            if (s + 2 < n_steps) body2(img1, s + 2);
         }
         __syncthreads();                     // the next unit reuses the images
     }
@@ -1397,9 +1414,10 @@ template <int D, int C>
 __global__ __launch_bounds__(64 * prefill_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void prefill_kernel(AttnArgs a) {
     constexpr bool kPingPong = D == 128;
-    // head_dim 256: four 16-key steps per barrier, from four images of two steps each
+    // head_dim 256: four 16-key steps per barrier, from four images of two
+    // steps each; head_dim 64: two steps per barrier, two images of two steps
     constexpr bool kFourStep = D == 256;
-    constexpr int kImg = (kFourStep ? 2 : 1) * Img<D>::kBytes;
+    constexpr int kImg = (kFourStep || D < 128 ? 2 : 1) * Img<D>::kBytes;
     __shared__ __attribute__((aligned(16))) char img0[kImg];
     __shared__ __attribute__((aligned(16))) char img1[kImg];
     __shared__ __attribute__((aligned(16))) char img2[kPingPong || kFourStep ? kImg : 16];
