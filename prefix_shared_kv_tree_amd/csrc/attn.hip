@@ -31,7 +31,8 @@
 //    step.  Prefill runs wider units of the same kind (run_unit_wide: eight
 //    waves, up to two 16-row tiles per wave, a causal limit per row; at
 //    head_dim 128 the two waves of each SIMD take turns, one issuing matrix
-//    products while the other runs its softmax).
+//    products while the other runs its softmax; at head_dim 256 four 16-key
+//    steps and at head_dim 64 two steps share a barrier).
 //  * Single-wave tasks (phase-2 items, and phase-1 row blocks of <= 16
 //    rows): every wave then walks its own list of tasks, keeping the next
 //    step's K/V -- or the next task's queries and first K/V -- in flight
@@ -1204,11 +1205,11 @@ __device__ __forceinline__ void run_unit_wide(const AttnArgs& a, cint* u, int wa
         __syncthreads();                     // the next unit reuses the images
     } else {
         // loads staged in registers (head_dim < 128): two steps per barrier.
-        // Steps s, s + 1 go from their registers into one image pair (img0,
-        // or img1; each holds two steps, the second Img<D>::kBytes in) and
-        // are computed there while s + 2, s + 3 load into the registers.  A
-        // wave that writes a pair has passed the previous barrier, which every
-        // wave reached only after computing the steps it held before.
+        // Steps s, s + 1 go from their registers into one image (img0 or
+        // img1 in turn; each holds two steps, the second Img<D>::kBytes in)
+        // and are computed there while s + 2, s + 3 load into the registers.
+        // A wave that writes an image has passed the previous barrier, which
+        // every wave reached only after computing the steps it held before.
         constexpr int kB = Img<D>::kBytes;
         h8 stg_b[kDirect ? 1 : NL];
         auto body2 = [&](char* img, int s) {
