@@ -539,13 +539,19 @@ int make_plan(const Tree& t, int32_t b, const int32_t* q_order, const PlanOpts& 
         // Every phase-1 item writes one partial (o, m, n) per row and head,
         // read back by the merge: 8 R (d+2) bytes against 4 c d KV bytes
         // per chunk.  Unless the caller fixed the size, an item is long
-        // enough that its partials cost at most a quarter of its KV bytes.
+        // enough that its partials cost at most a quarter of its KV bytes --
+        // except in units-only plans, which are cut into about one unit per
+        // workgroup even below that floor: there the launch is short and a
+        // grid left partly idle costs more than the extra partials (32 rows
+        // over a fully shared 1K context: 256 units of 2 chunks 14.3 us per
+        // layer, the floor's 128 units of 4 chunks 15.0-15.9 us).
         int32_t limit = s1;
         if (opts.phase1_chunks == 0) {
             const int64_t rows = seg_range[s].j - seg_range[s].i;
             if (rows >= opts.unit_rows) limit = units_only ? s1_units_only : s1_unit;
             const int64_t need = (8 * rows * (t.D + 2) * 4 + 4LL * t.C * t.D - 1) / (4LL * t.C * t.D);
-            limit = static_cast<int32_t>(std::min<int64_t>(kMaxItemChunks, std::max<int64_t>(limit, need)));
+            limit = static_cast<int32_t>(
+                std::min<int64_t>(kMaxItemChunks, units_only ? limit : std::max<int64_t>(limit, need)));
         }
         const std::vector<int32_t> at = cuts(static_cast<int32_t>(segs[s].size()), limit);
         for (size_t q = 0; q + 1 < at.size(); ++q) {
