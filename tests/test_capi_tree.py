@@ -421,3 +421,24 @@ def test_phase1_row_blocks(rows, unit_rows, want_units, want_single_rows):
               all(B.pkvt_tree_chunk_refcount(box.t, int(x)) > 1 for x in ch)]
     assert sorted(want_units, reverse=True) == got_units    # one item: 8 tokens = 2 chunks
     assert sorted(int(plan["waves"][i][5]) for i in shared) == sorted(want_single_rows)
+
+
+@pytest.mark.parametrize("n_s,want_items,floor_items", [(1024, 8, 4), (2048, 8, 7), (4096, 8, 8)])
+def test_units_only_plan_fills_the_grid(n_s, want_items, floor_items):
+    """A batch whose rows are all shared (32 rows over one prefix, 32 heads,
+    d = 128) runs on the units-only kernel, one workgroup per compute unit
+    (256 of the default 512), and is cut into about one unit per workgroup --
+    8 items x 32 heads -- even where the partial-cost floor alone (items long
+    enough that their partials cost at most a quarter of their K/V bytes:
+    5 chunks here) would leave the grid partly idle."""
+    w = W.one_prefix(21, 32, n_s, 0, h=32, d=128, c=64, with_kv=False)
+    box = TreeBox(h=32, d=128, c=64, n=256)
+    ids, _ = B.pkvt_tree_build(box.t, w.all_seq_tokens())
+    plan = _plan_and_check(box, ids)
+    info = B.pkvt_plan_info_get(box.t)
+    assert info["kernel"] == 1
+    assert info["phase1_items"] == want_items and info["wg_units"] == want_items * 32 == 256
+    # the floor: ceil(8 R (d + 2) 4 / (4 c d)) chunks per item, R = 32
+    need = -(-8 * 32 * 130 * 4 // (4 * 64 * 128))
+    assert need == 5 and -(-(n_s // 64) // max(need, (n_s // 64) // 8)) == floor_items
+    assert all(int(u[5]) == 32 for u in plan["units"])
