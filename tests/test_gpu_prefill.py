@@ -74,6 +74,27 @@ def test_prefill_schedule_edges(prefix, new, c):
     ps.close()
 
 
+@pytest.mark.parametrize("prefix,new,d,c", [
+    (0, 1, 256, 64), (0, 16, 256, 64), (16, 16, 256, 64), (32, 16, 256, 64), (48, 16, 256, 64),
+    (64, 16, 256, 64), (80, 16, 256, 64), (100, 28, 256, 32), (0, 128, 256, 16), (60, 77, 256, 128),
+    (0, 1, 64, 64), (0, 64, 64, 64), (64, 64, 64, 64), (128, 64, 64, 64), (192, 64, 64, 64),
+    (300, 255, 64, 64), (17, 200, 64, 16), (40, 129, 64, 128)])
+def test_prefill_schedule_edges_other_head_dims(prefix, new, d, c):
+    """Head_dim 256 takes four 16-key steps per barrier and head_dim 64 two
+    64-key steps: one sequence whose units have 1 to 9 steps (every remainder
+    of the groups of four and of two, and the alternation of the image
+    pairs), every row against the oracle."""
+    _torch()
+    print(f"\n[case] prefill schedule edges prefix={prefix} new={new} d={d} c={c}", flush=True)
+    pb = W.prefill_batch(950 + prefix + new + d, 1, prefix, new, h=2, d=d, c=c)
+    ref = A.prefill_attention(pb.w, pb.seqs, pb.q_from, pb.q)
+    ps = _setup(pb)
+    err = float(np.abs(_run(ps) - ref).max())
+    print(f"[case]   err={err:.3e} info={ps.info}", flush=True)
+    assert err <= TOL
+    ps.close()
+
+
 @pytest.mark.parametrize("b,prefix,new,d,c", [
     (12, 1000, [int(x) for x in np.random.default_rng(1).integers(1, 200, 12)], 128, 64),
     (7, 40, [3, 90, 17, 1, 64, 33, 5], 64, 16), (5, 130, [70, 1, 129, 3, 40], 256, 64)])
